@@ -1,0 +1,179 @@
+"""Seeded synthetic workloads for the folded split-KV MLA decode.
+
+This module only draws inputs: lengths, block tables, FP8 query rows and a paged FP8
+latent cache.  It holds none of the decode's arithmetic, and both the HIP path and the
+CPU oracle are fed from it.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, drawn in this order):
+  1. KV lengths per request;
+  2. one permutation of the page pool; requests take their pages from it in order,
+     so every block table is shuffled; unused table entries are -1 (never read);
+  3. the query, x_q of shape [R, k*H, 576], row i = t*H + h (token-major, then head);
+  4. the latent cache pool, x_kv of shape [pool, 64, 576] (512 latent then 64 rope).
+FP8 codes follow the usual per-tensor convention code = e4m3(x / scale), x_hat =
+code * scale, with x clipped to +-448 * scale first (torch turns out-of-range values
+into NaN rather than saturating).  Cache slots past a request's length in its last page,
+and whole unused pages, are filled with the E4M3 NaN code 0x7F, so that any read of
+them shows up in the results.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+PAGE = 64
+KDIM = 576
+VDIM = 512
+NAN_CODE = 0x7F
+E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    R: int
+    k: int
+    H: int
+    lengths: str          # "fixed:<L0>,<L1>,..." | "uniform:<L>" | "loguniform:<lo>,<hi>"
+    pool_pages: int = 0   # 0: exactly the pages the requests use
+    value_std: float = 1.0
+    scale: float = 0.0    # 0: per-tensor amax / 448
+    description: str = ""
+
+    @property
+    def M(self) -> int:
+        return self.k * self.H
+
+
+CONFIGS = {
+    "c1": Config("c1", 2, 4, 8, "fixed:200,317", pool_pages=16, value_std=0.5, scale=1.0 / 64,
+                 description="R=2 k=4 H=8, lengths 200 and 317, 16-page pool"),
+    "c2": Config("c2", 64, 4, 8, "uniform:8192",
+                 description="R=64 k=4 H=8 (32 rows), every length 8192"),
+    "c3": Config("c3", 128, 7, 8, "loguniform:512,65536",
+                 description="R=128 k=7 H=8 (56 rows), lengths log-uniform in [512, 65536]"),
+    "c4": Config("c4", 32, 4, 64, "uniform:32768",
+                 description="R=32 k=4 H=64 (256 rows), every length 32768"),
+    "c5": Config("c5", 16, 7, 64, "fixed:131072" + ",1024" * 15,
+                 description="R=16 k=7 H=64 (448 rows), one length 131072 and fifteen 1024"),
+}
+
+SM_SCALE = 1.0 / math.sqrt(192.0)   # qk_nope 128 + rope 64
+
+
+@dataclasses.dataclass
+class Workload:
+    cfg: Config
+    lengths: np.ndarray       # int32 [R]
+    block_table: np.ndarray   # int32 [R, cols]
+    q8: np.ndarray            # uint8 [R, M, 576]
+    kv8: np.ndarray           # uint8 [pool, 64, 576]
+    q_scale: float
+    k_scale: float
+    sm_scale: float = SM_SCALE
+
+    @property
+    def R(self) -> int:
+        return self.q8.shape[0]
+
+    @property
+    def M(self) -> int:
+        return self.q8.shape[1]
+
+    @property
+    def kv_bytes(self) -> int:
+        """Bytes of KV each request reads once: sum_r L_r * 576."""
+        return int(self.lengths.astype(np.int64).sum()) * KDIM
+
+
+def draw_lengths(spec: str, R: int, rng: np.random.Generator) -> np.ndarray:
+    kind, _, arg = spec.partition(":")
+    if kind == "fixed":
+        vals = [int(v) for v in arg.split(",")]
+        assert len(vals) == R, (spec, R)
+        return np.array(vals, dtype=np.int32)
+    if kind == "uniform":
+        return np.full(R, int(arg), dtype=np.int32)
+    if kind == "loguniform":
+        lo, hi = (int(v) for v in arg.split(","))
+        x = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), R)))
+        return np.clip(x, lo, hi).astype(np.int32)
+    raise ValueError(spec)
+
+
+def encode_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
+    """float32 values -> E4M3FN codes of x / scale, saturated to +-448 (torch cast)."""
+    y = np.clip(x / np.float32(scale), -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _codes(x: np.ndarray, scale: float, chunk: int = 1 << 26) -> np.ndarray:
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for s in range(0, flat.size, chunk):
+        out[s:s + chunk] = encode_e4m3(flat[s:s + chunk], scale)
+    return out.reshape(x.shape)
+
+
+def build_tables(lengths: np.ndarray, pool: int, rng: np.random.Generator, cols: int = 0):
+    pages = (lengths.astype(np.int64) + PAGE - 1) // PAGE
+    used = int(pages.sum())
+    assert used <= pool, (used, pool)
+    perm = rng.permutation(pool).astype(np.int32)
+    cols = max(cols, int(pages.max()) if len(pages) else 1, 1)
+    bt = np.full((len(lengths), cols), -1, dtype=np.int32)
+    pos = 0
+    for r, p in enumerate(pages):
+        bt[r, :p] = perm[pos:pos + p]
+        pos += p
+    return bt, perm[:used]
+
+
+def generate(cfg: Config | str, seed: int = 0, lengths: np.ndarray | None = None,
+             pool_pages: int | None = None, poison: bool = True) -> Workload:
+    """Draw one workload.  ``lengths``/``pool_pages`` override the config (for tests)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lengths = draw_lengths(cfg.lengths, cfg.R, rng)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    R = lengths.shape[0]
+    pages = (lengths.astype(np.int64) + PAGE - 1) // PAGE
+    pool = pool_pages if pool_pages is not None else (cfg.pool_pages or int(pages.sum()))
+    pool = max(pool, int(pages.sum()), 1)
+    bt, used = build_tables(lengths, pool, rng)
+
+    xq = rng.standard_normal((R, cfg.M, KDIM), dtype=np.float32) * np.float32(cfg.value_std)
+    q_scale = cfg.scale or float(np.abs(xq).max()) / E4M3_MAX
+    q8 = _codes(xq, q_scale)
+    del xq
+
+    xkv = rng.standard_normal((pool, PAGE, KDIM), dtype=np.float32)
+    if cfg.value_std != 1.0:
+        xkv *= np.float32(cfg.value_std)
+    k_scale = cfg.scale or float(np.abs(xkv).max()) / E4M3_MAX
+    kv8 = _codes(xkv, k_scale)
+    del xkv
+
+    if poison:
+        mask = np.ones(pool, dtype=bool)
+        mask[used] = False
+        kv8[mask] = NAN_CODE
+        for r in range(R):
+            tail = int(lengths[r]) % PAGE
+            if pages[r] > 0 and tail:
+                kv8[bt[r, pages[r] - 1], tail:, :] = NAN_CODE
+    return Workload(cfg, lengths, bt, q8, kv8, float(q_scale), float(k_scale))
+
+
+def small(R: int, k: int, H: int, lengths, seed: int = 0, extra_pages: int = 3,
+          value_std: float = 1.0) -> Workload:
+    """A small ad-hoc workload for tests: given lengths, a few spare (poisoned) pages."""
+    cfg = Config("adhoc", R, k, H, "fixed:" + ",".join(str(int(v)) for v in lengths),
+                 value_std=value_std)
+    pages = sum((int(v) + PAGE - 1) // PAGE for v in lengths)
+    return generate(cfg, seed=seed, pool_pages=pages + extra_pages)

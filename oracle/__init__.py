@@ -1,0 +1,204 @@
+"""CPU oracle of the folded split-KV absorbed-MLA decode.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` are the only users.  The product package never imports this
+module, and this module imports nothing from the product package.
+
+The numeric parts (E4M3 decode, FP64 attention, LSE merge, split plan) live in
+``oracle.c`` (built by ``oracle/build.py`` into ``liboracle.so``); this wrapper only
+marshals numpy arrays.  The host-side fold rules are small enough to state here in
+Python, each with the passage it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+PAGE = 64
+KDIM = 576
+VDIM = 512
+BALANCED, FIXED = 0, 1
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build  # compile the checker on first use
+
+            _build.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_table.restype = None
+        lib.oracle_e4m3_table.argtypes = [f64p]
+        lib.oracle_attend.restype = ctypes.c_int
+        lib.oracle_attend.argtypes = [u8p, u8p, ctypes.c_int64, i32p, ctypes.c_int32, i32p,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                      ctypes.c_double, ctypes.c_double, i32p, ctypes.c_int32,
+                                      f64p, f64p]
+        lib.oracle_merge.restype = None
+        lib.oracle_merge.argtypes = [f64p, f64p, ctypes.c_int32, f64p, f64p]
+        lib.oracle_plan.restype = ctypes.c_int
+        lib.oracle_plan.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p,
+                                    ctypes.c_int32]
+        lib.oracle_split_range.restype = ctypes.c_int
+        lib.oracle_split_range.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           i32p, i32p]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# --------------------------------------------------------------------------- E4M3FN
+
+def e4m3_value(code: int) -> float:
+    """Real value of one float8 E4M3FN code (NaN for 0x7F / 0xFF)."""
+    return _load().oracle_e4m3_value(int(code) & 0xFF)
+
+
+def e4m3_table() -> np.ndarray:
+    """All 256 E4M3FN codes decoded to float64."""
+    out = np.empty(256, dtype=np.float64)
+    _load().oracle_e4m3_table(_ptr(out, ctypes.c_double))
+    return out
+
+
+# ------------------------------------------------------------------------ attention
+
+def attend(q8, kv8, block_table, lengths, tasks, q_scale, k_scale, sm_scale):
+    """Exact FP64 attention of folded rows over key ranges.
+
+    q8: uint8 [R, M, 576]; kv8: uint8 [pool, 64, 576]; block_table: int32 [R, cols];
+    lengths: int32 [R]; tasks: int32 [n, 4] of (request, row, key_begin, key_end).
+    Returns (out float64 [n, 512], lse float64 [n], log2 units).
+    """
+    q8 = np.ascontiguousarray(q8, dtype=np.uint8)
+    kv8 = np.ascontiguousarray(kv8, dtype=np.uint8)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    tasks = np.ascontiguousarray(tasks, dtype=np.int32).reshape(-1, 4)
+    R, M = q8.shape[0], q8.shape[1]
+    assert q8.shape[2] == KDIM and kv8.shape[1:] == (PAGE, KDIM)
+    assert bt.ndim == 2 and bt.shape[0] == R and lengths.shape == (R,)
+    n = tasks.shape[0]
+    out = np.empty((n, VDIM), dtype=np.float64)
+    lse = np.empty(n, dtype=np.float64)
+    rc = _load().oracle_attend(_ptr(q8, ctypes.c_uint8), _ptr(kv8, ctypes.c_uint8),
+                               kv8.shape[0], _ptr(bt, ctypes.c_int32), bt.shape[1],
+                               _ptr(lengths, ctypes.c_int32), R, M, float(q_scale),
+                               float(k_scale), float(sm_scale), _ptr(tasks, ctypes.c_int32),
+                               n, _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle_attend: task, length or page id out of range")
+    return out, lse
+
+
+def decode(q8, kv8, block_table, lengths, q_scale, k_scale, sm_scale, rows=None):
+    """Folded decode of every request over its full key set [0, L_r).
+
+    rows: optional iterable of (request, row) pairs to compute (default: all).
+    Returns (out float64 [n, 512], lse float64 [n]) in the order of ``rows`` (default:
+    request-major, then row).
+    """
+    R, M = q8.shape[0], q8.shape[1]
+    if rows is None:
+        rows = [(r, i) for r in range(R) for i in range(M)]
+    tasks = np.array([(r, i, 0, int(lengths[r])) for r, i in rows], dtype=np.int32).reshape(-1, 4)
+    return attend(q8, kv8, block_table, lengths, tasks, q_scale, k_scale, sm_scale)
+
+
+# ---------------------------------------------------------------------------- merge
+
+def merge(o, lse):
+    """LSE merge of partials o [n, 512], lse [n] (log2) -> (out [512], lse)."""
+    o = np.ascontiguousarray(o, dtype=np.float64).reshape(-1, VDIM)
+    lse = np.ascontiguousarray(lse, dtype=np.float64).reshape(-1)
+    assert o.shape[0] == lse.shape[0]
+    out = np.empty(VDIM, dtype=np.float64)
+    lo = np.empty(1, dtype=np.float64)
+    _load().oracle_merge(_ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double), lse.shape[0],
+                         _ptr(out, ctypes.c_double), _ptr(lo, ctypes.c_double))
+    return out, float(lo[0])
+
+
+# ----------------------------------------------------------------------------- plan
+
+def plan(lengths, bt_cols, M, MT, W, min_split_tokens=256, max_splits=256, mode=BALANCED,
+         list_len=None):
+    """Split plan: (counts int32 [R], offsets int32 [R+1], work int32 [list_len], items)."""
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    R = lengths.shape[0]
+    if list_len is None:
+        list_len = 2 * (R + W)
+    counts = np.zeros(R, dtype=np.int32)
+    offsets = np.zeros(R + 1, dtype=np.int32)
+    work = np.zeros(max(list_len, 1), dtype=np.int32)
+    n = _load().oracle_plan(_ptr(lengths, ctypes.c_int32), R, bt_cols, M, MT, W,
+                            min_split_tokens, max_splits, mode, _ptr(counts, ctypes.c_int32),
+                            _ptr(offsets, ctypes.c_int32), _ptr(work, ctypes.c_int32), list_len)
+    if n == -1:
+        raise ValueError("oracle_plan: invalid arguments or lengths")
+    if n == -2:
+        raise ValueError("oracle_plan: list_len too small")
+    return counts, offsets, work[:list_len], n
+
+
+def split_range(length, count, s):
+    """Token range [a, b) of split s of a request of ``length`` keys cut in ``count``."""
+    a = ctypes.c_int32()
+    b = ctypes.c_int32()
+    if _load().oracle_split_range(int(length), int(count), int(s), ctypes.byref(a),
+                                  ctypes.byref(b)) != 0:
+        raise ValueError("oracle_split_range: bad split")
+    return a.value, b.value
+
+
+# ------------------------------------------------------------------- fold (host rules)
+
+def foldable(causal: bool, num_reqs: int, num_rows: int, num_decode_tokens: int,
+             block_table_rows: int, max_query_len: int) -> int:
+    """Query tokens per request when a decode batch can be folded, else 0.
+
+    Page "drafter.attention", foldable: only a non-causal batch folds; the rows must be
+    the batch's decode tokens and split evenly over the requests; one token per request
+    leaves nothing to fold; there must be a block-table row per request; and an even
+    split is only proof of uniform blocks when the longest block is exactly k tokens.
+    """
+    if causal:
+        return 0
+    if num_reqs <= 0 or num_rows != num_decode_tokens:
+        return 0
+    if num_rows % num_reqs != 0:
+        return 0
+    k = num_rows // num_reqs
+    if k < 2 or block_table_rows < num_reqs:
+        return 0
+    if max_query_len != k:
+        return 0
+    return k
+
+
+def fold_plan(k: int, heads: int, need_lse: bool, max_fold_heads: int) -> int:
+    """Tokens folded into one decode row.
+
+    Page "drafter.attention", fold_plan: without an LSE all k tokens fold; with one, the
+    largest divisor f of k with f * heads within the kernel's head limit.
+    """
+    if not need_lse:
+        return k
+    return max(d for d in range(1, k + 1) if k % d == 0 and d * heads <= max_fold_heads)

@@ -1,0 +1,26 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: longer CPU test")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The product binding on cuda:0; fails loudly when the HIP library is missing."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("gpu test selected but no GPU is visible")
+    from absorbed_mla_split_amd import binding
+
+    binding.load()
+    return binding
