@@ -1,0 +1,255 @@
+"""ctypes binding of libamla.so (include/amla.h): argument marshalling only.
+
+Every step of the decode runs in the HIP kernels of csrc/amla.hip.  torch is used for
+device memory (``data_ptr()``) and streams (``torch.cuda.current_stream().cuda_stream``)
+and nothing else.  There is no CPU fallback: ``load()`` raises when the library is
+missing or was not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libamla.so")
+
+PAGE = 64
+KDIM = 576
+VDIM = 512
+MAX_ROWS = 1024
+MAX_REQS = 4096
+MAX_SPLITS = 256
+
+OK = 0
+ERR_INVALID = -1
+ERR_WORKSPACE = -2
+ERR_LIST = -3
+ERR_HIP = -4
+
+DEV_BAD_LENGTH = 1
+DEV_BAD_PAGE = 2
+DEV_BAD_ITEM = 4
+
+PLAN_BALANCED = 0
+PLAN_FIXED = 1
+
+EXPORTS = (
+    "amla_fold_plan", "amla_bmm_scales", "amla_decode_config", "amla_reducer_bands",
+    "amla_workspace_bytes", "amla_plan_splits", "amla_folded_decode", "amla_combine",
+    "amla_status_string",
+)
+
+
+class PlanParams(ctypes.Structure):
+    _fields_ = [
+        ("rows_per_req", ctypes.c_int32),
+        ("mtile", ctypes.c_int32),
+        ("workers", ctypes.c_int32),
+        ("min_split_tokens", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        return ("PlanParams(rows_per_req=%d, mtile=%d, workers=%d, min_split_tokens=%d, "
+                "max_splits=%d, mode=%d)" % (self.rows_per_req, self.mtile, self.workers,
+                                             self.min_split_tokens, self.max_splits, self.mode))
+
+
+class AmlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """The HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python absorbed_mla_split_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    pp = ctypes.POINTER(PlanParams)
+    sig = {
+        "amla_fold_plan": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32p, i32p]),
+        "amla_bmm_scales": (ctypes.c_int, [f32, f32, f32, f32p, f32p]),
+        "amla_decode_config": (ctypes.c_int, [i32, i32, i32p, i32p]),
+        "amla_reducer_bands": (ctypes.c_int, [i32, i32, i32p]),
+        "amla_workspace_bytes": (sz, [i32, i32, i32]),
+        "amla_plan_splits": (ctypes.c_int, [vp, i32, i32, pp, vp, vp, vp, i32, vp, sz, vp]),
+        "amla_folded_decode": (ctypes.c_int, [vp, vp, i64, vp, i32, vp, i32, pp, f32, f32, vp,
+                                              vp, vp, i32, vp, sz, vp]),
+        "amla_combine": (ctypes.c_int, [vp, sz, vp, vp, i32, pp, i32, vp, vp, vp]),
+        "amla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().amla_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise AmlaError(fn, status)
+
+
+# ----------------------------------------------------------------------- host helpers
+
+def fold_plan(causal, num_reqs, num_rows, num_decode_tokens, block_table_rows, max_query_len,
+              heads, need_lse, max_fold_heads=MAX_ROWS):
+    """(k, fold) of a decode batch: k = 0 when it does not fold."""
+    k, f = ctypes.c_int32(), ctypes.c_int32()
+    _check("amla_fold_plan", load().amla_fold_plan(int(bool(causal)), num_reqs, num_rows,
+                                                   num_decode_tokens, block_table_rows,
+                                                   max_query_len, heads, int(bool(need_lse)),
+                                                   max_fold_heads, ctypes.byref(k), ctypes.byref(f)))
+    return k.value, f.value
+
+
+def bmm_scales(softmax_scale, q_scale, k_scale):
+    b1, b2 = ctypes.c_float(), ctypes.c_float()
+    _check("amla_bmm_scales", load().amla_bmm_scales(softmax_scale, q_scale, k_scale,
+                                                     ctypes.byref(b1), ctypes.byref(b2)))
+    return b1.value, b2.value
+
+
+def decode_config(compute_units, rows_per_req):
+    w, mt = ctypes.c_int32(), ctypes.c_int32()
+    _check("amla_decode_config", load().amla_decode_config(compute_units, rows_per_req,
+                                                           ctypes.byref(w), ctypes.byref(mt)))
+    return w.value, mt.value
+
+
+def reducer_bands(rows, compute_units):
+    b = ctypes.c_int32()
+    _check("amla_reducer_bands", load().amla_reducer_bands(rows, compute_units, ctypes.byref(b)))
+    return b.value
+
+
+def workspace_bytes(num_reqs, rows_per_req, workers):
+    return int(load().amla_workspace_bytes(num_reqs, rows_per_req, workers))
+
+
+def make_params(rows_per_req, mtile, workers, min_split_tokens=256, max_splits=MAX_SPLITS,
+                mode=PLAN_BALANCED) -> PlanParams:
+    return PlanParams(rows_per_req, mtile, workers, min_split_tokens, max_splits, mode)
+
+
+# ----------------------------------------------------------------------- device calls
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def plan_splits(lengths, bt_cols, params: PlanParams, counts, offsets, work, workspace,
+                stream=None):
+    _check("amla_plan_splits", load().amla_plan_splits(
+        _ptr(lengths), lengths.numel(), bt_cols, ctypes.byref(params), _ptr(counts),
+        _ptr(offsets), _ptr(work), work.numel(), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+
+
+def folded_decode(q, kv, block_table, lengths, params: PlanParams, bmm1, bmm2, counts, offsets,
+                  work, workspace, stream=None):
+    _check("amla_folded_decode", load().amla_folded_decode(
+        _ptr(q), _ptr(kv), kv.shape[0], _ptr(block_table), block_table.stride(0),
+        _ptr(lengths), lengths.numel(), ctypes.byref(params), bmm1, bmm2, _ptr(counts),
+        _ptr(offsets), _ptr(work), work.numel(), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+
+
+def combine(workspace, counts, offsets, num_reqs, params: PlanParams, compute_units, out, lse,
+            stream=None):
+    _check("amla_combine", load().amla_combine(
+        _ptr(workspace), workspace.numel(), _ptr(counts), _ptr(offsets), num_reqs,
+        ctypes.byref(params), compute_units, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+# ------------------------------------------------------------------------ the decoder
+
+class FoldedDecoder:
+    """Plan buffers plus one split-KV workspace for up to ``max_reqs`` requests of
+    ``rows_per_req`` folded rows, allocated once (before any graph capture).  ``plan`` runs
+    once per decode step; ``decode`` once per layer (page "...cutedsl.mla.balanced",
+    BalancedMla)."""
+
+    def __init__(self, max_reqs, rows_per_req, device=None, mode=PLAN_BALANCED,
+                 min_split_tokens=256, max_splits=MAX_SPLITS, workers=None, mtile=None):
+        import torch
+
+        load()
+        self.device = torch.device(device if device is not None else "cuda")
+        props = torch.cuda.get_device_properties(self.device)
+        self.compute_units = props.multi_processor_count
+        w, mt = decode_config(self.compute_units, rows_per_req)
+        self.params = make_params(rows_per_req, mtile or mt, workers or w, min_split_tokens,
+                                  max_splits, mode)
+        self.max_reqs = max_reqs
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.counts = torch.zeros(max(max_reqs, 1), **i32)
+        self.offsets = torch.zeros(max_reqs + 1, **i32)
+        self.work = torch.full((2 * (max_reqs + self.params.workers),), -1, **i32)
+        nbytes = workspace_bytes(max_reqs, rows_per_req, self.params.workers)
+        if nbytes == 0:
+            raise ValueError("unsupported sizes")
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        self.num_reqs = 0
+
+    def plan(self, lengths, bt_cols, stream=None):
+        n = lengths.numel()
+        if n > self.max_reqs:
+            raise ValueError(f"{n} requests > {self.max_reqs}")
+        self.num_reqs = n
+        plan_splits(lengths, bt_cols, self.params, self.counts[:n], self.offsets[:n + 1],
+                    self.work, self.workspace, stream)
+
+    def decode(self, q, kv, block_table, lengths, bmm1, bmm2, out=None, lse=None, stream=None):
+        import torch
+
+        R, M = q.shape[0], q.shape[1]
+        if R != self.num_reqs or M != self.params.rows_per_req:
+            raise ValueError("decode shape does not match the plan")
+        if q.dtype != torch.uint8 or kv.dtype != torch.uint8:
+            raise TypeError("q and kv are float8_e4m3fn codes viewed as uint8")
+        if out is None:
+            out = torch.empty((R, M, VDIM), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((R, M), dtype=torch.float32, device=q.device)
+        folded_decode(q, kv, block_table, lengths, self.params, bmm1, bmm2, self.counts[:R],
+                      self.offsets[:R + 1], self.work, self.workspace, stream)
+        combine(self.workspace, self.counts[:R], self.offsets[:R + 1], R, self.params,
+                self.compute_units, out, lse, stream)
+        return out, lse
+
+    def device_status(self) -> int:
+        """The workspace's device status word (synchronises; for checks, not hot loops)."""
+        return int(self.workspace[:4].view(dtype=__import__("torch").int32).item())
+
+    def plan_host(self):
+        """(counts, offsets, work, items) of the current plan, copied to the host."""
+        R = self.num_reqs
+        counts = self.counts[:R].cpu().numpy()
+        offsets = self.offsets[:R + 1].cpu().numpy()
+        work = self.work.cpu().numpy()
+        return counts, offsets, work, int(offsets[R]) if R >= 0 else 0

@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the folded split-KV absorbed-MLA decode on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the split plan, the persistent
+split-KV decode and the reducer, all on one stream, inputs resident in HBM.  The workload
+is the R=64, k=4, H=8 (32 folded rows), L=8192 draft step (``--config c2``, default);
+``--config`` selects another of the seeded workloads for exploration.  Three copies of the
+KV pool are rotated over the steps so the 256 MB last-level cache does not serve the pages.
+
+Prints ONE JSON line (rank 0): KV-cache GB/s (sum_r L_r * 576 B per step time) as
+``value``, folded rows/s alongside, the dominant kernel's roofline (live HIP-event timing
+of the decode kernel on its stream), and the CPU oracle's rate on a bounded sample of the
+same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--mode", default="balanced", choices=["balanced", "fixed"])
+    ap.add_argument("--unfolded", action="store_true",
+                    help="stock flattening: R*k single-token requests with replicated tables")
+    ap.add_argument("--pools", type=int, default=3, help="KV pool copies rotated over steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_digest():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "absorbed_mla_split_amd", "csrc", "amla.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(config, mode, unfolded):
+    """HBM bytes per decode launch measured by rocprofv3 counters, if recorded for the
+    current kernel source (null once the kernel has changed)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = f"{config}/{mode}/{'unfolded' if unfolded else 'folded'}"
+    ent = rec.get(key)
+    if not ent or ent.get("source") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_s):
+    """The oracle (as it stands) on a bounded sample of rows of this workload, on the host
+    cores; scaled to KV-cache GB/s of the whole workload."""
+    import oracle
+
+    threads = oracle.threads()
+    R, M = w.R, w.M
+    keys_total = float(w.lengths.astype(np.int64).sum()) * M          # (row, key) pairs
+    # calibrate on a few rows of the longest request
+    r0 = int(np.argmax(w.lengths))
+    cal = [(r0, i) for i in range(min(M, max(1, threads)))]
+    t = time.perf_counter()
+    oracle.decode(w.q8, w.kv8, w.block_table, w.lengths, w.q_scale, w.k_scale, w.sm_scale, rows=cal)
+    dt = time.perf_counter() - t
+    per_pair = dt / max(1.0, len(cal) * float(w.lengths[r0]))
+    want_pairs = target_s / max(per_pair, 1e-12)
+    if want_pairs >= keys_total:
+        rows = [(r, i) for r in range(R) for i in range(M)]
+        sample = f"all {R * M} rows"
+    else:
+        stride = max(1, int(np.ceil(keys_total / want_pairs)))
+        rows = [(r, i) for r in range(R) for i in range(M) if (r * M + i) % stride == 0]
+        sample = f"{len(rows)} of {R * M} rows (every {stride}th, request-major), full key sets"
+    pairs = float(sum(int(w.lengths[r]) for r, _ in rows))
+    t = time.perf_counter()
+    oracle.decode(w.q8, w.kv8, w.block_table, w.lengths, w.q_scale, w.k_scale, w.sm_scale, rows=rows)
+    dt = time.perf_counter() - t
+    full_s = dt * keys_total / max(pairs, 1.0)
+    return {"value": round(w.kv_bytes / full_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": f"{sample}; {dt:.1f} s measured, scaled to the workload",
+            "rows_per_s": round(R * M / full_s, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the per-GPU "
+              "path is the single-GPU kernel; sharding across GPUs is not part of it)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from absorbed_mla_split_amd import binding
+    from absorbed_mla_split_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    w = wl.generate(args.config)
+    if args.unfolded:
+        R, k, H = w.cfg.R, w.cfg.k, w.cfg.H
+        row_req = np.arange(R * k) // k
+        w = wl.Workload(w.cfg, w.lengths[row_req], w.block_table[row_req],
+                        w.q8.reshape(R * k, H, 576), w.kv8, w.q_scale, w.k_scale)
+    gen_s = time.perf_counter() - t0
+    R, M = w.R, w.M
+    q = torch.from_numpy(w.q8).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lengths = torch.from_numpy(w.lengths).to(dev)
+    kv0 = torch.from_numpy(w.kv8).to(dev)
+    pools = [kv0] + [kv0.clone() for _ in range(max(0, args.pools - 1))]
+    mode = binding.PLAN_FIXED if args.mode == "fixed" else binding.PLAN_BALANCED
+    dec = binding.FoldedDecoder(R, M, device=dev, mode=mode)
+    bmm1, bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
+    out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((R, M), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        dec.plan(lengths, bt.shape[1], stream)
+        if ev is not None:
+            ev[0].record(stream)
+        binding.folded_decode(q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2,
+                              dec.counts[:R], dec.offsets[:R + 1], dec.work, dec.workspace, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        binding.combine(dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params,
+                        dec.compute_units, out, lse, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    status = dec.device_status()
+    if status != 0:
+        print(f"device status {status}: {binding.status_string(status)}", file=sys.stderr)
+        sys.exit(1)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    decode_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    combine_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    dec_avg = float(np.mean(decode_ms))
+    comb_avg = float(np.mean(combine_ms))
+
+    # plan alone (once per decode step in a model, shared by its layers)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(20):
+        dec.plan(lengths, bt.shape[1], stream)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    plan_us = p0.elapsed_time(p1) / 20 * 1e3
+
+    kv_bytes = w.kv_bytes
+    pages = int(((w.lengths.astype(np.int64) + 63) // 64).sum())
+    dec_alg_bytes = kv_bytes + R * M * 576 + pages * 4
+    flops = 2.0 * M * float(w.lengths.astype(np.int64).sum()) * (576 + 512)
+    step_s = ms_per_step / 1e3
+    value = kv_bytes / step_s / 1e9
+    rows_per_s = R * M / step_s
+
+    mfma_bound = M >= 256
+    if mfma_bound:
+        achieved = flops / (dec_avg / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4)}
+    else:
+        achieved = dec_alg_bytes / (dec_avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "decode_kernel"
+    roof["traffic"] = traffic_for(args.config, args.mode, args.unfolded)
+    roof["algorithmic_bytes_per_launch"] = int(dec_alg_bytes)
+    roof["flops_per_launch"] = flops
+
+    cfg = w.cfg
+    workload = (f"{args.config}: R={cfg.R} k={cfg.k} H={cfg.H} (M={cfg.M}), {cfg.description}"
+                + (" [unfolded R*k rows]" if args.unfolded else ""))
+    res = {
+        "metric": "KV-cache HBM GB/s and folded query rows/s (R*k*H per s) per MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": workload, "requests": R, "rows_per_req": M,
+                   "kv_tokens": int(w.lengths.astype(np.int64).sum()), "page": 64,
+                   "plan": args.mode, "kv_pools_rotated": len(pools),
+                   "mtile": dec.params.mtile, "workers": dec.params.workers},
+        "rows_per_s": round(rows_per_s, 1),
+        "step_us": round(ms_per_step * 1e3, 2),
+        "decode_us": round(dec_avg * 1e3, 2),
+        "combine_us": round(comb_avg * 1e3, 2),
+        "plan_us": round(plan_us, 2),
+        "layer_kv_gbs": round(kv_bytes / ((dec_avg + comb_avg) / 1e3) / 1e9, 1),
+        "roofline": roof,
+        "wall_s": round(wall, 3),
+        "gen_s": round(gen_s, 1),
+        "source": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

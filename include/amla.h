@@ -1,0 +1,198 @@
+/*
+ * amla.h — C ABI of the folded split-KV absorbed-MLA decode for AMD MI355X (gfx950).
+ *
+ * The operation (page "vllm.models.kimi_k3.nvidia.specialized_decode.drafter.attention",
+ * module docstring; page "...cutedsl.mla.balanced", module docstring):
+ *
+ *   Absorbed MLA decode is MQA over a single latent KV head.  A speculative draft block of
+ *   k query tokens per request is non-causal: every token sees the request's whole cache.
+ *   The k tokens are folded into the head axis, q [R*k, H, 576] viewed as [R, k*H, 576]
+ *   (row i = t*H + h), so each request's paged FP8 latent cache is read once instead of
+ *   k times.  Each request's keys are split into a planned number of chunks; each chunk
+ *   yields FP32 partials plus a log2 LSE; a reducer merges them into BF16 out
+ *   [R, k*H, 512] and FP32 log2 LSE [R, k*H], the same memory order as the stock
+ *   [R*k, H, 512] / [R*k, H].
+ *
+ * Fixed geometry: pages of 64 tokens; a token row is 576 bytes of float8 E4M3FN (OCP),
+ * the 512 latent dims first, then the 64 rope dims; the value is the 512 latent dims.
+ *
+ * Calling convention for every entry point:
+ *   - pointers named d_* are device pointers, owned by the caller;
+ *   - the library never allocates device memory, never synchronises and keeps no global
+ *     state; all work is enqueued on `stream` (a hipStream_t, NULL = the null stream), so
+ *     the calls can be captured into a HIP graph;
+ *   - the return value is AMLA_OK (0) or a negative AMLA_ERR_* code; on error nothing has
+ *     been enqueued;
+ *   - values that only live on the device (lengths, block-table entries, the work list)
+ *     are checked by the kernels, which record a nonzero code in the workspace's device
+ *     status word (int32 at byte AMLA_WS_STATUS of the workspace) and skip the bad work
+ *     instead of reading out of bounds.
+ */
+#ifndef AMLA_H
+#define AMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AMLA_PAGE 64          /* tokens per cache page */
+#define AMLA_KDIM 576         /* bytes (E4M3 codes) per token row: 512 latent + 64 rope */
+#define AMLA_VDIM 512         /* value dims: the latent part */
+#define AMLA_MAX_ROWS 1024    /* most folded rows per request (k*H) */
+#define AMLA_MAX_REQS 4096    /* most requests one plan takes */
+#define AMLA_MAX_SPLITS 256   /* most splits per request */
+
+/* Host status codes. */
+#define AMLA_OK 0
+#define AMLA_ERR_INVALID (-1)   /* null pointer, size or parameter out of range */
+#define AMLA_ERR_WORKSPACE (-2) /* workspace smaller than amla_workspace_bytes() */
+#define AMLA_ERR_LIST (-3)      /* list_len < 2 * (num_reqs + workers) */
+#define AMLA_ERR_HIP (-4)       /* a kernel launch failed */
+
+/* Device status word (int32 at byte AMLA_WS_STATUS of the workspace), bit flags. */
+#define AMLA_WS_STATUS 0
+#define AMLA_DEV_BAD_LENGTH 1   /* plan: a length < 0 or more pages than table columns;
+                                   the plan is then empty (every count 0) */
+#define AMLA_DEV_BAD_PAGE 2     /* decode: a block-table entry outside [0, pool_pages) */
+#define AMLA_DEV_BAD_ITEM 4     /* decode: a work item or plan that does not match the call */
+
+/* Split-plan modes (page "...cutedsl.mla.balanced", module docstring). */
+#define AMLA_PLAN_BALANCED 0    /* split counts planned from the lengths */
+#define AMLA_PLAN_FIXED 1       /* every request in the same number of chunks */
+
+/*
+ * Plan / decode parameters; one value of this struct must be used for a plan and for the
+ * decode and combine calls that consume it.
+ *   rows_per_req      M = folded rows per request (k*H after folding), 1..AMLA_MAX_ROWS
+ *   mtile             MT = rows per decode work unit: 32, 64 or 128
+ *   workers           W = persistent decode workgroups (normally one per compute unit)
+ *   min_split_tokens  no split is planned shorter than this (rounded up to pages), >= 0
+ *   max_splits        most splits per request, 1..AMLA_MAX_SPLITS
+ *   mode              AMLA_PLAN_BALANCED or AMLA_PLAN_FIXED
+ */
+typedef struct amla_plan_params {
+    int32_t rows_per_req;
+    int32_t mtile;
+    int32_t workers;
+    int32_t min_split_tokens;
+    int32_t max_splits;
+    int32_t mode;
+} amla_plan_params;
+
+/*
+ * Fold plan of a decode batch (host only, no device work).
+ * Page "drafter.attention", sections foldable and fold_plan.
+ *   k_out:    query tokens per request when the batch folds, else 0: the batch must be
+ *             non-causal, num_rows == num_decode_tokens, num_rows divisible by
+ *             num_reqs with k >= 2, at least num_reqs block-table rows, and
+ *             max_query_len == k.
+ *   fold_out: tokens folded into one decode row (0 when k_out is 0): k without an LSE;
+ *             with one, the largest divisor f of k with f*heads <= max_fold_heads.
+ * Returns AMLA_ERR_INVALID for null outputs, heads < 1 or max_fold_heads < heads
+ * when an LSE is needed.
+ */
+int amla_fold_plan(int32_t causal, int32_t num_reqs, int32_t num_rows,
+                   int32_t num_decode_tokens, int32_t block_table_rows,
+                   int32_t max_query_len, int32_t heads, int32_t need_lse,
+                   int32_t max_fold_heads, int32_t *k_out, int32_t *fold_out);
+
+/*
+ * Scale composition of the stock decode for an FP8 cache (host only).
+ * Page "drafter.attention", section _scales: bmm1 = softmax_scale * q_scale * k_scale,
+ * bmm2 = k_scale.  Outputs in dequantised value units.
+ */
+int amla_bmm_scales(float softmax_scale, float q_scale, float k_scale,
+                    float *bmm1_out, float *bmm2_out);
+
+/*
+ * Decode launch shape for a device (host only): workers = compute_units (one persistent
+ * workgroup per CU), mtile = 32 for rows <= 32, 64 for rows <= 64, else 128.
+ */
+int amla_decode_config(int32_t compute_units, int32_t rows_per_req,
+                       int32_t *workers_out, int32_t *mtile_out);
+
+/*
+ * D512 bands per row for the reducer (host only).  Page "...cutedsl.mla.balanced",
+ * section reducer_d_tiles: 2 when ceil(2*rows/units) < 2*ceil(rows/units), else 1.
+ */
+int amla_reducer_bands(int32_t rows, int32_t compute_units, int32_t *bands_out);
+
+/*
+ * Workspace bytes for up to num_reqs requests (host only): a 256-byte header (device
+ * status, plan summary), then FP32 partials [num_reqs + workers][rows_per_req][512] and
+ * FP32 log2 LSE [num_reqs + workers][rows_per_req] (every plan has at most
+ * num_reqs + workers splits).  Returns 0 for arguments out of range.
+ */
+size_t amla_workspace_bytes(int32_t num_reqs, int32_t rows_per_req, int32_t workers);
+
+/*
+ * Plan the splits of one decode step from the KV lengths (one kernel, one workgroup).
+ * Page "...cutedsl.mla.balanced", module docstring and BalancedMla.plan: split counts are
+ * planned on the device from this step's lengths, once per step, and reused by every
+ * layer's decode.
+ *   d_lengths  int32 [num_reqs]: keys per request, including the draft block
+ *   bt_cols    columns of the block table (pages a request may have)
+ *   d_counts   int32 [num_reqs]  out: splits per request (0 for an empty request)
+ *   d_offsets  int32 [num_reqs+1] out: exclusive prefix sum; slot of split s of r is
+ *              offsets[r] + s; offsets[num_reqs] = items in the work list
+ *   d_work     int32 [list_len] out: (r, s) pairs, longest split first (ties: lower r,
+ *              then lower s), then -1
+ *   list_len   >= 2 * (num_reqs + workers)
+ *   d_workspace / ws_bytes: the workspace (header written here)
+ * The split rule: pages_r = ceil(L_r/64), mt = ceil(M/MT).  BALANCED: chunk = the
+ * smallest c >= 1 with mt * sum_r ceil(pages_r/c) <= W (the longest request if none),
+ * at least ceil(min_split_tokens/64); count_r = min(max_splits, ceil(pages_r/chunk)).
+ * FIXED: count_r = min(pages_r, clamp(floor(W/(R*mt)), 1, max_splits)).  Split s of r has
+ * q + (s < rem) pages starting at page s*q + min(s, rem), q = pages_r / count_r,
+ * rem = pages_r % count_r.
+ */
+int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols,
+                     const amla_plan_params *params, int32_t *d_counts, int32_t *d_offsets,
+                     int32_t *d_work, int32_t list_len, void *d_workspace, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Folded split-KV decode: one persistent kernel of `workers` workgroups walks the planned
+ * work list; every (request, split, row tile) stages its pages in LDS, computes S = Q K^T
+ * and O += P V on FP8 MFMA with an online softmax, and writes FP32 partials and the log2
+ * LSE of its split into the workspace.  Page "...cutedsl.mla.balanced", module docstring
+ * (FP32 split partials; the row max is kept lazily and P is fed to the MMA as E4M3).
+ *   d_q          E4M3 [num_reqs][rows_per_req][576], row i = t*H + h
+ *   d_kv         E4M3 [pool_pages][64][576]
+ *   d_block_table int32 [num_reqs][bt_stride]; entries for pages [0, ceil(L_r/64)) must
+ *                be in [0, pool_pages) (others are never read)
+ *   d_lengths    int32 [num_reqs] (the lengths the plan was made from)
+ *   bmm1_scale   softmax_scale * q_scale * k_scale;  bmm2_scale  k_scale
+ *   d_counts, d_offsets, d_work, list_len: the plan of amla_plan_splits with `params`
+ */
+int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                       const int32_t *d_block_table, int32_t bt_stride,
+                       const int32_t *d_lengths, int32_t num_reqs,
+                       const amla_plan_params *params, float bmm1_scale, float bmm2_scale,
+                       const int32_t *d_counts, const int32_t *d_offsets,
+                       const int32_t *d_work, int32_t list_len, void *d_workspace,
+                       size_t ws_bytes, void *stream);
+
+/*
+ * Reducer: merges each row's split partials (page "drafter.attention", DraftDcp: exp2
+ * weights of lse_s - max over their sum, in FP32, one BF16 rounding) into
+ *   d_out  BF16 (uint16 bits, round to nearest even) [num_reqs][rows_per_req][512]
+ *   d_lse  FP32 log2 LSE [num_reqs][rows_per_req]
+ * Requests with count 0 get out = 0 and lse = -inf.  compute_units feeds
+ * amla_reducer_bands.
+ */
+int amla_combine(const void *d_workspace, size_t ws_bytes, const int32_t *d_counts,
+                 const int32_t *d_offsets, int32_t num_reqs, const amla_plan_params *params,
+                 int32_t compute_units, uint16_t *d_out, float *d_lse, void *stream);
+
+/* Static text for a host status code or a device status word. */
+const char *amla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AMLA_H */

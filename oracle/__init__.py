@@ -37,6 +37,8 @@ def _load():
         i32p = ctypes.POINTER(ctypes.c_int32)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         f64p = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_table.restype = None
@@ -62,6 +64,11 @@ def _load():
 
 def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def threads() -> int:
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 # --------------------------------------------------------------------------- E4M3FN

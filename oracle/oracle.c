@@ -42,9 +42,17 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <omp.h>
+
 #define ORACLE_PAGE 64
 #define ORACLE_KDIM 576
 #define ORACLE_VDIM 512
+
+/* Threads the oracle's parallel loops use (OpenMP's current maximum). */
+int oracle_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ---------------------------------------------------------------- E4M3FN */
 

@@ -1,0 +1,175 @@
+"""The C ABI on the host: the library loads, exports what include/amla.h declares, and its
+host-only functions and argument checks behave as documented.  No device work is launched
+here (every call either is host-only or is rejected before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from absorbed_mla_split_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "amla.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "fold_examples.txt")
+
+
+def golden(kind):
+    out = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if line and not line.startswith("#") and line.split()[0] == kind:
+            out.append([int(v) for v in line.split()[1:]])
+    return out
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(amla_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.load()
+    names = declared_functions()
+    assert set(names) == set(b.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (AMLA_\w+) \(?(-?\d+)\)?", text))
+    assert int(consts["AMLA_PAGE"]) == b.PAGE and int(consts["AMLA_KDIM"]) == b.KDIM
+    assert int(consts["AMLA_VDIM"]) == b.VDIM and int(consts["AMLA_MAX_ROWS"]) == b.MAX_ROWS
+    assert int(consts["AMLA_MAX_REQS"]) == b.MAX_REQS
+    assert int(consts["AMLA_ERR_WORKSPACE"]) == b.ERR_WORKSPACE
+    assert int(consts["AMLA_DEV_BAD_PAGE"]) == b.DEV_BAD_PAGE
+    assert int(consts["AMLA_PLAN_FIXED"]) == b.PLAN_FIXED
+
+
+def test_fold_plan_pages_examples():
+    for k, heads, need_lse, cap, expect in golden("fold_plan"):
+        kk, f = b.fold_plan(False, 2, 2 * k, 2 * k, 2, k, heads, need_lse, cap)
+        assert kk == k and f == expect
+    for causal, reqs, rows, tokens, bt_rows, mql, expect in golden("foldable"):
+        kk, f = b.fold_plan(causal, reqs, rows, tokens, bt_rows, mql, 8, True, 128)
+        assert kk == expect and (f == 0) == (expect == 0)
+
+
+def test_fold_plan_matches_oracle_rules():
+    import oracle
+
+    for causal in (0, 1):
+        for reqs in (1, 2, 3):
+            for rows in (2, 4, 6, 8, 12):
+                for mql in (1, 2, 4, 6):
+                    for heads in (8, 64):
+                        for need_lse in (0, 1):
+                            k = oracle.foldable(bool(causal), reqs, rows, rows, reqs, mql)
+                            kk, f = b.fold_plan(causal, reqs, rows, rows, reqs, mql, heads,
+                                                need_lse, 128)
+                            assert kk == k
+                            if k:
+                                assert f == oracle.fold_plan(k, heads, bool(need_lse), 128)
+
+
+def test_reducer_bands_pages_example_and_formula():
+    for rows, units, expect in golden("reducer_bands"):
+        assert b.reducer_bands(rows, units) == expect
+    # the rule returns 2 when the rows fill at most half the units, and just above each
+    # whole wave (the docstring and the formula differ there; the formula is followed)
+    assert b.reducer_bands(74, 148) == 2
+    assert b.reducer_bands(75, 148) == 1
+    assert b.reducer_bands(148, 148) == 1
+    assert b.reducer_bands(200, 148) == 2
+
+
+def test_bmm_scales_composition():
+    b1, b2 = b.bmm_scales(0.125, 0.5, 0.25)
+    assert b1 == pytest.approx(0.125 * 0.5 * 0.25) and b2 == 0.25
+
+
+def test_decode_config():
+    assert b.decode_config(256, 32) == (256, 32)
+    assert b.decode_config(256, 56) == (256, 64)
+    assert b.decode_config(256, 256) == (256, 128)
+    assert b.decode_config(256, 448) == (256, 128)
+    with pytest.raises(b.AmlaError):
+        b.decode_config(256, 0)
+    with pytest.raises(b.AmlaError):
+        b.decode_config(0, 32)
+
+
+def test_workspace_bytes_formula():
+    # header 256 B + FP32 partials (R+W)*M*512*4 + FP32 LSE (R+W)*M*4 rounded to 256 B
+    R, M, W = 64, 32, 256
+    lse = ((R + W) * M * 4 + 255) // 256 * 256
+    assert b.workspace_bytes(R, M, W) == 256 + (R + W) * M * 512 * 4 + lse
+    assert b.workspace_bytes(-1, 32, 256) == 0
+    assert b.workspace_bytes(4, 0, 256) == 0
+    assert b.workspace_bytes(b.MAX_REQS + 1, 32, 256) == 0
+
+
+def _call_plan(lib, lengths=1, reqs=2, cols=4, params=None, counts=1, offsets=1, work=1,
+               list_len=1024, ws=1, ws_bytes=1 << 30):
+    p = params if params is not None else b.make_params(32, 32, 256)
+    vp = ctypes.c_void_p
+    return lib.amla_plan_splits(vp(lengths), reqs, cols, ctypes.byref(p), vp(counts), vp(offsets),
+                                vp(work), list_len, vp(ws), ws_bytes, None)
+
+
+def test_plan_argument_errors():
+    lib = b.load()
+    assert _call_plan(lib, lengths=0) == b.ERR_INVALID
+    assert _call_plan(lib, offsets=0) == b.ERR_INVALID
+    assert _call_plan(lib, ws=0) == b.ERR_INVALID
+    assert _call_plan(lib, reqs=-1) == b.ERR_INVALID
+    assert _call_plan(lib, reqs=b.MAX_REQS + 1) == b.ERR_INVALID
+    assert _call_plan(lib, params=b.make_params(32, 48, 256)) == b.ERR_INVALID     # mtile
+    assert _call_plan(lib, params=b.make_params(0, 32, 256)) == b.ERR_INVALID
+    assert _call_plan(lib, params=b.make_params(b.MAX_ROWS + 1, 128, 256)) == b.ERR_INVALID
+    assert _call_plan(lib, params=b.make_params(32, 32, 256, mode=7)) == b.ERR_INVALID
+    assert _call_plan(lib, params=b.make_params(32, 32, 256, max_splits=0)) == b.ERR_INVALID
+    assert _call_plan(lib, ws_bytes=100) == b.ERR_WORKSPACE
+    assert _call_plan(lib, list_len=2 * (2 + 256) - 1) == b.ERR_LIST
+
+
+def test_decode_and_combine_argument_errors():
+    lib = b.load()
+    p = b.make_params(32, 32, 256)
+    vp = ctypes.c_void_p
+    good = dict(q=1, kv=1, pool=16, bt=1, stride=4, lengths=1, reqs=2, b1=1.0, b2=1.0, counts=1,
+                offsets=1, work=1, list_len=1024, ws=1, ws_bytes=1 << 30)
+
+    def dec(**kw):
+        a = dict(good, **kw)
+        return lib.amla_folded_decode(vp(a["q"]), vp(a["kv"]), a["pool"], vp(a["bt"]), a["stride"],
+                                      vp(a["lengths"]), a["reqs"], ctypes.byref(p), a["b1"], a["b2"],
+                                      vp(a["counts"]), vp(a["offsets"]), vp(a["work"]),
+                                      a["list_len"], vp(a["ws"]), a["ws_bytes"], None)
+
+    for bad in (dict(q=0), dict(kv=0), dict(bt=0), dict(lengths=0), dict(counts=0),
+                dict(offsets=0), dict(work=0), dict(ws=0), dict(pool=0), dict(stride=0),
+                dict(reqs=-1), dict(b1=float("nan")), dict(b2=float("inf"))):
+        assert dec(**bad) == b.ERR_INVALID, bad
+    assert dec(ws_bytes=10) == b.ERR_WORKSPACE
+    assert dec(list_len=10) == b.ERR_LIST
+    assert dec(reqs=0) == b.OK            # nothing to do, nothing launched
+
+    def comb(ws=1, ws_bytes=1 << 30, counts=1, offsets=1, reqs=2, cus=256, out=1, lse=1):
+        return lib.amla_combine(vp(ws), ws_bytes, vp(counts), vp(offsets), reqs, ctypes.byref(p), cus,
+                                vp(out), vp(lse), None)
+
+    for bad in (dict(ws=0), dict(counts=0), dict(offsets=0), dict(out=0), dict(lse=0),
+                dict(cus=0), dict(reqs=-1)):
+        assert comb(**bad) == b.ERR_INVALID, bad
+    assert comb(ws_bytes=10) == b.ERR_WORKSPACE
+    assert comb(reqs=0) == b.OK
+
+
+def test_status_strings():
+    for code in (b.OK, b.ERR_INVALID, b.ERR_WORKSPACE, b.ERR_LIST, b.ERR_HIP, b.DEV_BAD_LENGTH,
+                 b.DEV_BAD_PAGE, b.DEV_BAD_ITEM):
+        assert b.status_string(code) and b.status_string(code) != "unknown status"
+    assert b.status_string(-99) == "unknown status"

@@ -1,0 +1,167 @@
+"""GPU folded split-KV decode + combine vs the CPU oracle, element by element.
+
+Small cases (every row) span several 64-key pages, ragged tails, empty requests, several
+splits per request and every row-tile shape; the five workload configurations run at full
+size in the benchmark's launch configuration and are checked on sampled rows.  Inputs
+carry NaN codes in every cache slot past a request's length and in unused pages, and the
+outputs, LSE and workspace start as NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from absorbed_mla_split_amd import binding
+from absorbed_mla_split_amd import workloads as wl
+from gpu_util import compare, run_gpu, sample_rows, to_dev, ws_partials, vmax, OUT_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def test_c1_every_row():
+    w = wl.generate("c1")
+    out, lse, dec = run_gpu(w)
+    counts, offsets, work, n = dec.plan_host()
+    assert counts.tolist() == [1, 2]             # 4 pages; 5 pages cut in two
+    compare(w, out, lse, tag="c1")
+    assert dec.device_status() == 0
+
+
+def test_c1_split_partials_match_oracle_chunks():
+    w = wl.generate("c1")
+    out, lse, dec = run_gpu(w)
+    counts, offsets, work, n = dec.plan_host()
+    part, plse = ws_partials(dec, w)
+    vm = vmax(w)
+    for r in range(w.R):
+        for s in range(counts[r]):
+            a, b = oracle.split_range(w.lengths[r], counts[r], s)
+            tasks = [(r, i, a, b) for i in range(w.M)]
+            ro, rl = oracle.attend(w.q8, w.kv8, w.block_table, w.lengths, tasks, w.q_scale,
+                                   w.k_scale, w.sm_scale)
+            slot = offsets[r] + s
+            err = np.max(np.abs(part[slot] - ro))
+            assert err <= OUT_TOL * vm, (r, s, err)
+            assert np.max(np.abs(plse[slot] - rl)) <= 1e-3, (r, s)
+
+
+SHAPES = [
+    # (k, H, lengths)
+    (4, 2, [1, 63, 64, 65]),
+    (4, 8, [200, 317, 0, 1000]),
+    (7, 8, [513, 2047, 64 * 9 + 5]),
+    (2, 32, [130, 1]),
+    (3, 32, [700, 0, 0, 129]),
+    (4, 64, [1500, 64]),
+    (7, 64, [1025, 3000]),
+    (1, 3, [77, 500]),
+]
+
+
+@pytest.mark.parametrize("k,H,lengths", SHAPES)
+@pytest.mark.parametrize("min_split_tokens", [0, 256])
+def test_small_shapes_every_row(k, H, lengths, min_split_tokens):
+    w = wl.small(len(lengths), k, H, lengths, seed=k * 100 + H)
+    out, lse, dec = run_gpu(w, min_split_tokens=min_split_tokens)
+    compare(w, out, lse, tag=f"k{k}H{H}L{lengths}ms{min_split_tokens}")
+    assert dec.device_status() == 0
+
+
+def test_many_splits_small_workers():
+    # few workers and no minimum split: long requests cut into many 1-page splits
+    w = wl.small(3, 4, 8, [2000, 64 * 40, 90], seed=3)
+    out, lse, _ = run_gpu(w, min_split_tokens=0, workers=96)
+    compare(w, out, lse, tag="many-splits")
+
+
+@pytest.mark.parametrize("mode", [binding.PLAN_BALANCED, binding.PLAN_FIXED])
+def test_plans_agree(mode):
+    w = wl.small(5, 7, 8, [3000, 100, 6000, 64, 9000], seed=2)
+    out, lse, _ = run_gpu(w, mode=mode)
+    compare(w, out, lse, tag=f"mode{mode}")
+
+
+def test_fold_equals_unfolded_rows():
+    # [R*k, H, D] folded to [R, k*H, D] vs the stock layout: R*k requests of H rows with
+    # row-replicated block tables and lengths.
+    R, k, H = 3, 4, 8
+    w = wl.small(R, k, H, [900, 333, 1200], seed=11)
+    out_f, lse_f, _ = run_gpu(w)
+    row_req = np.arange(R * k) // k
+    wu = wl.Workload(w.cfg, w.lengths[row_req], w.block_table[row_req],
+                     w.q8.reshape(R * k, H, 576), w.kv8, w.q_scale, w.k_scale)
+    out_u, lse_u, _ = run_gpu(wu)
+    vm = vmax(w)
+    assert np.max(np.abs(out_f.reshape(R * k, H, 512) - out_u)) <= OUT_TOL * vm
+    assert np.max(np.abs(lse_f.reshape(R * k, H) - lse_u)) <= 1e-3
+    compare(wu, out_u, lse_u, tag="unfolded")
+
+
+def test_deterministic_bitwise():
+    w = wl.small(4, 4, 16, [5000, 700, 64, 2500], seed=4)
+    t = to_dev(w)
+    a = run_gpu(w, tensors=t)
+    b = run_gpu(w, tensors=t)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_empty_batch_rows():
+    w = wl.small(3, 2, 8, [0, 0, 0], seed=1)
+    out, lse, dec = run_gpu(w)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_bad_page_id_flags_status_without_fault():
+    w = wl.small(2, 4, 8, [300, 200], seed=6)
+    w.block_table[1, 1] = w.kv8.shape[0] + 1000          # out of the pool
+    out, lse, dec = run_gpu(w)
+    assert dec.device_status() & binding.DEV_BAD_PAGE
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
+def test_full_size_sampled(cfg):
+    w = wl.generate(cfg)
+    out, lse, dec = run_gpu(w)
+    assert dec.device_status() == 0
+    compare(w, out, lse, rows=sample_rows(w, 4 if cfg != "c3" else 2), tag=cfg)
+
+
+def test_c5_unfolded_baseline_sampled():
+    # the stock flattening of c5: 112 single-token requests of 64 heads, each with its own
+    # copy of the request's table (k times the KV reads)
+    w = wl.generate("c5")
+    R, k, H = w.cfg.R, w.cfg.k, w.cfg.H
+    row_req = np.arange(R * k) // k
+    wu = wl.Workload(w.cfg, w.lengths[row_req], w.block_table[row_req],
+                     w.q8.reshape(R * k, H, 576), w.kv8, w.q_scale, w.k_scale)
+    out, lse, _ = run_gpu(wu)
+    rows = [(rr, i) for rr in (0, 3, 6, 7, 50, 111) for i in (0, 17, 63)]
+    compare(wu, out, lse, rows=rows, tag="c5-unfolded")
+
+
+def test_graph_capture_replay():
+    w = wl.small(4, 4, 8, [3000, 1000, 64, 2200], seed=8)
+    q, kv, bt, lengths = to_dev(w)
+    dec = binding.FoldedDecoder(w.R, w.M)
+    bmm1, bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
+    out = torch.empty((w.R, w.M, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.R, w.M), dtype=torch.float32, device="cuda")
+    dec.plan(lengths, bt.shape[1])
+    dec.decode(q, kv, bt, lengths, bmm1, bmm2, out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dec.plan(lengths, bt.shape[1])
+            dec.decode(q, kv, bt, lengths, bmm1, bmm2, out, lse)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
