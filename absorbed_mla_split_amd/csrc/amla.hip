@@ -41,7 +41,7 @@ constexpr int kSlots = 4;                      // LDS page ring
 constexpr int kDecodeThreads = 256;            // 4 waves
 constexpr int kChunksPerWave = kPageBytes / (4 * 1024);  // 9 x 1 KiB DMA per wave per page
 constexpr int kHeaderBytes = 256;
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kMaxRuns = 2 * AMLA_MAX_REQS;    // two split-size runs per request
 constexpr float kLog2e = 1.4426950408889634f;
 // Lazy max: the running row max is only raised when a page's max exceeds it by more
@@ -110,29 +110,54 @@ __device__ inline T wave_max(T v)
     return v;
 }
 
-// Sum over the 1024-thread plan workgroup; every thread gets the total.
-__device__ int64_t block_sum64(int64_t v, int64_t *scratch)
+// All-lane reductions of a wave without LDS traffic: DPP within rows of 16 lanes, then
+// v_permlane16_swap / v_permlane32_swap across rows.  64-bit values move as two halves.
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp64(int64_t v)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_sum(v);
-    __syncthreads();
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    int64_t t = 0;
-    for (int i = 0; i < kPlanThreads / 64; ++i) t += scratch[i];
-    return t;
+    const int lo = __builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((int64_t)hi << 32) | (uint32_t)lo;
 }
 
-__device__ int64_t block_max64(int64_t v, int64_t *scratch)
+template <bool MAX>
+__device__ __forceinline__ int64_t op64(int64_t a, int64_t b)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_max(v);
-    __syncthreads();
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    int64_t t = scratch[0];
-    for (int i = 1; i < kPlanThreads / 64; ++i) t = scratch[i] > t ? scratch[i] : t;
-    return t;
+    return MAX ? (a > b ? a : b) : a + b;
+}
+
+template <bool MAX>
+__device__ int64_t wave_all64(int64_t v)
+{
+    v = op64<MAX>(v, dpp64<0x128>(v));   // row_ror:8
+    v = op64<MAX>(v, dpp64<0x124>(v));   // row_ror:4
+    v = op64<MAX>(v, dpp64<0x4e>(v));    // quad_perm [2,3,0,1]
+    v = op64<MAX>(v, dpp64<0xb1>(v));    // quad_perm [1,0,3,2]
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = op64<MAX>(((int64_t)hi[0] << 32) | lo[0], ((int64_t)hi[1] << 32) | lo[1]);
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = op64<MAX>(((int64_t)hi[0] << 32) | lo[0], ((int64_t)hi[1] << 32) | lo[1]);
+    }
+    return v;
+}
+
+template <bool MAX>
+__device__ float wave_allf(float v)
+{
+    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false)));
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false)));
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false)));
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false)));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Exclusive scan over the workgroup of one value per thread (thread order); returns the
@@ -177,65 +202,127 @@ __device__ inline uint64_t run_key(int64_t size, int32_t r)
     return ((uint64_t)(0x7FFFFFFFll - size) << 32) | (uint32_t)r;
 }
 
+// Reduces four values over the workgroup at once (max, max, sum, sum).
+__device__ void block_reduce4(int64_t &mx0, int64_t &mx1, int64_t &sm0, int64_t &sm1,
+                              int64_t (*scratch)[4])
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    mx0 = wave_all64<true>(mx0);
+    mx1 = wave_all64<true>(mx1);
+    sm0 = wave_all64<false>(sm0);
+    sm1 = wave_all64<false>(sm1);
+    if (lane == 0) {
+        scratch[wave][0] = mx0;
+        scratch[wave][1] = mx1;
+        scratch[wave][2] = sm0;
+        scratch[wave][3] = sm1;
+    }
+    __syncthreads();
+    mx0 = mx1 = sm0 = sm1 = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+        mx0 = scratch[w][0] > mx0 ? scratch[w][0] : mx0;
+        mx1 = scratch[w][1] > mx1 ? scratch[w][1] : mx1;
+        sm0 += scratch[w][2];
+        sm1 += scratch[w][3];
+    }
+}
+
+constexpr int kRankSortRuns = kPlanThreads;   // rank sort up to this many runs, else bitonic
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
 {
-    __shared__ uint64_t keys[kMaxRuns];
-    __shared__ int64_t red64[kPlanThreads / 64];
+    __shared__ int32_t pg[AMLA_MAX_REQS];            // pages per request
+    __shared__ int32_t cnt[AMLA_MAX_REQS];           // splits per request
+    __shared__ uint64_t keys[kMaxRuns];              // run keys (sorted in place: bitonic)
+    __shared__ uint64_t ranked[kRankSortRuns];       // run keys in order (rank sort)
+    __shared__ int64_t red4[kPlanThreads / 64][4];
     __shared__ int32_t red32[kPlanThreads / 64];
-    const int tid = threadIdx.x;
+    __shared__ int32_t ok[2][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = a.reqs;
     const int64_t mt = ceil_div(a.rows, a.mtile);
+    const int64_t budget = (int64_t)a.workers / mt;  // most splits the workers take at once
 
-    // 1. validate lengths, longest request
-    int64_t bad = 0, pmax = 0;
+    // 1. pages per request, validity, longest request, total pages, non-empty requests
+    int64_t bad = 0, pmax = 0, total = 0, nz = 0;
     for (int r = tid; r < R; r += kPlanThreads) {
         const int32_t L = a.lengths[r];
         const int64_t p = pages_of(L);
-        if (L < 0 || p > a.bt_cols) bad = 1;
+        const bool b = L < 0 || p > a.bt_cols;
+        bad |= b;
+        pg[r] = b ? 0 : (int32_t)p;
         pmax = p > pmax ? p : pmax;
+        total += b ? 0 : p;
+        nz += (!b && p > 0);
     }
-    bad = block_max64(bad, red64);
-    pmax = block_max64(pmax, red64);
+    block_reduce4(bad, pmax, total, nz, red4);
 
-    // 2. split chunk (BALANCED) or fixed split count
+    // 2. BALANCED: the smallest chunk c with sum_r ceil(pages_r / c) <= budget.  Since
+    //    total/c <= sum <= total/c + nz, it lies in [ceil(total/budget),
+    //    ceil(total/(budget - nz))]; a 16-way search (one candidate per wave) narrows that.
     int64_t chunk = 1, fixed = 1;
-    if (!bad && a.mode == AMLA_PLAN_BALANCED) {
-        int64_t lo = 1, hi = pmax > 0 ? pmax : 1;
-        // units(c) = mt * sum_r ceil(p_r / c) is non-increasing in c: smallest c that fits.
-        auto units = [&](int64_t c) {
-            int64_t u = 0;
-            for (int r = tid; r < R; r += kPlanThreads) u += (pages_of(a.lengths[r]) + c - 1) / c;
-            return block_sum64(u, red64) * mt;
-        };
-        if (units(hi) <= a.workers) {
-            while (lo < hi) {
-                const int64_t mid = lo + (hi - lo) / 2;
-                if (units(mid) <= a.workers) hi = mid; else lo = mid + 1;
+    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
+        if (budget < nz) {
+            chunk = pmax;                         // no chunk fits: one split per request
+        } else {
+            int64_t lo = (total + budget - 1) / budget, hi = pmax;
+            if (budget > nz) {
+                const int64_t h = (total + (budget - nz) - 1) / (budget - nz);
+                hi = h < hi ? h : hi;
             }
+            lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
+            constexpr int kCand = 16, kPerWave = kCand / (kPlanThreads / 64);
+            int round = 0;
+            while (lo < hi) {
+                const int64_t span = hi - lo;
+#pragma unroll
+                for (int k = 0; k < kPerWave; ++k) {
+                    const int cand = wave * kPerWave + k;
+                    const uint32_t c = (uint32_t)(lo + span * cand / kCand);
+                    int64_t u = 0;
+                    for (int r = lane; r < R; r += 64) u += ((uint32_t)pg[r] + c - 1u) / c;
+                    u = wave_all64<false>(u);
+                    if (lane == 0) ok[round & 1][cand] = u <= budget;
+                }
+                __syncthreads();
+                int first = -1;
+                for (int w = kCand - 1; w >= 0; --w)
+                    if (ok[round & 1][w]) first = w;
+                if (first >= 0) {
+                    const int64_t cf = lo + span * first / kCand;
+                    const int64_t cp = first > 0 ? lo + span * (first - 1) / kCand + 1 : lo;
+                    hi = cf;
+                    lo = cp < cf ? cp : cf;
+                } else {
+                    lo = lo + span * (kCand - 1) / kCand + 1;
+                }
+                ++round;
+            }
+            chunk = hi;
         }
-        chunk = hi > a.min_pages ? hi : a.min_pages;
-        if (chunk < 1) chunk = 1;
-    } else if (!bad) {
+        chunk = chunk > a.min_pages ? chunk : a.min_pages;
+    } else if (!bad && a.mode == AMLA_PLAN_FIXED) {
         fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
         fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
     }
 
-    // 3. counts and offsets: thread t owns requests [t*per, (t+1)*per)
+    // 3. counts and their exclusive scan: thread t owns requests [t*per, (t+1)*per)
     const int per = ceil_div(R > 0 ? R : 1, kPlanThreads);
     int32_t mine = 0;
     for (int i = 0; i < per; ++i) {
         const int r = tid * per + i;
         if (r >= R) break;
-        const int64_t p = pages_of(a.lengths[r]);
+        const uint32_t p = (uint32_t)pg[r];
         int64_t c = 0;
         if (!bad && p > 0) {
             if (a.mode == AMLA_PLAN_BALANCED) {
-                c = (p + chunk - 1) / chunk;
+                c = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
                 c = c < a.max_splits ? c : a.max_splits;
             } else {
-                c = p < fixed ? p : fixed;
+                c = (int64_t)p < fixed ? (int64_t)p : fixed;
             }
         }
+        cnt[r] = (int32_t)c;
         a.counts[r] = (int32_t)c;
         mine += (int32_t)c;
     }
@@ -245,84 +332,91 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
         const int r = tid * per + i;
         if (r >= R) break;
         a.offsets[r] = run;
-        const int64_t p = pages_of(a.lengths[r]);
-        int64_t c = 0;
-        if (!bad && p > 0) {
-            if (a.mode == AMLA_PLAN_BALANCED) {
-                c = (p + chunk - 1) / chunk;
-                c = c < a.max_splits ? c : a.max_splits;
-            } else {
-                c = p < fixed ? p : fixed;
-            }
-        }
-        run += (int32_t)c;
+        run += cnt[r];
     }
     if (tid == 0) a.offsets[R] = n_items;
 
-    // 4. runs of equal-size splits: (q+1) x rem from s = 0, then q x (c - rem) from s = rem
-    int n = 2;
-    while (n < 2 * R) n <<= 1;
-    for (int i = tid; i < n; i += kPlanThreads) keys[i] = ~0ull;
-    __syncthreads();
-    for (int r = tid; r < R && !bad; r += kPlanThreads) {
-        const int64_t p = pages_of(a.lengths[r]);
-        if (p == 0) continue;
-        int64_t c;
-        if (a.mode == AMLA_PLAN_BALANCED) {
-            c = (p + chunk - 1) / chunk;
-            c = c < a.max_splits ? c : a.max_splits;
-        } else {
-            c = p < fixed ? p : fixed;
+    // 4. runs of equal-size splits, (q+1) x rem from s = 0 then q x (c-rem) from s = rem,
+    //    keyed (size descending, request ascending), sorted ascending
+    const int runs = 2 * R;
+    const uint64_t *sorted;
+    auto key_of = [&](int x) -> uint64_t {
+        const int r = x >> 1;
+        const int c = cnt[r];
+        if (c == 0) return ~0ull;
+        const int q = pg[r] / c, rem = pg[r] % c;
+        if ((x & 1) == 0) return rem > 0 ? run_key(q + 1, r) : ~0ull;
+        return run_key(q, r);
+    };
+    if (runs <= kRankSortRuns) {
+        const uint64_t mykey = tid < runs ? key_of(tid) : ~0ull;
+        if (tid < runs) keys[tid] = mykey;
+        __syncthreads();
+        if (tid < runs && mykey != ~0ull) {
+            int rank = 0;
+            for (int y = 0; y < runs; ++y) rank += keys[y] < mykey;
+            ranked[rank] = mykey;
         }
-        const int64_t q = p / c, rem = p % c;
-        if (rem > 0) keys[2 * r] = run_key(q + 1, r);
-        keys[2 * r + 1] = run_key(q, r);
-    }
-    __syncthreads();
-
-    // 5. bitonic sort of the run keys, ascending
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < n; i += kPlanThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint64_t x = keys[i], y = keys[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((x > y) == up) {
-                        keys[i] = y;
-                        keys[ixj] = x;
+        // empty runs sort last: fill the tail so the positions below see count 0
+        int nonempty = 0;
+        {
+            int64_t z0 = 0, z1 = 0, e0 = (tid < runs && mykey != ~0ull), e1 = 0;
+            block_reduce4(z0, z1, e0, e1, red4);
+            nonempty = (int)e0;
+        }
+        for (int i = nonempty + tid; i < kRankSortRuns; i += kPlanThreads) ranked[i] = ~0ull;
+        __syncthreads();
+        sorted = ranked;
+    } else {
+        int n = 2;
+        while (n < runs) n <<= 1;
+        for (int x = tid; x < n; x += kPlanThreads) keys[x] = x < runs ? key_of(x) : ~0ull;
+        __syncthreads();
+        for (int k = 2; k <= n; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < n; i += kPlanThreads) {
+                    const int ixj = i ^ j;
+                    if (ixj > i) {
+                        const uint64_t x = keys[i], y = keys[ixj];
+                        const bool up = (i & k) == 0;
+                        if ((x > y) == up) {
+                            keys[i] = y;
+                            keys[ixj] = x;
+                        }
                     }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
+        sorted = keys;
     }
 
-    // 6. positions of the runs in sorted order, then the (r, s) pairs
-    const int per_run = n / kPlanThreads > 0 ? n / kPlanThreads : 1;
-    int32_t cnt_local[kMaxRuns / kPlanThreads > 0 ? kMaxRuns / kPlanThreads : 1];
-    int32_t s0_local[kMaxRuns / kPlanThreads > 0 ? kMaxRuns / kPlanThreads : 1];
-    int32_t r_local[kMaxRuns / kPlanThreads > 0 ? kMaxRuns / kPlanThreads : 1];
+    // 5. positions of the runs in sorted order, then the (r, s) pairs
+    int n_sorted = 2;
+    while (n_sorted < runs) n_sorted <<= 1;
+    if (runs <= kRankSortRuns) n_sorted = kRankSortRuns;
+    const int per_run = n_sorted / kPlanThreads > 0 ? n_sorted / kPlanThreads : 1;
+    constexpr int kMaxPerRun = kMaxRuns / kPlanThreads;
+    int32_t cnt_local[kMaxPerRun], s0_local[kMaxPerRun], r_local[kMaxPerRun];
     int32_t my_items = 0;
     for (int i = 0; i < per_run; ++i) {
         const int idx = tid * per_run + i;
         cnt_local[i] = 0;
         s0_local[i] = 0;
         r_local[i] = 0;
-        if (idx >= n) continue;
-        const uint64_t key = keys[idx];
+        if (idx >= n_sorted) continue;
+        const uint64_t key = sorted[idx];
         if (key == ~0ull) continue;
         const int64_t size = 0x7FFFFFFFll - (int64_t)(key >> 32);
         const int32_t r = (int32_t)(key & 0xFFFFFFFFu);
-        const int64_t p = pages_of(a.lengths[r]);
-        const int32_t c = a.counts[r];
-        const int64_t q = p / c, rem = p % c;
+        const int32_t c = cnt[r];
+        const int32_t q = pg[r] / c, rem = pg[r] % c;
         if (rem > 0 && size == q + 1) {
-            cnt_local[i] = (int32_t)rem;
+            cnt_local[i] = rem;
             s0_local[i] = 0;
         } else {
-            cnt_local[i] = (int32_t)(c - rem);
-            s0_local[i] = (int32_t)rem;
+            cnt_local[i] = c - rem;
+            s0_local[i] = rem;
         }
         r_local[i] = r;
         my_items += cnt_local[i];
@@ -385,32 +479,84 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
-// This wave's 9 KiB share of one page, HBM -> LDS, 16 B per lane per instruction
-// (global_load_lds_dwordx4: lane i's 16 bytes land at M0 + 16*i).  Issued as inline asm
-// so that the compiler does not count these loads: otherwise it waits for all of them
-// before every transposed LDS read.  Completion is awaited explicitly with s_waitcnt
-// vmcnt before the barrier that publishes a page.  The s_nop covers the SALU-write-M0 ->
-// LDS-DMA hazard.
-__device__ __forceinline__ void issue_page(const uint8_t *kv, int64_t page, uint8_t *slot, int wave,
-                                           int lane)
+// LDS page layout: token row t occupies bytes [576t, 576t+576) of its slot, and within
+// the row the 16-byte chunk c is stored at chunk position c ^ ((t >> 2) & 3).  Rows are
+// 576 B apart, so without the swizzle 16 lanes reading one chunk of 16 consecutive rows
+// hit only 4 of the 16 bank groups; with it they hit all 16, and so do the transposed V
+// reads (8 keys x 2 chunks per 16 lanes).
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// One wave's 9 KiB share of a page, HBM -> LDS (global_load_lds_dwordx4: lane i's 16 bytes
+// land at M0 + 16*i, the source is the page base in SGPRs plus the lane's offset).  LDS
+// chunk position p of the slot receives the page's chunk (p / 36, (p % 36) ^ swz(p / 36));
+// the per-lane source offsets are the same for every page and are computed once.  Issued as
+// inline asm so that the compiler does not count these loads (it would otherwise wait for
+// all of them before every transposed LDS read); completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes a page.  The s_nop covers the
+// SALU-write-M0 -> LDS-DMA hazard.  M0 is not listed as clobbered (clang reserves it); no
+// compiler-generated code in these kernels reads M0.
+struct DmaOffsets {
+    uint32_t v[(kChunksPerWave + 1) / 2];   // two 16-bit offsets per register
+    __device__ __forceinline__ uint32_t get(int i) const
+    {
+        return (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
+    }
+};
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane)
 {
-    const uint8_t *src = kv + page * kPageBytes + wave * (kChunksPerWave * 1024) + lane * 16;
-    const uint32_t dst = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)slot + wave * (kChunksPerWave * 1024);
+    DmaOffsets o;
+#pragma unroll
+    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) o.v[i] = 0;
 #pragma unroll
     for (int i = 0; i < kChunksPerWave; ++i) {
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + i * 1024);
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(src + i * 1024), "s"(m0)
-                     : "memory", "m0");
+        const int p = (wave * kChunksPerWave + i) * 64 + lane;
+        const int row = p / (kKDim / 16), q = p - row * (kKDim / 16);
+        o.v[i >> 1] |= (uint32_t)(row * kKDim + 16 * (q ^ swz(row))) << (16 * (i & 1));
     }
+    return o;
 }
 
-__device__ __forceinline__ v8i lds_read32(const uint8_t *p)
+__device__ __forceinline__ void issue_page(const uint8_t *page_base, uint32_t lds_dst,
+                                           const DmaOffsets &o)
 {
-    const v4i a = *(const v4i *)p;
-    const v4i b = *(const v4i *)(p + 16);
+    asm volatile(
+        "s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o2], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o3], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o4], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x1400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o5], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x1800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o6], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x1c00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o7], %[b]\n\t"
+        "s_add_u32 m0, %[m], 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o8], %[b]"
+        :
+        : [o0] "v"(o.get(0)), [o1] "v"(o.get(1)), [o2] "v"(o.get(2)), [o3] "v"(o.get(3)),
+          [o4] "v"(o.get(4)), [o5] "v"(o.get(5)), [o6] "v"(o.get(6)), [o7] "v"(o.get(7)),
+          [o8] "v"(o.get(8)), [b] "s"(page_base), [m] "s"(lds_dst)
+        : "memory");
+}
+static_assert(kChunksPerWave == 9, "issue_page is written for 9 DMA instructions per wave");
+
+__device__ __forceinline__ v8i lds_read2x16(const uint8_t *p0, const uint8_t *p1)
+{
+    const v4i a = *(const v4i *)p0;
+    const v4i b = *(const v4i *)p1;
     return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Lanes l and l ^ 32 hold the two key halves of one row: v_permlane32_swap gives every
+// lane both values.
+__device__ __forceinline__ float half_pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ v2i lds_read_tr8(const uint8_t *p)
@@ -427,9 +573,19 @@ __device__ __forceinline__ int virtual_worker(int b, int W)
     return (b % 8) * (W / 8) + b / 8;
 }
 
+__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Read-only inputs are separate __restrict__ arguments so that the uniform reads
 // (work list, counts, block table) become scalar loads, which do not wait on the
 // in-flight page DMAs.
+//
+// Page loop (software pipelined): with page t+1 resident, iteration t runs the 18 score
+// MFMAs of page t+1 interleaved with the VALU work that turns page t's scores into P, then
+// page t's P V MFMAs, then page t+1's row max and (rarely) the O rescale.  The DMA of page
+// t+3 goes into the slot page t-1 used.
 template <int G>
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
     const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
@@ -442,8 +598,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
     constexpr int NT = 16 / DS;      // 32-dim output tiles per wave
     constexpr int MT = 32 * G;       // rows per work unit
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
+    // 128-row tiles: per wave, its P fragment (64 lanes x 32 B), per-row factor, flag
+    __shared__ __attribute__((aligned(16))) int32_t xch_p[G == 4 ? 4 : 1][G == 4 ? 64 * 8 : 1];
+    __shared__ float xch_alpha[G == 4 ? 4 : 1][32];
+    __shared__ int32_t xch_flag[G == 4 ? 4 : 1];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave / DS, dsi = wave % DS;
     const int l32 = lane & 31, half = lane >> 5;
     const int R = a.reqs, M = a.rows;
@@ -462,11 +623,24 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
     }
     const int units = n_items * mt;
 
-    // tr8 read geometry (independent of the page): within each 16-lane group, source
-    // lane i supplies key row b = i/2 and dims [8*(i%2), +8) of a 16-dim column block.
+    const DmaOffsets dmao = dma_offsets(wave, lane);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
+
+    // V^T fragment reads (ds_read_b64_tr_b8): within each 16-lane group, source lane i
+    // supplies key row b = i/2 and dims [8*(i%2), +8) of a 16-dim column block.  Keys are
+    // tr_key + 16*w2; dims [32*tile + 16*(g16&1) + 8*(i16&1), +8) lie in chunk
+    // 2*tile + (g16&1), swizzled by the key row (the same for the four w2 rows).
     const int g16 = lane >> 4, i16 = lane & 15;
-    const int tr_dim = 16 * (g16 & 1) + 8 * (i16 & 1);                 // + 32 * tile
-    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);    // + 16 * w2
+    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
+    int tr_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1) +
+                      64 * (dsi * NT / 2);
+    // K fragment reads: row l32 (+32 per key block), chunks 4k + 2*half + e, e = 0, 1
+    int k_off[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
 
     for (int u = virtual_worker(blockIdx.x, W); u < units; u += W) {
         const int item = u / mt, jt = u - item * mt;
@@ -490,8 +664,143 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
         const bool active = row0 < M;
         const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
 
-        // Q^T fragments: lane (row l32, half) holds dims [64k + 32*half, +32), k < 9.
-        v8i qf[9];
+        v8i qf[9];   // Q^T fragments, loaded below once the first pages are in flight
+
+        bool page_bad = false;
+        auto page_ptr = [&](int t) {
+            int64_t pid = bt[t];
+            if (pid < 0 || pid >= a.pool_pages) {
+                page_bad = true;
+                pid = 0;
+            }
+            return kv_in + pid * kPageBytes;
+        };
+        // keys past the request's length (only on its last page): zero the rows in LDS so
+        // that P*V stays finite; scores there are masked by key index
+        auto zero_tail = [&](int t) {
+            const int valid = L - (first + t) * kPage;
+            if (valid < kPage) {
+                uint8_t *slot = lds + (t % kSlots) * kPageBytes;
+                for (int off = valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
+                    *(v4i *)(slot + off) = v4i{0, 0, 0, 0};
+                lds_barrier();
+            }
+        };
+
+        float m_run = -INFINITY, l_run = 0.f;
+        v16f acc[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
+        v16f sc[2];          // the scores of the page being turned into P
+        v16f sn[2];          // the scores of the next page (pipelined schedule)
+
+        // S^T[64 keys x 32 rows] of the page in `slot`: 9 MFMAs per 32-key block, each fed
+        // by two 16-byte LDS reads of a key row.  Step j issues the reads of fragment j+2,
+        // then MFMA j, then `valu(j)` (other work to overlap with the MFMA); a scheduling
+        // fence after each step keeps that order, so the reads stay two MFMAs ahead.
+        auto scores = [&](const uint8_t *slot, v16f (&out)[2], auto &&valu) {
+            const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
+            out[0] = v16f{0};
+            out[1] = v16f{0};
+            v8i kf0 = lds_read2x16(kp0, kp1);
+            v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 18; ++j) {
+                const int b = j / 9, k = j % 9;
+                const v8i cur = (j & 1) ? kf1 : kf0;
+                if (j + 2 < 18) {
+                    const int o = 32 * ((j + 2) / 9) * kKDim + 64 * ((j + 2) % 9);
+                    if (j & 1)
+                        kf1 = lds_read2x16(kp0 + o, kp1 + o);
+                    else
+                        kf0 = lds_read2x16(kp0 + o, kp1 + o);
+                }
+                out[b] = mfma(cur, qf[k], out[b]);
+                valu(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // page max of the raw scores (score_scale > 0), masking keys >= valid, then the lazy
+        // running max in log2 units and, when it moves by more than 2^kTau, the O rescale
+        auto row_max = [&](v16f (&sv)[2], int t) {
+            const int valid = L - (first + t) * kPage;
+            if (valid < kPage) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sv[b][e] = -INFINITY;
+            }
+            float smax = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sv[b][e]);
+            const float mx = half_pair_max(smax) * a.score_scale;
+            const bool grow = mx > m_run + kTau;
+            if (__any(grow)) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+                m_run = m_new;
+            }
+        };
+        // P = 2^(s*scale - m + kPScale): FP32 into the row sum, E4M3 into the P^T operand;
+        // lane (l32, half) byte 16b + e holds key 32b + 8(e/4) + 4*half + e%4.  Group g of 8
+        // makes fragment dword g (four keys).
+        v8i pf;
+        float psum = 0.f, bias = 0.f;
+        auto probs_begin = [&]() {
+            bias = kPScale - m_run;
+            psum = 0.f;
+        };
+        auto probs_group = [&](const v16f (&sv)[2], int g) {
+            const int b = g >> 2, qd = g & 3;
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[b][4 * qd + e], a.score_scale, bias));
+                psum += p[e];
+            }
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+            pf[g] = w;
+        };
+        auto probs_end = [&]() { l_run += psum; };
+        // O^T += V^T P^T over this wave's NT tiles of 32 dims; four transposed LDS reads per
+        // tile, one tile ahead of the MFMAs
+        auto pv = [&](const uint8_t *slot) {
+            const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
+            auto vtile = [&](int n) {
+                v8i f;
+                const uint8_t *vp = (n & 1) ? vp1 : vp0;
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) {
+                    const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
+                    f[2 * w2] = x[0];
+                    f[2 * w2 + 1] = x[1];
+                }
+                return f;
+            };
+            v8i vf = vtile(0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                const v8i cur = vf;
+                if (n + 1 < NT) vf = vtile(n + 1);
+                acc[n] = mfma(cur, pf, acc[n]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        // The first pages' DMA, then the Q^T fragments (lane (row l32, half) holds dims
+        // [64k + 32*half, +32), k < 9), so that both latencies overlap; then wait for all
+        // of it (the compiler tracks the Q loads, not the DMA).
+        for (int d = 0; d < kSlots - 1 && d < size; ++d)
+            issue_page(page_ptr(d), lds_base + d * kPageBytes, dmao);
         {
             const int row = row0 + l32;
             if (row < M) {
@@ -507,138 +816,135 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
                 for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             }
         }
-
-        // The Q fragments are the only vector loads the compiler tracks; wait for them
-        // here, before any page DMA is in flight, so that no later wait drains the ring.
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 63));
-
-        float m_run = -INFINITY, l_run = 0.f;
-        v16f acc[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
-
-        // prologue: up to kSlots-1 pages in flight
-        bool page_bad = false;
-        for (int d = 0; d < kSlots - 1 && d < size; ++d) {
-            int64_t pid = bt[d];
-            if (pid < 0 || pid >= a.pool_pages) { page_bad = true; pid = 0; }
-            issue_page(kv_in, pid, lds + d * kPageBytes, wave, lane);
-        }
-
-        for (int t = 0; t < size; ++t) {
-            const int after = size - 1 - t;
-            wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
-            if (t + kSlots - 1 < size) {
-                int64_t pid = bt[t + kSlots - 1];
-                if (pid < 0 || pid >= a.pool_pages) { page_bad = true; pid = 0; }
-                issue_page(kv_in, pid, lds + ((t + kSlots - 1) % kSlots) * kPageBytes, wave, lane);
+        wait_pages_then_barrier(0);
+        auto no_valu = [](int) {};
+        if constexpr (G < 4) {
+            // pipelined: page 0's scores and max first
+            zero_tail(0);
+            if (active) {
+                scores(lds, sc, no_valu);
+                row_max(sc, 0);
             }
-            uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-            const int valid = L - (first + t) * kPage;   // >= 1
-            if (valid < kPage) {
-                // keys past the request's length: zero the rows so P*V stays finite
-                for (int off = valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
-                    *(v4i *)(slot + off) = v4i{0, 0, 0, 0};
+            for (int t = 0; t < size; ++t) {
+                const bool has_next = t + 1 < size;
+                if (has_next) {
+                    // page t+1 resident; every wave is past page t-1's P V (slot reused)
+                    const int after = size - 2 - t;
+                    wait_pages_then_barrier(after < 1 ? after : 1);
+                    if (t + kSlots - 1 < size)
+                        issue_page(page_ptr(t + kSlots - 1),
+                                   lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
+                    zero_tail(t + 1);
+                }
+                if (!active) continue;
+                probs_begin();
+                if (has_next) {
+                    // page t+1's 18 score MFMAs carry page t's P: one group per MFMA step
+                    scores(lds + ((t + 1) % kSlots) * kPageBytes, sn, [&](int j) {
+                        if (j < 8) probs_group(sc, j);
+                    });
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) probs_group(sc, g);
+                }
+                probs_end();
+                pv(lds + (t % kSlots) * kPageBytes);
+                if (has_next) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) sc[b] = sn[b];
+                    row_max(sc, t + 1);
+                }
+            }
+        } else {
+            // 128-row tiles, paired waves.  Wave w computes the scores, running max/sum and
+            // P of row block w; it owns O for the 64 rows of blocks {2p, 2p+1} (p = w/2) and
+            // the 256 dims [256*hw, +256) (hw = w%2).  Partners (w, w^1) swap their P
+            // fragments and rescale factors through LDS each page, so every V^T fragment
+            // read from LDS feeds two MFMAs (one per row block).
+            const int hw = wave & 1, pair = wave >> 1;
+            const bool o_active = jt * MT + 64 * pair < M;
+            // acc[n]: own row block (2p + hw), acc[8 + n]: the partner's (2p + 1 - hw);
+            // dim tile 8*hw + n in both
+            for (int t = 0; t < size; ++t) {
+                const int after = size - 1 - t;
+                wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
+                if (t + kSlots - 1 < size)
+                    issue_page(page_ptr(t + kSlots - 1),
+                               lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
+                zero_tail(t);
+                const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
+                float alpha = 1.f;
+                bool any_grow = false;
+                pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                if (active) {
+                    scores(slot, sc, no_valu);
+                    const int valid = L - (first + t) * kPage;
+                    if (valid < kPage) {
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e)
+                                if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid)
+                                    sc[b][e] = -INFINITY;
+                    }
+                    float smax = -INFINITY;
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
+                    const float mx = half_pair_max(smax) * a.score_scale;
+                    const bool grow = mx > m_run + kTau;
+                    any_grow = __any(grow);
+                    if (any_grow) {
+                        const float m_new = grow ? mx : m_run;
+                        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                        l_run *= alpha;
+                        m_run = m_new;
+                    }
+                    probs_begin();
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) probs_group(sc, g);
+                    probs_end();
+                }
+                // swap with the partner: P fragment, per-row rescale factor, rescale flag
+                *(v8i *)&xch_p[wave][lane * 8] = pf;
+                if (half == 0) xch_alpha[wave][l32] = alpha;
+                if (lane == 0) xch_flag[wave] = any_grow ? 1 : 0;
                 lds_barrier();
-            }
-            if (!active) continue;
-
-            // S^T = K Q^T for the page's two 32-key blocks: 18 MFMAs, each fed by two
-            // 16-byte LDS reads of one key row; the reads run two fragments ahead.
-            v16f sacc[2] = {v16f{0}, v16f{0}};
-            {
-                const uint8_t *kp = slot + l32 * kKDim + 32 * half;
-                v8i kf[2];
-                kf[0] = lds_read32(kp);
-                kf[1] = lds_read32(kp + 64);
+                if (!o_active) continue;
+                const v8i pf_other = *(const v8i *)&xch_p[wave ^ 1][lane * 8];
+                const float alpha_other = xch_alpha[wave ^ 1][l32];
+                const bool grow_other = xch_flag[wave ^ 1] != 0;
+                if (any_grow) {
 #pragma unroll
-                for (int j = 0; j < 18; ++j) {
-                    const int b = j / 9, k = j % 9;
-                    const v8i cur = kf[j & 1];
-                    if (j + 2 < 18) {
-                        const int b2 = (j + 2) / 9, k2 = (j + 2) % 9;
-                        kf[j & 1] = lds_read32(kp + 32 * b2 * kKDim + 64 * k2);
-                    }
-                    sacc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur, qf[k], sacc[b],
-                                                                             0, 0, 0, 0, 0, 0);
+                    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
                 }
-                // keep the reads two MFMAs ahead (and no further: registers)
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                if (grow_other) {
 #pragma unroll
-                for (int j = 0; j < 18; ++j) {
-                    if (j + 2 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    for (int n = 0; n < 8; ++n) acc[8 + n] *= alpha_other;
                 }
-            }
-
-            // scores in log2 units; lane holds row l32 and keys 32b + 8(e/4) + 4*half + e%4
-            float mx = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = 32 * b + 8 * (e >> 2) + 4 * half + (e & 3);
-                    const float tv = key < valid ? sacc[b][e] * a.score_scale : -INFINITY;
-                    sacc[b][e] = tv;
-                    mx = fmaxf(mx, tv);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool grow = mx > m_run + kTau;
-            if (__any(grow)) {
-                const float m_new = grow ? mx : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-                m_run = m_new;
-            }
-
-            // P = 2^(t - m): FP32 into the row sum, E4M3 (scaled by 2^kPScale) into P^T
-            v8i pf;
-            float psum = 0.f;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    float p[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        p[e] = __builtin_amdgcn_exp2f(sacc[b][4 * qd + e] - m_run + kPScale);
-                        psum += p[e];
-                    }
-                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                    w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                    pf[4 * b + qd] = w;
-                }
-            l_run += psum;
-
-            // O^T += V^T P^T: per 32-dim tile, four transposed LDS reads build the V^T
-            // fragment; the reads run one tile ahead of the MFMAs.
-            {
-                const uint8_t *vp = slot + tr_key * kKDim + 32 * dsi * NT + tr_dim;
+                const uint8_t *vp0 = slot + tr_off[0] + 64 * (4 * hw);
+                const uint8_t *vp1 = slot + tr_off[1] + 64 * (4 * hw);
                 auto vtile = [&](int n) {
                     v8i f;
+                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
 #pragma unroll
                     for (int w2 = 0; w2 < 4; ++w2) {
-                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 32 * n);
+                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
                         f[2 * w2] = x[0];
                         f[2 * w2 + 1] = x[1];
                     }
                     return f;
                 };
                 v8i vf = vtile(0);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int n = 0; n < NT; ++n) {
+                for (int n = 0; n < 8; ++n) {
                     const v8i cur = vf;
-                    if (n + 1 < NT) vf = vtile(n + 1);
-                    acc[n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur, pf, acc[n], 0, 0,
-                                                                            0, 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    if (n + 1 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (n + 1 < 8) vf = vtile(n + 1);
+                    acc[n] = mfma(cur, pf, acc[n]);
+                    acc[8 + n] = mfma(cur, pf_other, acc[8 + n]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -646,26 +952,54 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
 
         // epilogue: normalise and store this split's FP32 partial and log2 LSE.
         // l_run is scaled by 2^kPScale like P, so the scale cancels in O / l.
-        if (active) {
-            const float l_tot = l_run + __shfl_xor(l_run, 32);
-            const int row = row0 + l32;
-            if (row < M) {
-                const size_t slot_idx = (size_t)offsets[r] + s;
-                float *po = partial + (slot_idx * M + row) * kVDim;
-                const float inv = a.out_scale / l_tot;
+        const size_t slot_idx = (size_t)offsets[r] + s;
+        if constexpr (G < 4) {
+            if (active) {
+                const float l_tot = half_pair_sum(l_run);
+                const int row = row0 + l32;
+                if (row < M) {
+                    float *po = partial + (slot_idx * M + row) * kVDim;
+                    const float inv = a.out_scale / l_tot;
 #pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    const int dim = 32 * (dsi * NT + n) + 4 * half;
+                    for (int n = 0; n < NT; ++n) {
+                        const int dim = 32 * (dsi * NT + n) + 4 * half;
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const v4f o = v4f{acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2],
-                                          acc[n][4 * q4 + 3]} * inv;
-                        *(v4f *)(po + dim + 8 * q4) = o;
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const v4f o = v4f{acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2],
+                                              acc[n][4 * q4 + 3]} * inv;
+                            *(v4f *)(po + dim + 8 * q4) = o;
+                        }
+                    }
+                    if (dsi == 0 && half == 0)
+                        lse_out[slot_idx * M + row] = m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
+                }
+            }
+        } else {
+            const int hw = wave & 1, pair = wave >> 1;
+            const float l_tot = half_pair_sum(l_run);
+            if (half == 0) xch_alpha[wave][l32] = l_tot;
+            lds_barrier();
+            const float l_other = xch_alpha[wave ^ 1][l32];
+            if (active && half == 0 && row0 + l32 < M)
+                lse_out[slot_idx * M + row0 + l32] = m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
+#pragma unroll
+            for (int own = 1; own >= 0; --own) {
+                const int row = jt * MT + 32 * (2 * pair + (own ? hw : 1 - hw)) + l32;
+                if (row < M) {
+                    float *po = partial + (slot_idx * M + row) * kVDim;
+                    const float inv = a.out_scale / (own ? l_tot : l_other);
+#pragma unroll
+                    for (int n = 0; n < 8; ++n) {
+                        const int dim = 32 * (8 * hw + n) + 4 * half;
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const v16f &t16 = acc[(own ? 0 : 8) + n];
+                            const v4f o = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2],
+                                              t16[4 * q4 + 3]} * inv;
+                            *(v4f *)(po + dim + 8 * q4) = o;
+                        }
                     }
                 }
-                if (dsi == 0 && half == 0)
-                    lse_out[slot_idx * M + row] =
-                        m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
             }
         }
         lds_barrier();  // the next unit's prologue overwrites the ring
@@ -693,10 +1027,64 @@ __device__ inline uint16_t bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
-// One wave per (row, band): band b covers dims [b*512/bands, (b+1)*512/bands).
+// One wave per (row, band): band b covers dims [b*512/bands, (b+1)*512/bands).  The
+// partial loads of a batch of splits are issued before the weights are known, so the
+// wave waits for memory once per batch, not once per split.
+constexpr int kCombineBatch = 8;
+
+template <int PER_LANE>
+__device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int band, int lane,
+                                            int r, int i, int c, int64_t base)
+{
+    const int width = 256 * PER_LANE;
+    uint16_t *out = a.out + g * kVDim + band * width;
+    auto load_batch = [&](int s0, v4f (&part)[kCombineBatch][PER_LANE]) {
+#pragma unroll
+        for (int b = 0; b < kCombineBatch; ++b) {
+            const int s = s0 + b < c ? s0 + b : c - 1;
+            const float *p = a.partial + ((base + s) * a.rows + i) * kVDim + band * width;
+#pragma unroll
+            for (int k = 0; k < PER_LANE; ++k) part[b][k] = *(const v4f *)(p + 4 * (lane + 64 * k));
+        }
+    };
+    // the first batch of partials is in flight while the weights are computed
+    v4f part[kCombineBatch][PER_LANE];
+    load_batch(0, part);
+    // split weights exp2(lse_s - max) / sum, lane s (s < 64) holds split s's lse
+    float mx = -INFINITY;
+    for (int s = lane; s < c; s += 64) mx = fmaxf(mx, a.lse[(base + s) * a.rows + i]);
+    mx = wave_allf<true>(mx);
+    float sum = 0.f;
+    for (int s = lane; s < c; s += 64) sum += __builtin_amdgcn_exp2f(a.lse[(base + s) * a.rows + i] - mx);
+    sum = wave_allf<false>(sum);
+    const float inv = 1.0f / sum;
+
+    v4f acc[PER_LANE];
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) acc[k] = v4f{0, 0, 0, 0};
+    for (int s0 = 0; s0 < c; s0 += kCombineBatch) {
+        // this batch's weights: lane b holds split s0 + b's
+        const int sl = s0 + (lane % kCombineBatch) < c ? s0 + (lane % kCombineBatch) : c - 1;
+        const float wl = __builtin_amdgcn_exp2f(a.lse[(base + sl) * a.rows + i] - mx) * inv;
+#pragma unroll
+        for (int b = 0; b < kCombineBatch; ++b) {
+            const float w = s0 + b < c ? __shfl(wl, b) : 0.f;
+#pragma unroll
+            for (int k = 0; k < PER_LANE; ++k) acc[k] += w * part[b][k];
+        }
+        if (s0 + kCombineBatch < c) load_batch(s0 + kCombineBatch, part);
+    }
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) {
+        const uint32_t lo = bf16_rne(acc[k][0]) | ((uint32_t)bf16_rne(acc[k][1]) << 16);
+        const uint32_t hi = bf16_rne(acc[k][2]) | ((uint32_t)bf16_rne(acc[k][3]) << 16);
+        *(uint2 *)(out + 4 * (lane + 64 * k)) = make_uint2(lo, hi);
+    }
+    if (band == 0 && lane == 0) a.out_lse[g] = mx + __builtin_amdgcn_logf(sum);
+}
+
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
 {
-    __shared__ float weight[AMLA_MAX_SPLITS];
     const int lane = threadIdx.x;
     const int64_t g = blockIdx.x / a.bands;       // folded row, request-major
     const int band = blockIdx.x % a.bands;
@@ -720,28 +1108,10 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
         if (band == 0 && lane == 0) a.out_lse[g] = NAN;
         return;
     }
-    float mx = -INFINITY;
-    for (int s = lane; s < c; s += 64) mx = fmaxf(mx, a.lse[(base + s) * a.rows + i]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int s = lane; s < c; s += 64) sum += __builtin_amdgcn_exp2f(a.lse[(base + s) * a.rows + i] - mx);
-    sum = wave_sum(sum);
-    for (int s = lane; s < c; s += 64)
-        weight[s] = __builtin_amdgcn_exp2f(a.lse[(base + s) * a.rows + i] - mx) / sum;
-    __syncthreads();
-
-    v4f acc[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
-    for (int s = 0; s < c; ++s) {
-        const float w = weight[s];
-        const float *p = a.partial + ((base + s) * a.rows + i) * kVDim + band * width;
-        for (int k = 0; k < per_lane; ++k) acc[k] += w * *(const v4f *)(p + 4 * (lane + 64 * k));
-    }
-    for (int k = 0; k < per_lane; ++k) {
-        const uint32_t lo = bf16_rne(acc[k][0]) | ((uint32_t)bf16_rne(acc[k][1]) << 16);
-        const uint32_t hi = bf16_rne(acc[k][2]) | ((uint32_t)bf16_rne(acc[k][3]) << 16);
-        *(uint2 *)(out + 4 * (lane + 64 * k)) = make_uint2(lo, hi);
-    }
-    if (band == 0 && lane == 0) a.out_lse[g] = mx + __builtin_amdgcn_logf(sum);
+    if (per_lane == 2)
+        combine_row<2>(a, g, band, lane, r, i, c, base);
+    else
+        combine_row<1>(a, g, band, lane, r, i, c, base);
 }
 
 // ----------------------------------------------------------------------- host helpers
@@ -862,7 +1232,7 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
     if (!params_ok(params) || num_reqs < 0 || num_reqs > AMLA_MAX_REQS || pool_pages < 1 ||
         bt_stride < 1 || !d_kv || !d_offsets || !d_work || !d_workspace ||
         (num_reqs > 0 && (!d_q || !d_block_table || !d_lengths || !d_counts)) ||
-        !std::isfinite(bmm1_scale) || !std::isfinite(bmm2_scale))
+        !std::isfinite(bmm1_scale) || !(bmm1_scale > 0.f) || !std::isfinite(bmm2_scale))
         return AMLA_ERR_INVALID;
     const WsLayout lay = ws_layout(num_reqs, params->rows_per_req, params->workers);
     if (ws_bytes < lay.total) return AMLA_ERR_WORKSPACE;

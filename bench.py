@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--unfolded", action="store_true",
                     help="stock flattening: R*k single-token requests with replicated tables")
     ap.add_argument("--pools", type=int, default=3, help="KV pool copies rotated over steps")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the three kernels per step directly instead of replaying a "
+                         "captured HIP graph of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -139,9 +142,9 @@ def main():
     bmm1, bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
     out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, M), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        stream = torch.cuda.current_stream()
         dec.plan(lengths, bt.shape[1], stream)
         if ev is not None:
             ev[0].record(stream)
@@ -162,23 +165,55 @@ def main():
         print(f"device status {status}: {binding.status_string(status)}", file=sys.stderr)
         sys.exit(1)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # one HIP graph per KV pool: the step as a serving loop would replay it
+    graphs = []
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(len(pools)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(i)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(side)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    status = dec.device_status()
+    if status != 0:
+        print(f"device status {status} after the timed steps: {binding.status_string(status)}",
+              file=sys.stderr)
+        sys.exit(1)
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+
+    # the decode and combine kernels' own durations: events around each launch on the
+    # stream they run on, over the same number of steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     decode_ms = [e[0].elapsed_time(e[1]) for e in evs]
     combine_ms = [e[1].elapsed_time(e[2]) for e in evs]
     dec_avg = float(np.mean(decode_ms))
     comb_avg = float(np.mean(combine_ms))
+    stream = torch.cuda.current_stream()
 
     # plan alone (once per decode step in a model, shared by its layers)
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -230,7 +265,8 @@ def main():
         "config": {"workload": workload, "requests": R, "rows_per_req": M,
                    "kv_tokens": int(w.lengths.astype(np.int64).sum()), "page": 64,
                    "plan": args.mode, "kv_pools_rotated": len(pools),
-                   "mtile": dec.params.mtile, "workers": dec.params.workers},
+                   "mtile": dec.params.mtile, "workers": dec.params.workers,
+                   "launch": "eager" if args.eager else "hip_graph"},
         "rows_per_s": round(rows_per_s, 1),
         "step_us": round(ms_per_step * 1e3, 2),
         "decode_us": round(dec_avg * 1e3, 2),

@@ -165,7 +165,7 @@ int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols
  *   d_block_table int32 [num_reqs][bt_stride]; entries for pages [0, ceil(L_r/64)) must
  *                be in [0, pool_pages) (others are never read)
  *   d_lengths    int32 [num_reqs] (the lengths the plan was made from)
- *   bmm1_scale   softmax_scale * q_scale * k_scale;  bmm2_scale  k_scale
+ *   bmm1_scale   softmax_scale * q_scale * k_scale (finite, > 0);  bmm2_scale  k_scale
  *   d_counts, d_offsets, d_work, list_len: the plan of amla_plan_splits with `params`
  */
 int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,

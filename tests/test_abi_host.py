@@ -151,7 +151,7 @@ def test_decode_and_combine_argument_errors():
 
     for bad in (dict(q=0), dict(kv=0), dict(bt=0), dict(lengths=0), dict(counts=0),
                 dict(offsets=0), dict(work=0), dict(ws=0), dict(pool=0), dict(stride=0),
-                dict(reqs=-1), dict(b1=float("nan")), dict(b2=float("inf"))):
+                dict(reqs=-1), dict(b1=float("nan")), dict(b2=float("inf")), dict(b1=0.0), dict(b1=-1.0)):
         assert dec(**bad) == b.ERR_INVALID, bad
     assert dec(ws_bytes=10) == b.ERR_WORKSPACE
     assert dec(list_len=10) == b.ERR_LIST
