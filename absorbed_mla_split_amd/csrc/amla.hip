@@ -70,6 +70,16 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 #define LDS_AS __attribute__((address_space(3)))
+#define CONST_AS __attribute__((address_space(4)))
+
+// A uniform read of memory that no kernel of this file writes while reading it: through
+// the constant address space it is always a scalar load (lgkmcnt), never a vector load,
+// whose vmcnt wait would also wait for the page DMAs in flight.
+template <typename T>
+__device__ __forceinline__ T ldc(const T *p)
+{
+    return *(const CONST_AS T *)p;
+}
 
 struct WsLayout {
     size_t partial_off;  // FP32 [slots][M][512]
@@ -517,9 +527,20 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane)
     return o;
 }
 
+// A wave-uniform pointer, pinned to scalar registers for an inline-asm "s" operand.
+__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
+{
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void issue_page(const uint8_t *page_base, uint32_t lds_dst,
                                            const DmaOffsets &o)
 {
+    page_base = uniform_ptr(page_base);
+    lds_dst = __builtin_amdgcn_readfirstlane(lds_dst);
     asm volatile(
         "s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[b]\n\t"
         "s_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[b]\n\t"
@@ -537,6 +558,30 @@ __device__ __forceinline__ void issue_page(const uint8_t *page_base, uint32_t ld
         : "memory");
 }
 static_assert(kChunksPerWave == 9, "issue_page is written for 9 DMA instructions per wave");
+
+// A work unit's Q rows (MT rows x 576 B, contiguous in q) HBM -> LDS at `lds_dst`, same
+// layout; chunks of rows at or past `valid_rows` are not loaded.
+template <int MT>
+__device__ __forceinline__ void issue_q(const uint8_t *q_rows, uint32_t lds_dst, int valid_rows,
+                                        int wave, int lane)
+{
+    constexpr int kChunks = MT * (kKDim / 16);
+    constexpr int kPerWave = (kChunks / 4 + 63) / 64;
+    static_assert(kChunks * 16 <= kPageBytes, "Q rows must fit one ring slot");
+    q_rows = uniform_ptr(q_rows);
+    lds_dst = __builtin_amdgcn_readfirstlane(lds_dst);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+        const int p = (wave * kPerWave + i) * 64 + lane;
+        if (p < kChunks && p < valid_rows * (kKDim / 16)) {
+            asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o], %[b]"
+                         :
+                         : [o] "v"(p * 16), [b] "s"(q_rows),
+                           [m] "s"(lds_dst + (uint32_t)((wave * kPerWave + i) * 1024))
+                         : "memory");
+        }
+    }
+}
 
 __device__ __forceinline__ v8i lds_read2x16(const uint8_t *p0, const uint8_t *p1)
 {
@@ -611,13 +656,22 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
     const int mt = ceil_div(M, MT);
     const int W = a.workers;
 
-    if (header[kHdrPlanned] != kPlannedMagic || header[kHdrRows] != M ||
-        header[kHdrMtile] != MT || header[kHdrWorkers] != W || header[kHdrReqs] != R) {
-        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-        return;
-    }
-    const int n_items = offsets[R];
-    if (n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
+    // The plan summary, the item count and the first unit's work pair do not depend on
+    // each other, so they are loaded together and their latencies overlap.  The pair is
+    // inside the list: its item is below W and list_len >= 2 * (reqs + workers).
+    const int vw = virtual_worker(blockIdx.x, W);
+    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
+    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
+    const int h_reqs = ldc(&header[kHdrReqs]);
+    const int n_items = ldc(&offsets[R]);
+    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
+    // consume every value here so that the compiler cannot sink a load past the checks
+    // below (it would otherwise chain them one behind the other)
+    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
+                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
+                 "s"(lengths), "s"(counts));
+    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
         return;
     }
@@ -642,21 +696,21 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
 #pragma unroll
     for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
 
-    for (int u = virtual_worker(blockIdx.x, W); u < units; u += W) {
+    for (int u = vw; u < units; u += W) {
         const int item = u / mt, jt = u - item * mt;
-        const int r = work[2 * item], s = work[2 * item + 1];
-        const bool item_ok = r >= 0 && r < R && s >= 0 && s < counts[r];
-        if (!item_ok) {
-            if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-            continue;
-        }
-        const int L = lengths[r];
-        const int c = counts[r];
+        const int r = u == vw ? r_first : ldc(&work[2 * item]);
+        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
+        // the request's count, length and slot offset, loaded together (index clamped so
+        // that the loads stay in bounds before r is checked)
+        const int rc = r >= 0 && r < R ? r : 0;
+        const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
+        asm volatile("" ::"s"(c), "s"(L), "s"(off_r));
         const int pages = ceil_div(L, kPage);
-        const int q = pages / c, rem = pages % c;
+        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
         const int first = s * q + (s < rem ? s : rem);
         const int size = q + (s < rem ? 1 : 0);
-        if (L <= 0 || pages > a.bt_stride || size <= 0 || offsets[r] + s >= n_items) {
+        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
+            off_r + s >= n_items) {
             if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
             continue;
         }
@@ -667,14 +721,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
         v8i qf[9];   // Q^T fragments, loaded below once the first pages are in flight
 
         bool page_bad = false;
-        auto page_ptr = [&](int t) {
-            int64_t pid = bt[t];
+        auto page_at = [&](int32_t pid) {
             if (pid < 0 || pid >= a.pool_pages) {
                 page_bad = true;
                 pid = 0;
             }
-            return kv_in + pid * kPageBytes;
+            return kv_in + (int64_t)pid * kPageBytes;
         };
+        // block-table entry of page min(t, size - 1)
+        auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
         // keys past the request's length (only on its last page): zero the rows in LDS so
         // that P*V stays finite; scores there are masked by key index
         auto zero_tail = [&](int t) {
@@ -796,12 +851,44 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             }
         };
 
-        // The first pages' DMA, then the Q^T fragments (lane (row l32, half) holds dims
-        // [64k + 32*half, +32), k < 9), so that both latencies overlap; then wait for all
-        // of it (the compiler tracks the Q loads, not the DMA).
-        for (int d = 0; d < kSlots - 1 && d < size; ++d)
-            issue_page(page_ptr(d), lds_base + d * kPageBytes, dmao);
-        {
+        // The first pages' block-table entries, loaded together.
+        int32_t pid0[kSlots - 1];
+#pragma unroll
+        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
+        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
+        // the entry of the next page to fetch, read one fetch ahead
+        int32_t pid_next = page_id(kSlots - 1);
+        const int ahead = (size < kSlots - 1 ? size : kSlots - 1) - 1;  // pages after page 0
+        if constexpr (G < 4) {
+            // This unit's Q rows go to the last ring slot (free until page kSlots-1 is
+            // fetched) by DMA, then pages 0..kSlots-2; the first barrier waits for Q and
+            // page 0 only.  Q^T fragments: lane (row l32, half) holds dims
+            // [64k + 32*half, +32), k < 9.
+            issue_q<MT>(q_in + ((size_t)r * M + (size_t)jt * MT) * kKDim,
+                        (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + (kSlots - 1) * kPageBytes,
+                        M - jt * MT, wave, lane);
+#pragma unroll
+            for (int d = 0; d < kSlots - 1; ++d)
+                if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
+            wait_pages_then_barrier(ahead);
+            // the lane index is re-read here rather than kept live across the unit loop
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            const uint8_t *qs = lds + (kSlots - 1) * kPageBytes + (32 * grp + (ln & 31)) * kKDim +
+                                32 * (ln >> 5);
+            const bool row_ok = row0 + l32 < M;
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const v8i x = lds_read2x16(qs + 64 * k, qs + 64 * k + 16);
+                qf[k] = row_ok ? x : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        } else {
+            // The first pages' DMA, then the Q^T fragments from global memory, so that
+            // both latencies overlap; then wait for all of it (the compiler tracks the Q
+            // loads, not the DMA).
+#pragma unroll
+            for (int d = 0; d < kSlots - 1; ++d)
+                if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
             const int row = row0 + l32;
             if (row < M) {
                 const uint8_t *qp = q_in + ((size_t)r * M + row) * kKDim + 32 * half;
@@ -815,8 +902,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
 #pragma unroll
                 for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             }
+            wait_pages_then_barrier(0);
         }
-        wait_pages_then_barrier(0);
         auto no_valu = [](int) {};
         if constexpr (G < 4) {
             // pipelined: page 0's scores and max first
@@ -831,9 +918,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
                     // page t+1 resident; every wave is past page t-1's P V (slot reused)
                     const int after = size - 2 - t;
                     wait_pages_then_barrier(after < 1 ? after : 1);
-                    if (t + kSlots - 1 < size)
-                        issue_page(page_ptr(t + kSlots - 1),
+                    if (t + kSlots - 1 < size) {
+                        issue_page(page_at(pid_next),
                                    lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
+                        pid_next = page_id(t + kSlots);
+                    }
                     zero_tail(t + 1);
                 }
                 if (!active) continue;
@@ -868,9 +957,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             for (int t = 0; t < size; ++t) {
                 const int after = size - 1 - t;
                 wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
-                if (t + kSlots - 1 < size)
-                    issue_page(page_ptr(t + kSlots - 1),
+                if (t + kSlots - 1 < size) {
+                    issue_page(page_at(pid_next),
                                lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
+                    pid_next = page_id(t + kSlots);
+                }
                 zero_tail(t);
                 const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
                 float alpha = 1.f;
@@ -952,7 +1043,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
 
         // epilogue: normalise and store this split's FP32 partial and log2 LSE.
         // l_run is scaled by 2^kPScale like P, so the scale cancels in O / l.
-        const size_t slot_idx = (size_t)offsets[r] + s;
+        const size_t slot_idx = (size_t)off_r + s;
         if constexpr (G < 4) {
             if (active) {
                 const float l_tot = half_pair_sum(l_run);
@@ -1003,6 +1094,307 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             }
         }
         lds_barrier();  // the next unit's prologue overwrites the ring
+    }
+}
+
+
+// 32-row tiles, wave pairs on alternate pages.  Pair p (waves 2p, 2p+1) computes the pages
+// t = p (mod 2) of the split: both waves of the pair compute the page's scores for all 32
+// rows and the same P, and wave 2p+h accumulates O^T for the dims [256h, +256).  Each page's
+// scores are computed twice instead of four times (once per wave of a shared page stream),
+// which halves the MFMA and LDS work per page.  The two pairs' (max, sum, O) are merged
+// through LDS at the end of the unit.  Per iteration: pages 2i and 2i+1 are computed while
+// pages 2i+2 and 2i+3 are fetched into the other two ring slots.
+constexpr int kMergeStride = kVDim / 2 + 4;   // floats per row of a merge region (+16 B pad)
+static_assert(4 * 32 * kMergeStride * 4 <= kSlots * kPageBytes, "merge regions must fit the ring");
+
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
+    const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
+    float *__restrict__ lse_out, DecodeArgs a)
+{
+    constexpr int MT = 32;
+    constexpr int NT = kVDim / 64;   // 8 output tiles of 32 dims per wave
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
+    __shared__ float xm[2][32], xl[2][32];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave >> 1, hw = wave & 1;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int R = a.reqs, M = a.rows;
+    const int mt = ceil_div(M, MT);
+    const int W = a.workers;
+
+    // plan summary, item count and the first unit's work pair, loaded together (see
+    // decode_kernel)
+    const int vw = virtual_worker(blockIdx.x, W);
+    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
+    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
+    const int h_reqs = ldc(&header[kHdrReqs]);
+    const int n_items = ldc(&offsets[R]);
+    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
+    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
+                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
+                 "s"(lengths), "s"(counts));
+    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
+        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+        return;
+    }
+    const int units = n_items * mt;
+
+    const DmaOffsets dmao = dma_offsets(wave, lane);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
+
+    // V^T fragment reads of this wave's tile n (dims 256*hw + 32n): vp[n & 1] + 64 * (n >> 1)
+    // (layout as in decode_kernel)
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
+    int tr_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1) +
+                      64 * (hw * NT / 2);
+    int k_off[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
+
+    for (int u = vw; u < units; u += W) {
+        const int item = u / mt, jt = u - item * mt;
+        const int r = u == vw ? r_first : ldc(&work[2 * item]);
+        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
+        const int rc = r >= 0 && r < R ? r : 0;
+        const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
+        asm volatile("" ::"s"(c), "s"(L), "s"(off_r));
+        const int pages = ceil_div(L, kPage);
+        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
+        const int first = s * q + (s < rem ? s : rem);
+        const int size = q + (s < rem ? 1 : 0);
+        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
+            off_r + s >= n_items) {
+            if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+            continue;
+        }
+        const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
+        const int row = jt * MT + l32;
+
+        bool page_bad = false;
+        auto page_at = [&](int32_t pid) {
+            if (pid < 0 || pid >= a.pool_pages) {
+                page_bad = true;
+                pid = 0;
+            }
+            return kv_in + (int64_t)pid * kPageBytes;
+        };
+        auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
+        auto issue = [&](int t, int32_t pid) {
+            issue_page(page_at(pid), lds_base + (t % kSlots) * kPageBytes, dmao);
+        };
+
+        // Prologue: the unit's Q rows by DMA into the last ring slot, pages 0..2 into the
+        // others; once Q and pages 0, 1 are in, every wave reads its Q^T fragments (lane
+        // (row l32, half) holds dims [64k + 32*half, +32)), and page 3 then takes the slot.
+        int32_t pid0[kSlots];
+#pragma unroll
+        for (int d = 0; d < kSlots; ++d) pid0[d] = page_id(d);
+        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]), "s"(pid0[3]));
+        issue_q<MT>(q_in + ((size_t)r * M + (size_t)jt * MT) * kKDim,
+                    (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + (kSlots - 1) * kPageBytes, M - jt * MT,
+                    wave, lane);
+#pragma unroll
+        for (int d = 0; d < kSlots - 1; ++d)
+            if (d < size) issue(d, pid0[d]);
+        int32_t pid_a = page_id(kSlots), pid_b = page_id(kSlots + 1);
+        wait_pages_then_barrier(size > 2 ? 1 : 0);
+        v8i qf[9];
+        {
+            // the lane index is re-read here rather than kept live across the unit loop
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            const uint8_t *qs = lds + (kSlots - 1) * kPageBytes + (ln & 31) * kKDim + 32 * (ln >> 5);
+            const bool row_ok = jt * MT + (ln & 31) < M;
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const v8i x = lds_read2x16(qs + 64 * k, qs + 64 * k + 16);
+                qf[k] = row_ok ? x : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+        lds_barrier();  // every wave has its Q^T: page 3 may overwrite it
+        if (kSlots - 1 < size) issue(kSlots - 1, pid0[kSlots - 1]);
+
+        float m_run = -INFINITY, l_run = 0.f;
+        v16f acc[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
+
+        for (int t0 = 0; t0 < size; t0 += 2) {
+            if (t0 > 0) {
+                // pages t0, t0+1 resident (nothing newer in flight); every wave is past
+                // pages t0-2, t0-1, whose slots take pages t0+2, t0+3
+                wait_pages_then_barrier(0);
+                if (t0 + 2 < size) issue(t0 + 2, pid_a);
+                if (t0 + 3 < size) issue(t0 + 3, pid_b);
+                pid_a = page_id(t0 + 4);
+                pid_b = page_id(t0 + 5);
+            }
+            // keys past the request's length (its last page only): zero their rows so that
+            // P V stays finite; their scores are masked by key index below
+            const int last_valid = L - (first + (t0 + 1 < size ? t0 + 1 : t0)) * kPage;
+            if (last_valid < kPage) {
+                const int tz = t0 + 1 < size ? t0 + 1 : t0;
+                uint8_t *zs = lds + (tz % kSlots) * kPageBytes;
+                for (int off = last_valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
+                    *(v4i *)(zs + off) = v4i{0, 0, 0, 0};
+                lds_barrier();
+            }
+            const int t = t0 + pair;
+            if (t >= size) continue;
+            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
+            const int valid = L - (first + t) * kPage;
+
+            // S^T[64 keys x 32 rows]: 18 MFMAs, K fragment reads two ahead
+            v16f sc[2];
+            {
+                const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
+                sc[0] = v16f{0};
+                sc[1] = v16f{0};
+                v8i kf0 = lds_read2x16(kp0, kp1);
+                v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 18; ++j) {
+                    const int b = j / 9, k = j % 9;
+                    const v8i cur = (j & 1) ? kf1 : kf0;
+                    if (j + 2 < 18) {
+                        const int o = 32 * ((j + 2) / 9) * kKDim + 64 * ((j + 2) % 9);
+                        if (j & 1)
+                            kf1 = lds_read2x16(kp0 + o, kp1 + o);
+                        else
+                            kf0 = lds_read2x16(kp0 + o, kp1 + o);
+                    }
+                    sc[b] = mfma(cur, qf[k], sc[b]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // page max (masked), lazy running max and O rescale
+            if (valid < kPage) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sc[b][e] = -INFINITY;
+            }
+            float smax = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
+            const float mx = half_pair_max(smax) * a.score_scale;
+            const bool grow = mx > m_run + kTau;
+            if (__any(grow)) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+                m_run = m_new;
+            }
+            // P = 2^(s*scale - m + kPScale): FP32 into the row sum, E4M3 into P^T
+            v8i pf;
+            {
+                const float bias = kPScale - m_run;
+                float psum = 0.f;
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const int b = g >> 2, qd = g & 3;
+                    float p4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        p4[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][4 * qd + e], a.score_scale, bias));
+                        psum += p4[e];
+                    }
+                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
+                    pf[g] = w4;
+                }
+                l_run += psum;
+            }
+            // O^T += V^T P^T over this wave's 8 tiles, transposed V reads one tile ahead
+            {
+                const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
+                auto vtile = [&](int n) {
+                    v8i f;
+                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
+                        f[2 * w2] = x[0];
+                        f[2 * w2 + 1] = x[1];
+                    }
+                    return f;
+                };
+                v8i vf = vtile(0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const v8i cur = vf;
+                    if (n + 1 < NT) vf = vtile(n + 1);
+                    acc[n] = mfma(cur, pf, acc[n]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
+
+        // merge the two pairs: m = max_p m_p, l = sum_p l_p 2^(m_p - m) and
+        // O = sum_p O_p 2^(m_p - m) / l (l_run carries P's 2^kPScale, which cancels)
+        const float l_tot = half_pair_sum(l_run);
+        if (hw == 0 && half == 0) {
+            xm[pair][l32] = m_run;
+            xl[pair][l32] = l_tot;
+        }
+        lds_barrier();  // also: every wave is done with the ring
+        const float m0 = xm[0][l32], m1 = xm[1][l32];
+        const float m_all = fmaxf(m0, m1);
+        const float l_all = (m0 == -INFINITY ? 0.f : xl[0][l32] * __builtin_amdgcn_exp2f(m0 - m_all)) +
+                            (m1 == -INFINITY ? 0.f : xl[1][l32] * __builtin_amdgcn_exp2f(m1 - m_all));
+        const float f_own =
+            m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_all) * (a.out_scale / l_all);
+        const size_t slot_idx = (size_t)off_r + s;
+        if (wave == 0 && half == 0 && row < M)
+            lse_out[slot_idx * M + row] = m_all + __builtin_amdgcn_logf(l_all) - kPScale;
+        // every wave stores its scaled O (32 rows x 256 dims) in region `wave`; then wave w
+        // adds dims [128w, +128) of the two pairs' regions and stores them
+        float *const region = (float *)(void *)lds;
+        {
+            float *mine = region + wave * (32 * kMergeStride) + l32 * kMergeStride + 4 * half;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *(v4f *)(mine + 32 * n + 8 * q4) =
+                        v4f{acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2], acc[n][4 * q4 + 3]} * f_own;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        lds_barrier();
+        {
+            const int hsel = wave >> 1, dbase = 128 * (wave & 1);
+            const float *r0 = region + hsel * (32 * kMergeStride);         // pair 0, half hsel
+            const float *r1 = region + (2 + hsel) * (32 * kMergeStride);   // pair 1, half hsel
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int f = i * 64 + lane, rr = f >> 5, d = dbase + 4 * (f & 31);
+                const v4f sum = *(const v4f *)(r0 + rr * kMergeStride + d) +
+                                *(const v4f *)(r1 + rr * kMergeStride + d);
+                if (jt * MT + rr < M)
+                    *(v4f *)(partial + (slot_idx * M + jt * MT + rr) * kVDim + 256 * hsel + d) = sum;
+            }
+        }
+        lds_barrier();  // the next unit's pages overwrite the regions
     }
 }
 
@@ -1255,7 +1647,7 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
     hipStream_t st = (hipStream_t)stream;
 #define AMLA_DECODE_ARGS d_q, d_kv, d_block_table, d_lengths, d_counts, d_offsets, d_work, hdr, part, lse, a
     switch (params->mtile) {
-    case 32: hipLaunchKernelGGL(decode_kernel<1>, grid, block, 0, st, AMLA_DECODE_ARGS); break;
+    case 32: hipLaunchKernelGGL(decode32_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     case 64: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     }

@@ -40,8 +40,10 @@ def parse():
                     help="stock flattening: R*k single-token requests with replicated tables")
     ap.add_argument("--pools", type=int, default=3, help="KV pool copies rotated over steps")
     ap.add_argument("--eager", action="store_true",
-                    help="launch the three kernels per step directly instead of replaying a "
-                         "captured HIP graph of the step")
+                    help="launch the three kernels per step directly instead of replaying "
+                         "captured HIP graphs of consecutive steps")
+    ap.add_argument("--graph-steps", type=int, default=12,
+                    help="steps per captured HIP graph (rounded to a multiple of --pools)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -86,16 +88,20 @@ def cpu_baseline(w, target_s):
     dt = time.perf_counter() - t
     per_pair = dt / max(1.0, len(cal) * float(w.lengths[r0]))
     want_pairs = target_s / max(per_pair, 1e-12)
+    passes = 1
     if want_pairs >= keys_total:
         rows = [(r, i) for r in range(R) for i in range(M)]
-        sample = f"all {R * M} rows"
+        passes = max(1, min(100, int(want_pairs / keys_total)))
+        sample = f"all {R * M} rows, {passes} passes"
     else:
         stride = max(1, int(np.ceil(keys_total / want_pairs)))
         rows = [(r, i) for r in range(R) for i in range(M) if (r * M + i) % stride == 0]
         sample = f"{len(rows)} of {R * M} rows (every {stride}th, request-major), full key sets"
-    pairs = float(sum(int(w.lengths[r]) for r, _ in rows))
+    pairs = float(sum(int(w.lengths[r]) for r, _ in rows)) * passes
     t = time.perf_counter()
-    oracle.decode(w.q8, w.kv8, w.block_table, w.lengths, w.q_scale, w.k_scale, w.sm_scale, rows=rows)
+    for _ in range(passes):
+        oracle.decode(w.q8, w.kv8, w.block_table, w.lengths, w.q_scale, w.k_scale, w.sm_scale,
+                      rows=rows)
     dt = time.perf_counter() - t
     full_s = dt * keys_total / max(pairs, 1.0)
     return {"value": round(w.kv_bytes / full_s / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -165,20 +171,32 @@ def main():
         print(f"device status {status}: {binding.status_string(status)}", file=sys.stderr)
         sys.exit(1)
 
-    # one HIP graph per KV pool: the step as a serving loop would replay it
-    graphs = []
+    # Consecutive steps captured into HIP graphs, as a serving loop replays a decode step's
+    # layers: `chain` steps per graph (a multiple of the pool count, so the pool rotation
+    # runs on across replays) and one graph for the remainder of --steps.
+    plan_graphs = []          # (graph, steps it holds) in timed order
     if not args.eager:
+        P = len(pools)
+        chain = max(P, (max(1, args.graph_steps) + P - 1) // P * P)
+        chain = min(chain, max(P, (args.steps + P - 1) // P * P))
+        full, rest = divmod(args.steps, chain)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(len(pools)):
-                g = torch.cuda.CUDAGraph()
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
                 with torch.cuda.graph(g, stream=side):
-                    step(i)
-                graphs.append(g)
+                    for i in range(n):
+                        step(i)
+            return g
+
+        g_full = capture(chain) if full else None
+        g_rest = capture(rest) if rest else None
         torch.cuda.current_stream().wait_stream(side)
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+        plan_graphs = [(g_full, chain)] * full + ([(g_rest, rest)] if rest else [])
+        for g, _ in plan_graphs[:max(1, args.warmup // chain)]:
+            g.replay()
         torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -187,10 +205,11 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
+    if plan_graphs:
+        for g, _ in plan_graphs:
+            g.replay()
+    else:
+        for i in range(args.steps):
             step(i)
     end.record(stream)
     torch.cuda.synchronize()
@@ -266,7 +285,8 @@ def main():
                    "kv_tokens": int(w.lengths.astype(np.int64).sum()), "page": 64,
                    "plan": args.mode, "kv_pools_rotated": len(pools),
                    "mtile": dec.params.mtile, "workers": dec.params.workers,
-                   "launch": "eager" if args.eager else "hip_graph"},
+                   "launch": "eager" if args.eager else
+                   f"hip_graph x{plan_graphs[0][1]} steps" if plan_graphs else "hip_graph"},
         "rows_per_s": round(rows_per_s, 1),
         "step_us": round(ms_per_step * 1e3, 2),
         "decode_us": round(dec_avg * 1e3, 2),
