@@ -8,8 +8,10 @@
 // FP32 partials and a log2 LSE, and a reducer merging the splits into BF16 rows.
 //
 // gfx950 mapping (this file's design, not the pages'):
-//   * plan    one 1024-thread workgroup; binary search for the split chunk, block scans,
-//             an LDS bitonic sort of per-request split runs to build the work list.
+//   * plan    one 256-thread workgroup.  Up to 256 requests: every wave derives the chunk
+//             and the scans by itself (DPP, no barrier), then each thread places one run of
+//             equal-size splits by counting the runs that sort before it.  More requests:
+//             block reductions and scans, a rank or bitonic sort of the runs.
 //   * decode  one persistent 256-thread workgroup per CU.  A work unit is (request, split,
 //             row tile of MT = 32*G rows).  The four waves share one page stream: pages
 //             (64 tokens x 576 B) go HBM -> LDS by global_load_lds_dwordx4 into a ring of
@@ -441,6 +443,198 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
         pos += cnt_local[i];
     }
     for (int i = 2 * total_items + tid; i < a.list_len; i += kPlanThreads) a.work[i] = -1;
+
+    if (tid == 0) {
+        a.header[kHdrStatus] = bad ? AMLA_DEV_BAD_LENGTH : 0;
+        a.header[kHdrItems] = n_items;
+        a.header[kHdrRows] = a.rows;
+        a.header[kHdrMtile] = a.mtile;
+        a.header[kHdrWorkers] = a.workers;
+        a.header[kHdrMode] = a.mode;
+        a.header[kHdrReqs] = R;
+        a.header[kHdrPlanned] = kPlannedMagic;
+    }
+}
+
+// Inclusive scan over the 64 lanes of a wave: DPP row shifts within rows of 16 lanes,
+// then the row broadcasts of lanes 15 and 31 into the rows above them.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ int32_t wave_total(int32_t incl)
+{
+    return __builtin_amdgcn_readlane(incl, 63);
+}
+
+// Plan of up to kSmallReqs requests.  Every wave derives the whole plan summary by itself
+// (lane l holds requests l, l+64, l+128, l+192), so the chunk search and the scans need
+// no barrier; one barrier publishes the runs, whose list positions the 256 threads then
+// compute one run each.  Same result as plan_kernel.
+constexpr int kSmallReqs = 256;
+constexpr int kSmallPer = kSmallReqs / 64;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
+{
+    // runs in request order, packed (0x7FFFFFFF - size) << 32 | r << 18 | s0 << 9 | length
+    // (s0 = its first split): the order of the packed words is the list order (size
+    // descending, then r; a request has one run per size)
+    __shared__ uint64_t runs[2 * kSmallReqs];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = a.reqs;
+    const int64_t mt = ceil_div(a.rows, a.mtile);
+    const int64_t budget = (int64_t)a.workers / mt;
+
+    // 1. pages per request (every wave reads all lengths)
+    int32_t pg[kSmallPer];
+    int32_t len[kSmallPer];
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const int r = lane + 64 * k;
+        len[k] = r < R ? a.lengths[r] : 0;
+    }
+    bool bad_l = false;
+    int32_t pmax_l = 0, nz_l = 0;
+    int64_t total_l = 0;
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const int32_t L = len[k];
+        const int32_t p = (L >> 6) + ((L & 63) != 0);   // ceil(L / 64) without overflow
+        const bool b = L < 0 || p > a.bt_cols;
+        bad_l |= b;
+        pg[k] = b ? 0 : p;
+        pmax_l = pg[k] > pmax_l ? pg[k] : pmax_l;
+        total_l += pg[k];
+        nz_l += pg[k] > 0;
+    }
+    const bool bad = __any(bad_l);
+    const int64_t pmax = wave_all64<true>(pmax_l);
+    const int64_t total = wave_all64<false>(total_l);
+    const int64_t nz = wave_all64<false>(nz_l);
+    if (bad) {
+#pragma unroll
+        for (int k = 0; k < kSmallPer; ++k) pg[k] = 0;
+    }
+
+    // 2. chunk (BALANCED) or fixed count.  units(c) = sum_r ceil(pages_r / c) falls with c
+    //    and total/c <= units(c) <= total/c + nz, so the smallest c with units(c) <= budget
+    //    lies in [ceil(total/budget), ceil(total/(budget - nz))]: binary search, trying the
+    //    lower bound first (the answer for near-uniform lengths)
+    auto units = [&](int64_t c) {
+        int64_t u = 0;
+#pragma unroll
+        for (int k = 0; k < kSmallPer; ++k) u += ((uint32_t)pg[k] + (uint32_t)c - 1u) / (uint32_t)c;
+        return wave_all64<false>(u);
+    };
+    int64_t chunk = 1, fixed = 1;
+    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
+        if (budget < nz) {
+            chunk = pmax;
+        } else {
+            int64_t lo = (total + budget - 1) / budget, hi = pmax;
+            if (budget > nz) {
+                const int64_t h = (total + (budget - nz) - 1) / (budget - nz);
+                hi = h < hi ? h : hi;
+            }
+            lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
+            if (lo < hi && units(lo) <= budget) hi = lo;
+            else if (lo < hi) ++lo;
+            while (lo < hi) {
+                const int64_t mid = lo + (hi - lo) / 2;
+                if (units(mid) <= budget) hi = mid;
+                else lo = mid + 1;
+            }
+            chunk = hi;
+        }
+        chunk = chunk > a.min_pages ? chunk : a.min_pages;
+    } else if (!bad && a.mode == AMLA_PLAN_FIXED) {
+        fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
+        fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
+    }
+
+    // 3. counts, offsets (request order = k-major lane order) and the runs of each request:
+    //    (q+1) x rem from s = 0, then q x (c - rem) from s = rem
+    int32_t cnt[kSmallPer], off[kSmallPer], rbase[kSmallPer];
+    int32_t carry = 0, rcarry = 0;
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const uint32_t p = (uint32_t)pg[k];
+        int32_t c = 0;
+        if (p > 0) {
+            if (a.mode == AMLA_PLAN_BALANCED) {
+                const uint32_t cc = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
+                c = (int32_t)(cc < (uint32_t)a.max_splits ? cc : (uint32_t)a.max_splits);
+            } else {
+                c = (int32_t)((int64_t)p < fixed ? (int64_t)p : fixed);
+            }
+        }
+        cnt[k] = c;
+        const int32_t rem = c > 0 ? (int32_t)(p % (uint32_t)c) : 0;
+        const int32_t nruns = (rem > 0) + (c - rem > 0);
+        const int32_t ci = wave_incl_scan(c), ri = wave_incl_scan(nruns);
+        off[k] = carry + ci - c;
+        rbase[k] = rcarry + ri - nruns;
+        carry += wave_total(ci);
+        rcarry += wave_total(ri);
+    }
+    const int32_t n_items = carry, n_runs = rcarry;
+    if (wave == 0) {
+#pragma unroll
+        for (int k = 0; k < kSmallPer; ++k) {
+            const int r = lane + 64 * k;
+            if (r < R) {
+                a.counts[r] = cnt[k];
+                a.offsets[r] = off[k];
+                const int32_t c = cnt[k];
+                if (c > 0) {
+                    const uint32_t p = (uint32_t)pg[k];
+                    const int32_t q = (int32_t)(p / (uint32_t)c), rem = (int32_t)(p % (uint32_t)c);
+                    int idx = rbase[k];
+                    if (rem > 0)
+                        runs[idx++] = ((uint64_t)(0x7FFFFFFF - (q + 1)) << 32) | ((uint32_t)r << 18) |
+                                      (uint32_t)rem;
+                    if (c - rem > 0)
+                        runs[idx] = ((uint64_t)(0x7FFFFFFF - q) << 32) | ((uint32_t)r << 18) |
+                                    ((uint32_t)rem << 9) | (uint32_t)(c - rem);
+                }
+            }
+        }
+        if (lane == 0) a.offsets[R] = n_items;
+    }
+    __syncthreads();
+
+    // 4. list position of each run: the lengths of the runs that sort before it; then its
+    //    (r, s) pairs
+    for (int x = tid; x < n_runs; x += kPlanThreads) {
+        const uint64_t key = runs[x];
+        int32_t pos = 0;
+        int y = 0;
+        for (; y + 4 <= n_runs; y += 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint64_t o = runs[y + j];
+                pos += o < key ? (int32_t)(o & 0x1FF) : 0;
+            }
+        }
+        for (; y < n_runs; ++y) {
+            const uint64_t o = runs[y];
+            pos += o < key ? (int32_t)(o & 0x1FF) : 0;
+        }
+        const int32_t r = (int32_t)((key >> 18) & 0xFF), s0 = (int32_t)((key >> 9) & 0x1FF);
+        const int32_t n = (int32_t)(key & 0x1FF);
+        for (int e = 0; e < n && 2 * n_items <= a.list_len; ++e) {
+            a.work[2 * (pos + e)] = r;
+            a.work[2 * (pos + e) + 1] = s0 + e;
+        }
+    }
+    for (int i = 2 * n_items + tid; i < a.list_len; i += kPlanThreads) a.work[i] = -1;
 
     if (tid == 0) {
         a.header[kHdrStatus] = bad ? AMLA_DEV_BAD_LENGTH : 0;
@@ -1610,7 +1804,10 @@ int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols
     a.max_splits = params->max_splits;
     a.mode = params->mode;
     a.list_len = list_len;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a);
+    if (num_reqs <= kSmallReqs)
+        hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 

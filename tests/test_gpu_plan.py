@@ -74,3 +74,16 @@ def test_plan_bad_length_sets_status_and_empties_plan():
     lengths = torch.tensor([100, 64 * 5, 64], dtype=torch.int32, device="cuda")   # > 4 columns
     dec.plan(lengths, 4)
     assert dec.device_status() & binding.DEV_BAD_LENGTH
+
+
+@pytest.mark.parametrize("R", [63, 64, 65, 128, 255, 256, 257])
+def test_plan_request_count_boundaries(R):
+    # up to 256 requests take the single-pass planner, more the block-wide one
+    rng = np.random.default_rng(R)
+    lengths = rng.integers(0, 20000, R).astype(np.int32)
+    lengths[rng.random(R) < 0.1] = 0
+    for M, workers in ((32, None), (56, 16), (448, 96)):
+        plan_both(lengths, M, binding.PLAN_BALANCED, 256, workers=workers)
+        plan_both(lengths, M, binding.PLAN_FIXED, 0, workers=workers)
+    plan_both(np.full(R, 8192, np.int32), 32)            # uniform: the lower bound is the chunk
+    plan_both(np.full(R, 8192, np.int32), 32, max_splits=3)
