@@ -1614,13 +1614,16 @@ __device__ inline uint16_t bf16_rne(float f)
 }
 
 // One wave per (row, band): band b covers dims [b*512/bands, (b+1)*512/bands).  The
-// partial loads of a batch of splits are issued before the weights are known, so the
-// wave waits for memory once per batch, not once per split.
+// request's count and offset are loaded together; then the LSE of every split (lane s, and
+// s + 64j, holds split s + 64j's) and the first batch of partials are in flight at once,
+// so the wave waits for memory twice before its first output, and the split weights are
+// broadcast from the lanes that computed them.
 constexpr int kCombineBatch = 8;
+constexpr int kLsePerLane = AMLA_MAX_SPLITS / 64;
 
 template <int PER_LANE>
 __device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int band, int lane,
-                                            int r, int i, int c, int64_t base)
+                                            int i, int c, int64_t base)
 {
     const int width = 256 * PER_LANE;
     uint16_t *out = a.out + g * kVDim + band * width;
@@ -1633,15 +1636,25 @@ __device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int
             for (int k = 0; k < PER_LANE; ++k) part[b][k] = *(const v4f *)(p + 4 * (lane + 64 * k));
         }
     };
-    // the first batch of partials is in flight while the weights are computed
+    float ls[kLsePerLane];
+#pragma unroll
+    for (int j = 0; j < kLsePerLane; ++j) {
+        const int s = lane + 64 * j;
+        ls[j] = s < c ? a.lse[(base + s) * a.rows + i] : -INFINITY;
+    }
     v4f part[kCombineBatch][PER_LANE];
     load_batch(0, part);
-    // split weights exp2(lse_s - max) / sum, lane s (s < 64) holds split s's lse
+    // weights exp2(lse_s - max) / sum_s exp2(lse_s - max)
     float mx = -INFINITY;
-    for (int s = lane; s < c; s += 64) mx = fmaxf(mx, a.lse[(base + s) * a.rows + i]);
+#pragma unroll
+    for (int j = 0; j < kLsePerLane; ++j) mx = fmaxf(mx, ls[j]);
     mx = wave_allf<true>(mx);
-    float sum = 0.f;
-    for (int s = lane; s < c; s += 64) sum += __builtin_amdgcn_exp2f(a.lse[(base + s) * a.rows + i] - mx);
+    float wt[kLsePerLane], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kLsePerLane; ++j) {
+        wt[j] = lane + 64 * j < c ? __builtin_amdgcn_exp2f(ls[j] - mx) : 0.f;
+        sum += wt[j];
+    }
     sum = wave_allf<false>(sum);
     const float inv = 1.0f / sum;
 
@@ -1649,12 +1662,13 @@ __device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int
 #pragma unroll
     for (int k = 0; k < PER_LANE; ++k) acc[k] = v4f{0, 0, 0, 0};
     for (int s0 = 0; s0 < c; s0 += kCombineBatch) {
-        // this batch's weights: lane b holds split s0 + b's
-        const int sl = s0 + (lane % kCombineBatch) < c ? s0 + (lane % kCombineBatch) : c - 1;
-        const float wl = __builtin_amdgcn_exp2f(a.lse[(base + sl) * a.rows + i] - mx) * inv;
+        const int j = s0 >> 6;   // the batch lies in one 64-split group (64 % batch == 0)
+        const float wj = j == 0 ? wt[0] : j == 1 ? wt[1] : j == 2 ? wt[2] : wt[3];
 #pragma unroll
         for (int b = 0; b < kCombineBatch; ++b) {
-            const float w = s0 + b < c ? __shfl(wl, b) : 0.f;
+            const float w = s0 + b < c
+                                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), (s0 + b) & 63)) * inv
+                                : 0.f;
 #pragma unroll
             for (int k = 0; k < PER_LANE; ++k) acc[k] += w * part[b][k];
         }
@@ -1668,6 +1682,8 @@ __device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int
     }
     if (band == 0 && lane == 0) a.out_lse[g] = mx + __builtin_amdgcn_logf(sum);
 }
+static_assert(64 % kCombineBatch == 0, "a batch of splits must not straddle a lane group");
+static_assert(AMLA_MAX_SPLITS <= 4 * 64, "combine_row holds at most four LSEs per lane");
 
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
 {
@@ -1675,7 +1691,9 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
     const int64_t g = blockIdx.x / a.bands;       // folded row, request-major
     const int band = blockIdx.x % a.bands;
     const int r = (int)(g / a.rows), i = (int)(g % a.rows);
-    const int c = a.counts[r];
+    const int c = ldc(&a.counts[r]);
+    const int64_t base = ldc(&a.offsets[r]);
+    asm volatile("" ::"s"(c), "s"(base));
     const int width = kVDim / a.bands;            // 512 or 256
     const int per_lane = width / 256;             // float4s per lane: 2 or 1
     uint16_t *out = a.out + g * kVDim + band * width;
@@ -1686,7 +1704,6 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
         if (band == 0 && lane == 0) a.out_lse[g] = -INFINITY;
         return;
     }
-    const int64_t base = a.offsets[r];
     if (c > AMLA_MAX_SPLITS || base < 0 || base + c > a.slots) {
         // not a plan of these sizes: flag the row as NaN rather than read out of bounds
         for (int k = 0; k < per_lane; ++k)
@@ -1695,9 +1712,9 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
         return;
     }
     if (per_lane == 2)
-        combine_row<2>(a, g, band, lane, r, i, c, base);
+        combine_row<2>(a, g, band, lane, i, c, base);
     else
-        combine_row<1>(a, g, band, lane, r, i, c, base);
+        combine_row<1>(a, g, band, lane, i, c, base);
 }
 
 // ----------------------------------------------------------------------- host helpers

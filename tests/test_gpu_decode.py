@@ -74,6 +74,14 @@ def test_many_splits_small_workers():
     compare(w, out, lse, tag="many-splits")
 
 
+def test_over_64_splits_per_request():
+    # one-page splits: 201 and 70 splits, so the reducer holds several LSEs per lane
+    w = wl.small(2, 4, 8, [64 * 200 + 5, 64 * 70], seed=6)
+    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=300)
+    assert dec.plan_host()[0].tolist() == [201, 70]
+    compare(w, out, lse, tag="201-splits")
+
+
 @pytest.mark.parametrize("mode", [binding.PLAN_BALANCED, binding.PLAN_FIXED])
 def test_plans_agree(mode):
     w = wl.small(5, 7, 8, [3000, 100, 6000, 64, 9000], seed=2)
