@@ -30,6 +30,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/amla.h"
 
@@ -81,6 +82,17 @@ template <typename T>
 __device__ __forceinline__ T ldc(const T *p)
 {
     return *(const CONST_AS T *)p;
+}
+
+// f(std::integral_constant<int, I>) for I in [I0, N): a loop whose index is a constant in
+// every step, so register arrays indexed by it stay in registers.
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I0 < N) {
+        f(std::integral_constant<int, I0>{});
+        static_for<I0 + 1, N>(f);
+    }
 }
 
 struct WsLayout {
@@ -1592,6 +1604,337 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
     }
 }
 
+// 64-row tiles, wave pairs on alternate pages.  Pair p (waves 2p, 2p+1) computes the pages
+// t = p (mod 2) of the split for all 64 rows: wave 2p+h computes the scores, running
+// max/sum and P of row block h and accumulates O^T for both row blocks and the dims
+// [256h, +256), so every V^T fragment read from LDS feeds two MFMAs; the partners swap P,
+// the per-row rescale factor and a rescale flag through LDS.  Each page's scores are
+// computed once (with one shared page stream the two waves of each row block would both
+// compute them).  At the end the two pairs' (max, sum, O) are merged through LDS: pair p
+// merges and stores row block p.
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
+    const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
+    float *__restrict__ lse_out, DecodeArgs a)
+{
+    constexpr int MT = 64;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
+    __shared__ __attribute__((aligned(16))) int32_t xch_p[4][64 * 8];  // per wave: its P fragment
+    __shared__ float xch_alpha[4][32];                                  // per-row rescale factor
+    __shared__ int32_t xch_flag[4];                                     // any row rescaled
+    __shared__ float xm[2][2][32], xl[2][2][32];                        // [pair][block][row]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave >> 1, hw = wave & 1;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int R = a.reqs, M = a.rows;
+    const int mt = ceil_div(M, MT);
+    const int W = a.workers;
+
+    const int vw = virtual_worker(blockIdx.x, W);
+    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
+    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
+    const int h_reqs = ldc(&header[kHdrReqs]);
+    const int n_items = ldc(&offsets[R]);
+    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
+    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
+                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
+                 "s"(lengths), "s"(counts));
+    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
+        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+        return;
+    }
+    const int units = n_items * mt;
+
+    const DmaOffsets dmao = dma_offsets(wave, lane);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
+    int tr_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1) +
+                      64 * (4 * hw);
+    int k_off[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
+
+    for (int u = vw; u < units; u += W) {
+        const int item = u / mt, jt = u - item * mt;
+        const int r = u == vw ? r_first : ldc(&work[2 * item]);
+        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
+        const int rc = r >= 0 && r < R ? r : 0;
+        const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
+        asm volatile("" ::"s"(c), "s"(L), "s"(off_r));
+        const int pages = ceil_div(L, kPage);
+        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
+        const int first = s * q + (s < rem ? s : rem);
+        const int size = q + (s < rem ? 1 : 0);
+        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
+            off_r + s >= n_items) {
+            if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+            continue;
+        }
+        const int row0 = jt * MT + 32 * hw;     // this wave's score rows (block hw)
+        const bool active = row0 < M;
+        const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
+
+        bool page_bad = false;
+        auto page_at = [&](int32_t pid) {
+            if (pid < 0 || pid >= a.pool_pages) {
+                page_bad = true;
+                pid = 0;
+            }
+            return kv_in + (int64_t)pid * kPageBytes;
+        };
+        auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
+
+        // the first pages' DMA, then the Q^T fragments of the score rows; wait for all of
+        // it (the compiler tracks the Q loads, not the DMA)
+        int32_t pid0[kSlots - 1];
+#pragma unroll
+        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
+        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
+#pragma unroll
+        for (int d = 0; d < kSlots - 1; ++d)
+            if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
+        int32_t pid_a = page_id(kSlots - 1), pid_b = page_id(kSlots);
+        v8i qf[9];
+        if (active && row0 + l32 < M) {
+            const uint8_t *qp = q_in + ((size_t)r * M + row0 + l32) * kKDim + 32 * half;
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const v4i x = *(const v4i *)(qp + 64 * k);
+                const v4i y = *(const v4i *)(qp + 64 * k + 16);
+                qf[k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        wait_pages_then_barrier(0);
+
+        float m_run = -INFINITY, l_run = 0.f;
+        v16f acc[16];   // [0, 8): row block hw, [8, 16): block 1 - hw; dim tile 8*hw + n
+#pragma unroll
+        for (int n = 0; n < 16; ++n) acc[n] = v16f{0};
+
+        for (int t0 = 0; t0 < size; t0 += 2) {
+            if (t0 > 0) {
+                // pages t0, t0+1 resident; every wave is past pages t0-2, t0-1, whose slots
+                // take pages t0+2, t0+3 (page 3 goes into slot 3, untouched so far)
+                wait_pages_then_barrier(0);
+                if (t0 + 2 < size) {
+                    issue_page(page_at(pid_a), lds_base + ((t0 + 2) % kSlots) * kPageBytes, dmao);
+                    pid_a = page_id(t0 + 4);
+                }
+                if (t0 + 3 < size) {
+                    issue_page(page_at(pid_b), lds_base + ((t0 + 3) % kSlots) * kPageBytes, dmao);
+                    pid_b = page_id(t0 + 5);
+                }
+            } else if (kSlots - 1 < size) {
+                // page 3 into the free fourth slot
+                issue_page(page_at(pid_a), lds_base + (kSlots - 1) * kPageBytes, dmao);
+                pid_a = page_id(kSlots + 1);
+                // (pid_b already holds page 4's entry, fetched at the next iteration)
+                const int32_t swap = pid_a;
+                pid_a = pid_b;
+                pid_b = swap;
+            }
+            // keys past the request's length (its last page only): zero their rows so that
+            // P V stays finite; their scores are masked by key index below
+            const int tz = t0 + 1 < size ? t0 + 1 : t0;
+            const int last_valid = L - (first + tz) * kPage;
+            if (last_valid < kPage) {
+                uint8_t *zs = lds + (tz % kSlots) * kPageBytes;
+                for (int off = last_valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
+                    *(v4i *)(zs + off) = v4i{0, 0, 0, 0};
+                lds_barrier();
+            }
+            const int t = t0 + pair;
+            const bool has = t < size;
+            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
+            float alpha = 1.f;
+            bool any_grow = false;
+            v8i pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            if (has && active) {
+                // S^T[64 keys x 32 rows]: 18 MFMAs, K fragment reads two ahead
+                v16f sc[2];
+                const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
+                sc[0] = v16f{0};
+                sc[1] = v16f{0};
+                v8i kf0 = lds_read2x16(kp0, kp1);
+                v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 18; ++j) {
+                    const int b = j / 9, k = j % 9;
+                    const v8i cur = (j & 1) ? kf1 : kf0;
+                    if (j + 2 < 18) {
+                        const int o = 32 * ((j + 2) / 9) * kKDim + 64 * ((j + 2) % 9);
+                        if (j & 1)
+                            kf1 = lds_read2x16(kp0 + o, kp1 + o);
+                        else
+                            kf0 = lds_read2x16(kp0 + o, kp1 + o);
+                    }
+                    sc[b] = mfma(cur, qf[k], sc[b]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int valid = L - (first + t) * kPage;
+                if (valid < kPage) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sc[b][e] = -INFINITY;
+                }
+                float smax = -INFINITY;
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
+                const float mx = half_pair_max(smax) * a.score_scale;
+                const bool grow = mx > m_run + kTau;
+                any_grow = __any(grow);
+                if (any_grow) {
+                    const float m_new = grow ? mx : m_run;
+                    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+                    m_run = m_new;
+                }
+                const float bias = kPScale - m_run;
+                float psum = 0.f;
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    const int b = g >> 2, qd = g & 3;
+                    float p4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        p4[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][4 * qd + e], a.score_scale, bias));
+                        psum += p4[e];
+                    }
+                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
+                    pf[g] = w4;
+                }
+                l_run += psum;
+            }
+            // swap with the partner: P fragment, per-row rescale factor, rescale flag
+            *(v8i *)&xch_p[wave][lane * 8] = pf;
+            if (half == 0) xch_alpha[wave][l32] = alpha;
+            if (lane == 0) xch_flag[wave] = any_grow ? 1 : 0;
+            lds_barrier();
+            if (has) {
+                const v8i pf_other = *(const v8i *)&xch_p[wave ^ 1][lane * 8];
+                const float alpha_other = xch_alpha[wave ^ 1][l32];
+                const bool grow_other = xch_flag[wave ^ 1] != 0;
+                if (any_grow) {
+#pragma unroll
+                    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+                }
+                if (grow_other) {
+#pragma unroll
+                    for (int n = 0; n < 8; ++n) acc[8 + n] *= alpha_other;
+                }
+                const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
+                auto vtile = [&](int n) {
+                    v8i f;
+                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
+                        f[2 * w2] = x[0];
+                        f[2 * w2 + 1] = x[1];
+                    }
+                    return f;
+                };
+                v8i vf = vtile(0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const v8i cur = vf;
+                    if (n + 1 < 8) vf = vtile(n + 1);
+                    acc[n] = mfma(cur, pf, acc[n]);
+                    acc[8 + n] = mfma(cur, pf_other, acc[8 + n]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
+
+        // merge the pairs.  Block b's state of pair p (m, l over its pages) is in wave
+        // 2p + b; its O for dims half h is in wave 2p + h (slot own if b == h).
+        const float l_tot = half_pair_sum(l_run);
+        lds_barrier();   // every wave is done with the ring and the exchange
+        if (half == 0) {
+            xm[pair][hw][l32] = m_run;
+            xl[pair][hw][l32] = l_tot;
+        }
+        lds_barrier();
+        float f_blk[2];          // this pair's factor for block hw (own) and 1 - hw
+        float m_blk[2], l_blk[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+            const int b = o == 0 ? hw : 1 - hw;
+            const float m0 = xm[0][b][l32], m1 = xm[1][b][l32];
+            const float mm = fmaxf(m0, m1);
+            const float ll = (m0 == -INFINITY ? 0.f : xl[0][b][l32] * __builtin_amdgcn_exp2f(m0 - mm)) +
+                             (m1 == -INFINITY ? 0.f : xl[1][b][l32] * __builtin_amdgcn_exp2f(m1 - mm));
+            const float mine = xm[pair][b][l32];
+            f_blk[o] = mine == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mine - mm) * (a.out_scale / ll);
+            m_blk[o] = mm;
+            l_blk[o] = ll;
+        }
+        const size_t slot_idx = (size_t)off_r + s;
+        // LSE of block `pair`, by the wave of this pair that holds it as its own block
+        if (hw == pair && half == 0 && jt * MT + 32 * pair + l32 < M)
+            lse_out[slot_idx * M + jt * MT + 32 * pair + l32] = m_blk[0] + __builtin_amdgcn_logf(l_blk[0]) - kPScale;
+        // every wave stores its scaled O of block 1 - pair (the block the other pair
+        // stores) in region [1 - pair][hw]; then it adds the other pair's O of block `pair`
+        constexpr int kRegion = 32 * kMergeStride;
+        float *const region = (float *)(void *)lds;
+        {
+            const int b = 1 - pair;
+            const int o = b == hw ? 0 : 1;           // acc slot of block b
+            float *mine = region + (b * 2 + hw) * kRegion + l32 * kMergeStride + 4 * half;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const v16f &t16 = acc[8 * o + n];
+                    *(v4f *)(mine + 32 * n + 8 * q4) =
+                        v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]} * f_blk[o];
+                }
+            }
+        }
+        lds_barrier();
+        {
+            const int b = pair;
+            const int o = b == hw ? 0 : 1;
+            const int row = jt * MT + 32 * b + l32;
+            const float *theirs = region + (b * 2 + hw) * kRegion + l32 * kMergeStride + 4 * half;
+            if (row < M) {
+                float *po = partial + (slot_idx * M + row) * kVDim + 256 * hw;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const v16f &t16 = acc[8 * o + n];
+                        const v4f sum = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]} * f_blk[o] +
+                                        *(const v4f *)(theirs + 32 * n + 8 * q4);
+                        *(v4f *)(po + 32 * n + 8 * q4 + 4 * half) = sum;
+                    }
+                }
+            }
+        }
+        lds_barrier();  // the next unit's pages overwrite the regions
+    }
+}
+
 // ------------------------------------------------------------------- combine kernel
 
 struct CombineArgs {
@@ -1862,7 +2205,7 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
 #define AMLA_DECODE_ARGS d_q, d_kv, d_block_table, d_lengths, d_counts, d_offsets, d_work, hdr, part, lse, a
     switch (params->mtile) {
     case 32: hipLaunchKernelGGL(decode32_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
-    case 64: hipLaunchKernelGGL(decode_kernel<2>, grid, block, 0, st, AMLA_DECODE_ARGS); break;
+    case 64: hipLaunchKernelGGL(decode64_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     }
 #undef AMLA_DECODE_ARGS

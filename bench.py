@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--unfolded", action="store_true",
                     help="stock flattening: R*k single-token requests with replicated tables")
     ap.add_argument("--pools", type=int, default=3, help="KV pool copies rotated over steps")
+    ap.add_argument("--mtile", type=int, default=None, choices=[32, 64, 128],
+                    help="rows per decode work unit (default: the library's choice)")
+    ap.add_argument("--workers", type=int, default=None,
+                    help="persistent decode workgroups and plan budget (default: one per CU)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the three kernels per step directly instead of replaying "
                          "captured HIP graphs of consecutive steps")
@@ -144,7 +148,8 @@ def main():
     kv0 = torch.from_numpy(w.kv8).to(dev)
     pools = [kv0] + [kv0.clone() for _ in range(max(0, args.pools - 1))]
     mode = binding.PLAN_FIXED if args.mode == "fixed" else binding.PLAN_BALANCED
-    dec = binding.FoldedDecoder(R, M, device=dev, mode=mode)
+    dec = binding.FoldedDecoder(R, M, device=dev, mode=mode, mtile=args.mtile,
+                                workers=args.workers)
     bmm1, bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
     out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, M), dtype=torch.float32, device=dev)
