@@ -818,9 +818,12 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t *p)
 // blockIdx -> virtual worker: hardware hands workgroups to the 8 XCDs round-robin, so
 // virtual workers v and v+1 (the row tiles of one split) are put on the same XCD and
 // share its L2.
-__device__ __forceinline__ int virtual_worker(int b, int W)
+__device__ __forceinline__ int virtual_worker(int b, int W, int mt)
 {
-    if (W % 8 != 0) return b;
+    // with one row tile per split there is nothing to share: workgroups take the list in
+    // order, so those that start first (and those started as CUs free up) take the
+    // longest items
+    if (mt == 1 || W % 8 != 0) return b;
     return (b % 8) * (W / 8) + b / 8;
 }
 
@@ -865,7 +868,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
     // The plan summary, the item count and the first unit's work pair do not depend on
     // each other, so they are loaded together and their latencies overlap.  The pair is
     // inside the list: its item is below W and list_len >= 2 * (reqs + workers).
-    const int vw = virtual_worker(blockIdx.x, W);
+    const int vw = virtual_worker(blockIdx.x, W, mt);
     const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
     const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
     const int h_reqs = ldc(&header[kHdrReqs]);
@@ -1336,7 +1339,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
 
     // plan summary, item count and the first unit's work pair, loaded together (see
     // decode_kernel)
-    const int vw = virtual_worker(blockIdx.x, W);
+    const int vw = virtual_worker(blockIdx.x, W, mt);
     const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
     const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
     const int h_reqs = ldc(&header[kHdrReqs]);
@@ -1634,7 +1637,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
     const int mt = ceil_div(M, MT);
     const int W = a.workers;
 
-    const int vw = virtual_worker(blockIdx.x, W);
+    const int vw = virtual_worker(blockIdx.x, W, mt);
     const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
     const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
     const int h_reqs = ldc(&header[kHdrReqs]);

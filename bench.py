@@ -228,39 +228,24 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # Each kernel's own average duration, measured live with HIP events on the stream its
-    # launches run on: `steps` launches of it back to back, captured in one HIP graph as in a
-    # step, replayed between two events.  The plan is redone before the decodes and
-    # combines, which read it.
+    # launches run on: `steps` more steps launched one by one, with events around the
+    # decode and the combine of each (the launch latency before each event-bracketed
+    # kernel is included, so this is an upper bound on the kernel time); the plan
+    # alone, `steps` launches back to back between two events.
     stream = torch.cuda.current_stream()
-
-    def timed(fn, n):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for i in range(n):
-                    fn(i, side)
-        stream.wait_stream(side)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    n_k = args.steps
-    plan_ms = timed(lambda i, s: dec.plan(lengths, bt.shape[1], s), n_k)
-    dec.plan(lengths, bt.shape[1], stream)
-    dec_avg = timed(lambda i, s: binding.folded_decode(
-        q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2, dec.counts[:R],
-        dec.offsets[:R + 1], dec.work, dec.workspace, s), n_k)
-    comb_avg = timed(lambda i, s: binding.combine(
-        dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params, dec.compute_units,
-        out, lse, s), n_k)
-    plan_us = plan_ms * 1e3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_avg = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    comb_avg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(args.steps):
+        dec.plan(lengths, bt.shape[1], stream)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    plan_us = p0.elapsed_time(p1) / args.steps * 1e3
 
     kv_bytes = w.kv_bytes
     pages = int(((w.lengths.astype(np.int64) + 63) // 64).sum())
