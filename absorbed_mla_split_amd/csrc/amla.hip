@@ -504,13 +504,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
     const int64_t mt = ceil_div(a.rows, a.mtile);
     const int64_t budget = (int64_t)a.workers / mt;
 
-    // 1. pages per request (every wave reads all lengths)
+    // 1. pages per request (every wave reads all lengths); kn = request groups in use
+    const int kn = (R + 63) >> 6;
     int32_t pg[kSmallPer];
     int32_t len[kSmallPer];
 #pragma unroll
     for (int k = 0; k < kSmallPer; ++k) {
         const int r = lane + 64 * k;
-        len[k] = r < R ? a.lengths[r] : 0;
+        len[k] = k < kn && r < R ? a.lengths[r] : 0;
     }
     bool bad_l = false;
     int32_t pmax_l = 0, nz_l = 0;
@@ -542,17 +543,25 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
     auto units = [&](int64_t c) {
         int64_t u = 0;
 #pragma unroll
-        for (int k = 0; k < kSmallPer; ++k) u += ((uint32_t)pg[k] + (uint32_t)c - 1u) / (uint32_t)c;
+        for (int k = 0; k < kSmallPer; ++k)
+            if (k < kn) u += ((uint32_t)pg[k] + (uint32_t)c - 1u) / (uint32_t)c;
         return wave_all64<false>(u);
+    };
+    // ceil(x / y) for x >= 0, y > 0, in 32 bits when both fit
+    auto cdiv = [](int64_t x, int64_t y) -> int64_t {
+        if (x == 0) return 0;
+        if ((uint64_t)x <= 0xFFFFFFFFull && (uint64_t)y <= 0xFFFFFFFFull)
+            return (int64_t)((uint32_t)(x - 1) / (uint32_t)y) + 1;
+        return (x - 1) / y + 1;
     };
     int64_t chunk = 1, fixed = 1;
     if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
         if (budget < nz) {
             chunk = pmax;
         } else {
-            int64_t lo = (total + budget - 1) / budget, hi = pmax;
+            int64_t lo = cdiv(total, budget), hi = pmax;
             if (budget > nz) {
-                const int64_t h = (total + (budget - nz) - 1) / (budget - nz);
+                const int64_t h = cdiv(total, budget - nz);
                 hi = h < hi ? h : hi;
             }
             lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
@@ -577,6 +586,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
     int32_t carry = 0, rcarry = 0;
 #pragma unroll
     for (int k = 0; k < kSmallPer; ++k) {
+        cnt[k] = off[k] = rbase[k] = 0;
+        if (k >= kn) continue;
         const uint32_t p = (uint32_t)pg[k];
         int32_t c = 0;
         if (p > 0) {
@@ -623,27 +634,48 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
     __syncthreads();
 
     // 4. list position of each run: the lengths of the runs that sort before it; then its
-    //    (r, s) pairs
-    for (int x = tid; x < n_runs; x += kPlanThreads) {
-        const uint64_t key = runs[x];
-        int32_t pos = 0;
-        int y = 0;
-        for (; y + 4 <= n_runs; y += 4) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint64_t o = runs[y + j];
-                pos += o < key ? (int32_t)(o & 0x1FF) : 0;
-            }
-        }
-        for (; y < n_runs; ++y) {
-            const uint64_t o = runs[y];
-            pos += o < key ? (int32_t)(o & 0x1FF) : 0;
-        }
+    //    (r, s) pairs.  Up to 64 runs, the four threads of a quad count over every fourth
+    //    run and sum in the quad (all 256 threads busy); more, one thread per run.
+    auto place = [&](uint64_t key, int32_t pos, int e0, int de) {
         const int32_t r = (int32_t)((key >> 18) & 0xFF), s0 = (int32_t)((key >> 9) & 0x1FF);
         const int32_t n = (int32_t)(key & 0x1FF);
-        for (int e = 0; e < n && 2 * n_items <= a.list_len; ++e) {
+        for (int e = e0; e < n && 2 * n_items <= a.list_len; e += de) {
             a.work[2 * (pos + e)] = r;
             a.work[2 * (pos + e) + 1] = s0 + e;
+        }
+    };
+    if (n_runs <= kPlanThreads / 4) {
+        const int part = tid & 3, x = tid >> 2;
+        const uint64_t key = x < n_runs ? runs[x] : ~0ull;
+        int32_t pos = 0;
+        for (int y0 = 0; y0 < n_runs; y0 += 16) {   // uniform trip count, four reads in flight
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int y = y0 + 4 * j + part;
+                const uint64_t o = runs[y < n_runs ? y : 0];
+                pos += y < n_runs && o < key ? (int32_t)(o & 0x1FF) : 0;
+            }
+        }
+        pos += __builtin_amdgcn_mov_dpp(pos, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+        pos += __builtin_amdgcn_mov_dpp(pos, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+        if (x < n_runs) place(key, pos, part, 4);
+    } else {
+        for (int x = tid; x < n_runs; x += kPlanThreads) {
+            const uint64_t key = runs[x];
+            int32_t pos = 0;
+            int y = 0;
+            for (; y + 4 <= n_runs; y += 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint64_t o = runs[y + j];
+                    pos += o < key ? (int32_t)(o & 0x1FF) : 0;
+                }
+            }
+            for (; y < n_runs; ++y) {
+                const uint64_t o = runs[y];
+                pos += o < key ? (int32_t)(o & 0x1FF) : 0;
+            }
+            place(key, pos, 0, 1);
         }
     }
     for (int i = 2 * n_items + tid; i < a.list_len; i += kPlanThreads) a.work[i] = -1;
