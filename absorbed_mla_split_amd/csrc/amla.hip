@@ -70,6 +70,7 @@ constexpr int kPlannedMagic = 0x600DF00D;
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -864,34 +865,30 @@ __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Read-only inputs are separate __restrict__ arguments so that the uniform reads
-// (work list, counts, block table) become scalar loads, which do not wait on the
-// in-flight page DMAs.
-//
-// Page loop (software pipelined): with page t+1 resident, iteration t runs the 18 score
-// MFMAs of page t+1 interleaved with the VALU work that turns page t's scores into P, then
-// page t's P V MFMAs, then page t+1's row max and (rarely) the O rescale.  The DMA of page
-// t+3 goes into the slot page t-1 used.
-template <int G>
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
+// 128-row tiles, paired waves sharing each page: wave w computes the scores, running
+// max/sum and P of row block w; it accumulates O^T for the rows of blocks {2p, 2p+1}
+// (p = w/2) and the dims [256h, +256) (h = w%2), so every V^T fragment read from LDS feeds
+// two MFMAs.  Partners (w, w^1) swap P, the per-row rescale factor and a rescale flag
+// through LDS each page.  The DMA of page t+3 goes into the slot page t-1 used.  Read-only
+// inputs are separate __restrict__ arguments; their uniform reads go through the constant
+// address space (scalar loads, which do not wait on the in-flight page DMAs).
+__global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
     const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
     float *__restrict__ lse_out, DecodeArgs a)
 {
-    constexpr int DS = 4 / G;        // waves per row group (they split the output dims)
-    constexpr int NT = 16 / DS;      // 32-dim output tiles per wave
-    constexpr int MT = 32 * G;       // rows per work unit
+    constexpr int MT = 128;          // rows per work unit
+    constexpr int NT = 16;           // accumulator tiles per wave: 2 row blocks x 8 dim tiles
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
-    // 128-row tiles: per wave, its P fragment (64 lanes x 32 B), per-row factor, flag
-    __shared__ __attribute__((aligned(16))) int32_t xch_p[G == 4 ? 4 : 1][G == 4 ? 64 * 8 : 1];
-    __shared__ float xch_alpha[G == 4 ? 4 : 1][32];
-    __shared__ int32_t xch_flag[G == 4 ? 4 : 1];
+    // per wave: its P fragment (64 lanes x 32 B), per-row rescale factor, rescale flag
+    __shared__ __attribute__((aligned(16))) int32_t xch_p[4][64 * 8];
+    __shared__ float xch_alpha[4][32];
+    __shared__ int32_t xch_flag[4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave / DS, dsi = wave % DS;
     const int l32 = lane & 31, half = lane >> 5;
     const int R = a.reqs, M = a.rows;
     const int mt = ceil_div(M, MT);
@@ -930,8 +927,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
     int tr_off[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par)
-        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1) +
-                      64 * (dsi * NT / 2);
+        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1);
     // K fragment reads: row l32 (+32 per key block), chunks 4k + 2*half + e, e = 0, 1
     int k_off[2];
 #pragma unroll
@@ -955,7 +951,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
             continue;
         }
-        const int row0 = jt * MT + 32 * grp;
+        const int row0 = jt * MT + 32 * wave;   // this wave's score rows
         const bool active = row0 < M;
         const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
 
@@ -983,12 +979,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             }
         };
 
-        float m_run = -INFINITY, l_run = 0.f;
+        // l_run: row sum of the FP32 P (for the LSE); lq_run: of the E4M3 P that the MMA
+        // uses (O is normalised by it, so the weights of the output rows sum to one)
+        float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
         v16f acc[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
-        v16f sc[2];          // the scores of the page being turned into P
-        v16f sn[2];          // the scores of the next page (pipelined schedule)
+        v16f sc[2];          // the scores of the page
 
         // S^T[64 keys x 32 rows] of the page in `slot`: 9 MFMAs per 32-key block, each fed
         // by two 16-byte LDS reads of a key row.  Step j issues the reads of fragment j+2,
@@ -1017,41 +1014,15 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // page max of the raw scores (score_scale > 0), masking keys >= valid, then the lazy
-        // running max in log2 units and, when it moves by more than 2^kTau, the O rescale
-        auto row_max = [&](v16f (&sv)[2], int t) {
-            const int valid = L - (first + t) * kPage;
-            if (valid < kPage) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sv[b][e] = -INFINITY;
-            }
-            float smax = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sv[b][e]);
-            const float mx = half_pair_max(smax) * a.score_scale;
-            const bool grow = mx > m_run + kTau;
-            if (__any(grow)) {
-                const float m_new = grow ? mx : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-                m_run = m_new;
-            }
-        };
         // P = 2^(s*scale - m + kPScale): FP32 into the row sum, E4M3 into the P^T operand;
         // lane (l32, half) byte 16b + e holds key 32b + 8(e/4) + 4*half + e%4.  Group g of 8
         // makes fragment dword g (four keys).
         v8i pf;
-        float psum = 0.f, bias = 0.f;
+        float psum = 0.f, qsum = 0.f, bias = 0.f;
         auto probs_begin = [&]() {
             bias = kPScale - m_run;
             psum = 0.f;
+            qsum = 0.f;
         };
         auto probs_group = [&](const v16f (&sv)[2], int g) {
             const int b = g >> 2, qd = g & 3;
@@ -1064,12 +1035,115 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
             w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
             pf[g] = w;
+            const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
         };
-        auto probs_end = [&]() { l_run += psum; };
-        // O^T += V^T P^T over this wave's NT tiles of 32 dims; four transposed LDS reads per
-        // tile, one tile ahead of the MFMAs
-        auto pv = [&](const uint8_t *slot) {
-            const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
+        auto probs_end = [&]() {
+            l_run += psum;
+            lq_run += qsum;
+        };
+        // The first pages' block-table entries, loaded together.
+        int32_t pid0[kSlots - 1];
+#pragma unroll
+        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
+        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
+        // the entry of the next page to fetch, read one fetch ahead
+        int32_t pid_next = page_id(kSlots - 1);
+        // The first pages' DMA, then the Q^T fragments from global memory, so that
+        // both latencies overlap; then wait for all of it (the compiler tracks the Q
+        // loads, not the DMA).
+#pragma unroll
+        for (int d = 0; d < kSlots - 1; ++d)
+            if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
+        const int row = row0 + l32;
+        if (row < M) {
+            const uint8_t *qp = q_in + ((size_t)r * M + row) * kKDim + 32 * half;
+#pragma unroll
+            for (int k = 0; k < 9; ++k) {
+                const v4i x = *(const v4i *)(qp + 64 * k);
+                const v4i y = *(const v4i *)(qp + 64 * k + 16);
+                qf[k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        wait_pages_then_barrier(0);
+
+        auto no_valu = [](int) {};
+        // 128-row tiles, paired waves.  Wave w computes the scores, running max/sum and
+        // P of row block w; it owns O for the 64 rows of blocks {2p, 2p+1} (p = w/2) and
+        // the 256 dims [256*hw, +256) (hw = w%2).  Partners (w, w^1) swap their P
+        // fragments and rescale factors through LDS each page, so every V^T fragment
+        // read from LDS feeds two MFMAs (one per row block).
+        const int hw = wave & 1, pair = wave >> 1;
+        const bool o_active = jt * MT + 64 * pair < M;
+        // acc[n]: own row block (2p + hw), acc[8 + n]: the partner's (2p + 1 - hw);
+        // dim tile 8*hw + n in both
+        for (int t = 0; t < size; ++t) {
+            const int after = size - 1 - t;
+            wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
+            if (t + kSlots - 1 < size) {
+                issue_page(page_at(pid_next),
+                           lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
+                pid_next = page_id(t + kSlots);
+            }
+            zero_tail(t);
+            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
+            float alpha = 1.f;
+            bool any_grow = false;
+            pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            if (active) {
+                scores(slot, sc, no_valu);
+                const int valid = L - (first + t) * kPage;
+                if (valid < kPage) {
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid)
+                                sc[b][e] = -INFINITY;
+                }
+                float smax = -INFINITY;
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
+                const float mx = half_pair_max(smax) * a.score_scale;
+                const bool grow = mx > m_run + kTau;
+                any_grow = __any(grow);
+                if (any_grow) {
+                    const float m_new = grow ? mx : m_run;
+                    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+                    lq_run *= alpha;
+                    m_run = m_new;
+                }
+                probs_begin();
+#pragma unroll
+                for (int g = 0; g < 8; ++g) probs_group(sc, g);
+                probs_end();
+            }
+            // swap with the partner: P fragment, per-row rescale factor, rescale flag
+            *(v8i *)&xch_p[wave][lane * 8] = pf;
+            if (half == 0) xch_alpha[wave][l32] = alpha;
+            if (lane == 0) xch_flag[wave] = any_grow ? 1 : 0;
+            lds_barrier();
+            if (!o_active) continue;
+            const v8i pf_other = *(const v8i *)&xch_p[wave ^ 1][lane * 8];
+            const float alpha_other = xch_alpha[wave ^ 1][l32];
+            const bool grow_other = xch_flag[wave ^ 1] != 0;
+            if (any_grow) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) acc[n] *= alpha;
+            }
+            if (grow_other) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n) acc[8 + n] *= alpha_other;
+            }
+            const uint8_t *vp0 = slot + tr_off[0] + 64 * (4 * hw);
+            const uint8_t *vp1 = slot + tr_off[1] + 64 * (4 * hw);
             auto vtile = [&](int n) {
                 v8i f;
                 const uint8_t *vp = (n & 1) ? vp1 : vp0;
@@ -1084,256 +1158,46 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode_kernel(
             v8i vf = vtile(0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
+            for (int n = 0; n < 8; ++n) {
                 const v8i cur = vf;
-                if (n + 1 < NT) vf = vtile(n + 1);
+                if (n + 1 < 8) vf = vtile(n + 1);
                 acc[n] = mfma(cur, pf, acc[n]);
+                acc[8 + n] = mfma(cur, pf_other, acc[8 + n]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        };
+        }
 
-        // The first pages' block-table entries, loaded together.
-        int32_t pid0[kSlots - 1];
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
-        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
-        // the entry of the next page to fetch, read one fetch ahead
-        int32_t pid_next = page_id(kSlots - 1);
-        const int ahead = (size < kSlots - 1 ? size : kSlots - 1) - 1;  // pages after page 0
-        if constexpr (G < 4) {
-            // This unit's Q rows go to the last ring slot (free until page kSlots-1 is
-            // fetched) by DMA, then pages 0..kSlots-2; the first barrier waits for Q and
-            // page 0 only.  Q^T fragments: lane (row l32, half) holds dims
-            // [64k + 32*half, +32), k < 9.
-            issue_q<MT>(q_in + ((size_t)r * M + (size_t)jt * MT) * kKDim,
-                        (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + (kSlots - 1) * kPageBytes,
-                        M - jt * MT, wave, lane);
-#pragma unroll
-            for (int d = 0; d < kSlots - 1; ++d)
-                if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
-            wait_pages_then_barrier(ahead);
-            // the lane index is re-read here rather than kept live across the unit loop
-            int ln;
-            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-            const uint8_t *qs = lds + (kSlots - 1) * kPageBytes + (32 * grp + (ln & 31)) * kKDim +
-                                32 * (ln >> 5);
-            const bool row_ok = row0 + l32 < M;
-#pragma unroll
-            for (int k = 0; k < 9; ++k) {
-                const v8i x = lds_read2x16(qs + 64 * k, qs + 64 * k + 16);
-                qf[k] = row_ok ? x : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        } else {
-            // The first pages' DMA, then the Q^T fragments from global memory, so that
-            // both latencies overlap; then wait for all of it (the compiler tracks the Q
-            // loads, not the DMA).
-#pragma unroll
-            for (int d = 0; d < kSlots - 1; ++d)
-                if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
-            const int row = row0 + l32;
-            if (row < M) {
-                const uint8_t *qp = q_in + ((size_t)r * M + row) * kKDim + 32 * half;
-#pragma unroll
-                for (int k = 0; k < 9; ++k) {
-                    const v4i x = *(const v4i *)(qp + 64 * k);
-                    const v4i y = *(const v4i *)(qp + 64 * k + 16);
-                    qf[k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-            wait_pages_then_barrier(0);
-        }
-        auto no_valu = [](int) {};
-        if constexpr (G < 4) {
-            // pipelined: page 0's scores and max first
-            zero_tail(0);
-            if (active) {
-                scores(lds, sc, no_valu);
-                row_max(sc, 0);
-            }
-            for (int t = 0; t < size; ++t) {
-                const bool has_next = t + 1 < size;
-                if (has_next) {
-                    // page t+1 resident; every wave is past page t-1's P V (slot reused)
-                    const int after = size - 2 - t;
-                    wait_pages_then_barrier(after < 1 ? after : 1);
-                    if (t + kSlots - 1 < size) {
-                        issue_page(page_at(pid_next),
-                                   lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
-                        pid_next = page_id(t + kSlots);
-                    }
-                    zero_tail(t + 1);
-                }
-                if (!active) continue;
-                probs_begin();
-                if (has_next) {
-                    // page t+1's 18 score MFMAs carry page t's P: one group per MFMA step
-                    scores(lds + ((t + 1) % kSlots) * kPageBytes, sn, [&](int j) {
-                        if (j < 8) probs_group(sc, j);
-                    });
-                } else {
-#pragma unroll
-                    for (int g = 0; g < 8; ++g) probs_group(sc, g);
-                }
-                probs_end();
-                pv(lds + (t % kSlots) * kPageBytes);
-                if (has_next) {
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) sc[b] = sn[b];
-                    row_max(sc, t + 1);
-                }
-            }
-        } else {
-            // 128-row tiles, paired waves.  Wave w computes the scores, running max/sum and
-            // P of row block w; it owns O for the 64 rows of blocks {2p, 2p+1} (p = w/2) and
-            // the 256 dims [256*hw, +256) (hw = w%2).  Partners (w, w^1) swap their P
-            // fragments and rescale factors through LDS each page, so every V^T fragment
-            // read from LDS feeds two MFMAs (one per row block).
-            const int hw = wave & 1, pair = wave >> 1;
-            const bool o_active = jt * MT + 64 * pair < M;
-            // acc[n]: own row block (2p + hw), acc[8 + n]: the partner's (2p + 1 - hw);
-            // dim tile 8*hw + n in both
-            for (int t = 0; t < size; ++t) {
-                const int after = size - 1 - t;
-                wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
-                if (t + kSlots - 1 < size) {
-                    issue_page(page_at(pid_next),
-                               lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
-                    pid_next = page_id(t + kSlots);
-                }
-                zero_tail(t);
-                const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-                float alpha = 1.f;
-                bool any_grow = false;
-                pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-                if (active) {
-                    scores(slot, sc, no_valu);
-                    const int valid = L - (first + t) * kPage;
-                    if (valid < kPage) {
-#pragma unroll
-                        for (int b = 0; b < 2; ++b)
-#pragma unroll
-                            for (int e = 0; e < 16; ++e)
-                                if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid)
-                                    sc[b][e] = -INFINITY;
-                    }
-                    float smax = -INFINITY;
-#pragma unroll
-                    for (int b = 0; b < 2; ++b)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
-                    const float mx = half_pair_max(smax) * a.score_scale;
-                    const bool grow = mx > m_run + kTau;
-                    any_grow = __any(grow);
-                    if (any_grow) {
-                        const float m_new = grow ? mx : m_run;
-                        alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                        l_run *= alpha;
-                        m_run = m_new;
-                    }
-                    probs_begin();
-#pragma unroll
-                    for (int g = 0; g < 8; ++g) probs_group(sc, g);
-                    probs_end();
-                }
-                // swap with the partner: P fragment, per-row rescale factor, rescale flag
-                *(v8i *)&xch_p[wave][lane * 8] = pf;
-                if (half == 0) xch_alpha[wave][l32] = alpha;
-                if (lane == 0) xch_flag[wave] = any_grow ? 1 : 0;
-                lds_barrier();
-                if (!o_active) continue;
-                const v8i pf_other = *(const v8i *)&xch_p[wave ^ 1][lane * 8];
-                const float alpha_other = xch_alpha[wave ^ 1][l32];
-                const bool grow_other = xch_flag[wave ^ 1] != 0;
-                if (any_grow) {
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-                }
-                if (grow_other) {
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) acc[8 + n] *= alpha_other;
-                }
-                const uint8_t *vp0 = slot + tr_off[0] + 64 * (4 * hw);
-                const uint8_t *vp1 = slot + tr_off[1] + 64 * (4 * hw);
-                auto vtile = [&](int n) {
-                    v8i f;
-                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
-                        f[2 * w2] = x[0];
-                        f[2 * w2 + 1] = x[1];
-                    }
-                    return f;
-                };
-                v8i vf = vtile(0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const v8i cur = vf;
-                    if (n + 1 < 8) vf = vtile(n + 1);
-                    acc[n] = mfma(cur, pf, acc[n]);
-                    acc[8 + n] = mfma(cur, pf_other, acc[8 + n]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
         if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
 
         // epilogue: normalise and store this split's FP32 partial and log2 LSE.
         // l_run is scaled by 2^kPScale like P, so the scale cancels in O / l.
         const size_t slot_idx = (size_t)off_r + s;
-        if constexpr (G < 4) {
-            if (active) {
-                const float l_tot = half_pair_sum(l_run);
-                const int row = row0 + l32;
-                if (row < M) {
-                    float *po = partial + (slot_idx * M + row) * kVDim;
-                    const float inv = a.out_scale / l_tot;
+        const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
+        if (half == 0) xch_alpha[wave][l32] = lq_tot;
+        lds_barrier();
+        const float lq_other = xch_alpha[wave ^ 1][l32];
+        if (active && half == 0 && row0 + l32 < M)
+            lse_out[slot_idx * M + row0 + l32] = m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) {
-                        const int dim = 32 * (dsi * NT + n) + 4 * half;
+        for (int own = 1; own >= 0; --own) {
+            const int row = jt * MT + 32 * (2 * pair + (own ? hw : 1 - hw)) + l32;
+            if (row < M) {
+                float *po = partial + (slot_idx * M + row) * kVDim;
+                const float inv = a.out_scale / (own ? lq_tot : lq_other);
 #pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            const v4f o = v4f{acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2],
-                                              acc[n][4 * q4 + 3]} * inv;
-                            *(v4f *)(po + dim + 8 * q4) = o;
-                        }
-                    }
-                    if (dsi == 0 && half == 0)
-                        lse_out[slot_idx * M + row] = m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
-                }
-            }
-        } else {
-            const int hw = wave & 1, pair = wave >> 1;
-            const float l_tot = half_pair_sum(l_run);
-            if (half == 0) xch_alpha[wave][l32] = l_tot;
-            lds_barrier();
-            const float l_other = xch_alpha[wave ^ 1][l32];
-            if (active && half == 0 && row0 + l32 < M)
-                lse_out[slot_idx * M + row0 + l32] = m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
+                for (int n = 0; n < 8; ++n) {
+                    const int dim = 32 * (8 * hw + n) + 4 * half;
 #pragma unroll
-            for (int own = 1; own >= 0; --own) {
-                const int row = jt * MT + 32 * (2 * pair + (own ? hw : 1 - hw)) + l32;
-                if (row < M) {
-                    float *po = partial + (slot_idx * M + row) * kVDim;
-                    const float inv = a.out_scale / (own ? l_tot : l_other);
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) {
-                        const int dim = 32 * (8 * hw + n) + 4 * half;
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            const v16f &t16 = acc[(own ? 0 : 8) + n];
-                            const v4f o = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2],
-                                              t16[4 * q4 + 3]} * inv;
-                            *(v4f *)(po + dim + 8 * q4) = o;
-                        }
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const v16f &t16 = acc[(own ? 0 : 8) + n];
+                        const v4f o = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2],
+                                          t16[4 * q4 + 3]} * inv;
+                        *(v4f *)(po + dim + 8 * q4) = o;
                     }
                 }
             }
         }
+
         lds_barrier();  // the next unit's prologue overwrites the ring
     }
 }
@@ -1359,7 +1223,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
     constexpr int MT = 32;
     constexpr int NT = kVDim / 64;   // 8 output tiles of 32 dims per wave
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
-    __shared__ float xm[2][32], xl[2][32];
+    __shared__ float xm[2][32], xl[2][32], xq[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1466,7 +1330,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
         lds_barrier();  // every wave has its Q^T: page 3 may overwrite it
         if (kSlots - 1 < size) issue(kSlots - 1, pid0[kSlots - 1]);
 
-        float m_run = -INFINITY, l_run = 0.f;
+        // l_run: row sum of the FP32 P (for the LSE); lq_run: of the E4M3 P that the MMA
+        // uses (O is normalised by it, so the weights of the output rows sum to one)
+        float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
         v16f acc[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
@@ -1539,6 +1405,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
                 const float m_new = grow ? mx : m_run;
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 l_run *= alpha;
+                lq_run *= alpha;
 #pragma unroll
                 for (int n = 0; n < NT; ++n) acc[n] *= alpha;
                 m_run = m_new;
@@ -1547,7 +1414,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
             v8i pf;
             {
                 const float bias = kPScale - m_run;
-                float psum = 0.f;
+                float psum = 0.f, qsum = 0.f;
 #pragma unroll
                 for (int g = 0; g < 8; ++g) {
                     const int b = g >> 2, qd = g & 3;
@@ -1560,8 +1427,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
                     int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
                     w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
                     pf[g] = w4;
+                    const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, false);
+                    const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
+                    qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
                 }
                 l_run += psum;
+                lq_run += qsum;
             }
             // O^T += V^T P^T over this wave's 8 tiles, transposed V reads one tile ahead
             {
@@ -1590,20 +1461,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
         }
         if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
 
-        // merge the two pairs: m = max_p m_p, l = sum_p l_p 2^(m_p - m) and
-        // O = sum_p O_p 2^(m_p - m) / l (l_run carries P's 2^kPScale, which cancels)
-        const float l_tot = half_pair_sum(l_run);
+        // merge the two pairs: m = max_p m_p, l = sum_p l_p 2^(m_p - m) (likewise lq) and
+        // O = sum_p O_p 2^(m_p - m) / lq (the sums carry P's 2^kPScale, which cancels)
+        const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
         if (hw == 0 && half == 0) {
             xm[pair][l32] = m_run;
             xl[pair][l32] = l_tot;
+            xq[pair][l32] = lq_tot;
         }
         lds_barrier();  // also: every wave is done with the ring
         const float m0 = xm[0][l32], m1 = xm[1][l32];
         const float m_all = fmaxf(m0, m1);
-        const float l_all = (m0 == -INFINITY ? 0.f : xl[0][l32] * __builtin_amdgcn_exp2f(m0 - m_all)) +
-                            (m1 == -INFINITY ? 0.f : xl[1][l32] * __builtin_amdgcn_exp2f(m1 - m_all));
+        const float e0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m_all);
+        const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_all);
+        const float l_all = xl[0][l32] * e0 + xl[1][l32] * e1;
+        const float lq_all = xq[0][l32] * e0 + xq[1][l32] * e1;
         const float f_own =
-            m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_all) * (a.out_scale / l_all);
+            m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_all) * (a.out_scale / lq_all);
         const size_t slot_idx = (size_t)off_r + s;
         if (wave == 0 && half == 0 && row < M)
             lse_out[slot_idx * M + row] = m_all + __builtin_amdgcn_logf(l_all) - kPScale;
@@ -1659,7 +1533,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
     __shared__ __attribute__((aligned(16))) int32_t xch_p[4][64 * 8];  // per wave: its P fragment
     __shared__ float xch_alpha[4][32];                                  // per-row rescale factor
     __shared__ int32_t xch_flag[4];                                     // any row rescaled
-    __shared__ float xm[2][2][32], xl[2][2][32];                        // [pair][block][row]
+    __shared__ float xm[2][2][32], xl[2][2][32], xq[2][2][32];          // [pair][block][row]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1753,7 +1627,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
         }
         wait_pages_then_barrier(0);
 
-        float m_run = -INFINITY, l_run = 0.f;
+        // l_run: row sum of the FP32 P (for the LSE); lq_run: of the E4M3 P that the MMA
+        // uses (O is normalised by it, so the weights of the output rows sum to one)
+        float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
         v16f acc[16];   // [0, 8): row block hw, [8, 16): block 1 - hw; dim tile 8*hw + n
 #pragma unroll
         for (int n = 0; n < 16; ++n) acc[n] = v16f{0};
@@ -1839,10 +1715,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
                     const float m_new = grow ? mx : m_run;
                     alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     l_run *= alpha;
+                    lq_run *= alpha;
                     m_run = m_new;
                 }
                 const float bias = kPScale - m_run;
-                float psum = 0.f;
+                float psum = 0.f, qsum = 0.f;
 #pragma unroll
                 for (int g = 0; g < 8; ++g) {
                     const int b = g >> 2, qd = g & 3;
@@ -1855,8 +1732,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
                     int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
                     w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
                     pf[g] = w4;
+                    const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, false);
+                    const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
+                    qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
                 }
                 l_run += psum;
+                lq_run += qsum;
             }
             // swap with the partner: P fragment, per-row rescale factor, rescale flag
             *(v8i *)&xch_p[wave][lane * 8] = pf;
@@ -1903,11 +1784,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
 
         // merge the pairs.  Block b's state of pair p (m, l over its pages) is in wave
         // 2p + b; its O for dims half h is in wave 2p + h (slot own if b == h).
-        const float l_tot = half_pair_sum(l_run);
+        const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
         lds_barrier();   // every wave is done with the ring and the exchange
         if (half == 0) {
             xm[pair][hw][l32] = m_run;
             xl[pair][hw][l32] = l_tot;
+            xq[pair][hw][l32] = lq_tot;
         }
         lds_barrier();
         float f_blk[2];          // this pair's factor for block hw (own) and 1 - hw
@@ -1917,10 +1799,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
             const int b = o == 0 ? hw : 1 - hw;
             const float m0 = xm[0][b][l32], m1 = xm[1][b][l32];
             const float mm = fmaxf(m0, m1);
-            const float ll = (m0 == -INFINITY ? 0.f : xl[0][b][l32] * __builtin_amdgcn_exp2f(m0 - mm)) +
-                             (m1 == -INFINITY ? 0.f : xl[1][b][l32] * __builtin_amdgcn_exp2f(m1 - mm));
+            const float e0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
+            const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+            const float ll = xl[0][b][l32] * e0 + xl[1][b][l32] * e1;
+            const float lq = xq[0][b][l32] * e0 + xq[1][b][l32] * e1;
             const float mine = xm[pair][b][l32];
-            f_blk[o] = mine == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mine - mm) * (a.out_scale / ll);
+            f_blk[o] = mine == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mine - mm) * (a.out_scale / lq);
             m_blk[o] = mm;
             l_blk[o] = ll;
         }
@@ -2241,7 +2125,7 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
     switch (params->mtile) {
     case 32: hipLaunchKernelGGL(decode32_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     case 64: hipLaunchKernelGGL(decode64_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
-    default: hipLaunchKernelGGL(decode_kernel<4>, grid, block, 0, st, AMLA_DECODE_ARGS); break;
+    default: hipLaunchKernelGGL(decode128_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     }
 #undef AMLA_DECODE_ARGS
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;

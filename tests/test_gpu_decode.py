@@ -53,6 +53,10 @@ SHAPES = [
     (2, 32, [130, 1]),
     (3, 32, [700, 0, 0, 129]),
     (4, 64, [1500, 64]),
+    (3, 11, [300, 64]),          # M = 33: a 64-row tile with one row in its second block
+    (5, 13, [129, 700]),         # M = 65: a 128-row tile with one row in its third block
+    (3, 43, [100, 640]),         # M = 129: two 128-row tiles, the second with one row
+    (16, 64, [70]),              # M = 1024, the most rows per request
     (7, 64, [1025, 3000]),
     (1, 3, [77, 500]),
 ]
@@ -147,8 +151,10 @@ def test_c5_unfolded_baseline_sampled():
     compare(wu, out, lse, rows=rows, tag="c5-unfolded")
 
 
-def test_graph_capture_replay():
-    w = wl.small(4, 4, 8, [3000, 1000, 64, 2200], seed=8)
+@pytest.mark.parametrize("k,H", [(4, 8), (7, 8), (4, 64)])
+def test_graph_capture_replay(k, H):
+    # one case per decode kernel (32-, 64- and 128-row tiles)
+    w = wl.small(4, k, H, [3000, 1000, 64, 2200], seed=8)
     q, kv, bt, lengths = to_dev(w)
     dec = binding.FoldedDecoder(w.R, w.M)
     bmm1, bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
