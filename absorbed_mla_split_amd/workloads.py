@@ -177,3 +177,18 @@ def small(R: int, k: int, H: int, lengths, seed: int = 0, extra_pages: int = 3,
                  value_std=value_std)
     pages = sum((int(v) + PAGE - 1) // PAGE for v in lengths)
     return generate(cfg, seed=seed, pool_pages=pages + extra_pages)
+
+
+UV_DIM = 128   # v_head_dim: the per-head output width of the W_UV up-projection
+
+
+def uv_weights(H: int, seed: int = 0, std: float | None = None) -> np.ndarray:
+    """Synthetic W_UV for H heads as BF16 bits (uint16), latent-contiguous: logical
+    [H, 512, 128], stored [H][128][512] (for each head and output dim, the 512 latent
+    weights are adjacent).  Values N(0, 1) * std (default 1/sqrt(512), so a projected row
+    keeps the scale of the latent), rounded to BF16 by torch's cast.  Drawn from their own
+    stream (seed, 1), so adding them leaves every other input unchanged."""
+    rng = np.random.default_rng([seed, 1])
+    s = np.float32(std if std is not None else 1.0 / math.sqrt(VDIM))
+    x = rng.standard_normal((H, UV_DIM, VDIM), dtype=np.float32) * s
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)

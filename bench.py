@@ -158,19 +158,13 @@ def main():
     out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, M), dtype=torch.float32, device=dev)
 
-    def step(i, ev=None):
+    def step(i):
         stream = torch.cuda.current_stream()
         dec.plan(lengths, bt.shape[1], stream)
-        if ev is not None:
-            ev[0].record(stream)
         binding.folded_decode(q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2,
                               dec.counts[:R], dec.offsets[:R + 1], dec.work, dec.workspace, stream)
-        if ev is not None:
-            ev[1].record(stream)
         binding.combine(dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params,
                         dec.compute_units, out, lse, stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -232,17 +226,28 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # Each kernel's own average duration, measured live with HIP events on the stream its
-    # launches run on: `steps` more steps launched one by one, with events around the
-    # decode and the combine of each (the launch latency before each event-bracketed
-    # kernel is included, so this is an upper bound on the kernel time); the plan
-    # alone, `steps` launches back to back between two events.
+    # launches run on: after one plan, `steps` launches of the kernel back to back between
+    # two events (the decode rotating over the KV pool copies like the timed steps), so the
+    # figure is the kernel's duration plus the dispatch gap between consecutive launches.
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    dec_avg = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    comb_avg = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    dec.plan(lengths, bt.shape[1], stream)
+
+    def timed(launch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        launch(0)
+        e0.record(stream)
+        for i in range(args.steps):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    dec_avg = timed(lambda i: binding.folded_decode(
+        q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2, dec.counts[:R],
+        dec.offsets[:R + 1], dec.work, dec.workspace, stream))
+    comb_avg = timed(lambda i: binding.combine(
+        dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params, dec.compute_units,
+        out, lse, stream))
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record(stream)
     for _ in range(args.steps):

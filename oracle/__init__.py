@@ -6,8 +6,9 @@ module, and this module imports nothing from the product package.
 
 The numeric parts (E4M3 decode, FP64 attention, LSE merge, split plan) live in
 ``oracle.c`` (built by ``oracle/build.py`` into ``liboracle.so``); this wrapper only
-marshals numpy arrays.  The host-side fold rules are small enough to state here in
-Python, each with the passage it follows.
+marshals numpy arrays.  The host-side fold rules and the value stage (the W_UV
+up-projection after the merge: a BF16 decode and one matrix product per head) are small
+enough to state here in Python, each with the passage it follows.
 """
 from __future__ import annotations
 
@@ -209,3 +210,38 @@ def fold_plan(k: int, heads: int, need_lse: bool, max_fold_heads: int) -> int:
     if not need_lse:
         return k
     return max(d for d in range(1, k + 1) if k % d == 0 and d * heads <= max_fold_heads)
+
+
+# ------------------------------------------------------------ value stage (W_UV)
+
+UVDIM = 128
+
+
+def bf16_values(bits) -> np.ndarray:
+    """BF16 bit patterns (uint16) -> float64.  A BF16 value is the float32 whose upper 16
+    bits are the pattern and whose lower 16 bits are zero."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):      # signalling-NaN patterns stay NaN
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def uv_project(latent, w_uv_bits, heads: int) -> np.ndarray:
+    """Attention output of folded rows: each merged latent row times its head's W_UV.
+
+    Page "drafter.attention", DraftDcp (value stage: the merged BF16 latent rows times
+    W_UV, accumulated in FP32 there, exactly here) and latent_major (W_UV [H, 512, 128]
+    stored latent-contiguous, [H][128][512] in memory).  Folded row i of a request is
+    draft token t = i // H of head h = i % H (page "drafter.attention", folded_decode), so
+    its output is the 128 values sum_c latent[r, i, c] * W_UV[h, c, v], which land at
+    [r * k + t, h * 128 + v] of the [R * k, H * 128] attention output.
+
+    latent: float64 [R, M, 512]; w_uv_bits: uint16 [H, 128, 512]; returns float64
+    [R, M, 128].
+    """
+    lat = np.asarray(latent, dtype=np.float64)
+    assert lat.ndim == 3 and lat.shape[2] == VDIM and lat.shape[1] % heads == 0
+    w = bf16_values(w_uv_bits).reshape(heads, UVDIM, VDIM)    # [h][v][c]
+    out = np.empty(lat.shape[:2] + (UVDIM,), dtype=np.float64)
+    for h in range(heads):
+        out[:, h::heads, :] = lat[:, h::heads, :] @ w[h].T     # rows i with i % H == h
+    return out
