@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libamla.so")
 PAGE = 64
 KDIM = 576
 VDIM = 512
+UVDIM = 128
 MAX_ROWS = 1024
 MAX_REQS = 4096
 MAX_SPLITS = 256
@@ -36,7 +37,7 @@ PLAN_FIXED = 1
 EXPORTS = (
     "amla_fold_plan", "amla_bmm_scales", "amla_decode_config", "amla_reducer_bands",
     "amla_workspace_bytes", "amla_plan_splits", "amla_folded_decode", "amla_combine",
-    "amla_status_string",
+    "amla_combine_uv", "amla_status_string",
 )
 
 
@@ -88,6 +89,7 @@ def load() -> ctypes.CDLL:
         "amla_folded_decode": (ctypes.c_int, [vp, vp, i64, vp, i32, vp, i32, pp, f32, f32, vp,
                                               vp, vp, i32, vp, sz, vp]),
         "amla_combine": (ctypes.c_int, [vp, sz, vp, vp, i32, pp, i32, vp, vp, vp]),
+        "amla_combine_uv": (ctypes.c_int, [vp, sz, vp, vp, i32, pp, i32, vp, vp, vp, vp, vp]),
         "amla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -186,6 +188,17 @@ def combine(workspace, counts, offsets, num_reqs, params: PlanParams, compute_un
         ctypes.byref(params), compute_units, _ptr(out), _ptr(lse), _stream(stream)))
 
 
+def combine_uv(workspace, counts, offsets, num_reqs, params: PlanParams, heads, w_uv, attn_out,
+               out=None, lse=None, stream=None):
+    """Merge fused with the W_UV up-projection: attn_out [R*k, heads*128] BF16 from the
+    split partials and W_UV (BF16 bits [heads][128][512], latent-contiguous); the merged
+    BF16 latent ``out`` and LSE ``lse`` are written only when given."""
+    _check("amla_combine_uv", load().amla_combine_uv(
+        _ptr(workspace), workspace.numel(), _ptr(counts), _ptr(offsets), num_reqs,
+        ctypes.byref(params), heads, _ptr(w_uv), _ptr(attn_out), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
 # ------------------------------------------------------------------------ the decoder
 
 class FoldedDecoder:
@@ -241,6 +254,27 @@ class FoldedDecoder:
         combine(self.workspace, self.counts[:R], self.offsets[:R + 1], R, self.params,
                 self.compute_units, out, lse, stream)
         return out, lse
+
+    def decode_uv(self, q, kv, block_table, lengths, bmm1, bmm2, heads, w_uv, attn_out=None,
+                  out=None, lse=None, stream=None):
+        """Decode, then the merge fused with W_UV: returns attn_out [R*k, heads*128] BF16
+        (``out``/``lse``, the merged latent and LSE, are filled only when given)."""
+        import torch
+
+        R, M = q.shape[0], q.shape[1]
+        if R != self.num_reqs or M != self.params.rows_per_req or M % heads:
+            raise ValueError("decode shape does not match the plan")
+        if w_uv.dtype not in (torch.uint16, torch.int16, torch.bfloat16) or \
+                tuple(w_uv.shape) != (heads, UVDIM, VDIM) or not w_uv.is_contiguous():
+            raise TypeError("w_uv is BF16 [heads, 128, 512] (latent-contiguous), contiguous")
+        if attn_out is None:
+            attn_out = torch.empty((R * (M // heads), heads * UVDIM), dtype=torch.bfloat16,
+                                   device=q.device)
+        folded_decode(q, kv, block_table, lengths, self.params, bmm1, bmm2, self.counts[:R],
+                      self.offsets[:R + 1], self.work, self.workspace, stream)
+        combine_uv(self.workspace, self.counts[:R], self.offsets[:R + 1], R, self.params, heads,
+                   w_uv, attn_out, out, lse, stream)
+        return attn_out
 
     def device_status(self) -> int:
         """The workspace's device status word (synchronises; for checks, not hot loops)."""

@@ -1979,6 +1979,152 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
         combine_row<1>(a, g, band, lane, i, c, base);
 }
 
+// ------------------------------------------------------- merge + W_UV (value stage)
+
+// Page "drafter.attention", DraftDcp (value stage): each row's split partials merged as in
+// combine_kernel, the merged latent rounded once to BF16, then multiplied by its head's
+// W_UV [H, 512, 128] on BF16 MFMA with FP32 accumulation, into the attention output
+// [R*k, H*128] (the same bytes as [R][M][128] in folded row order).  W_UV is stored
+// latent-contiguous ([H][128][512]; page "drafter.attention", latent_major), so every
+// MFMA operand fragment is 16 adjacent bytes.
+// One workgroup per (head h, 16 rows of that head); row j of head h is draft token
+// t = j % k of request r = j / k, folded row i = t*H + h.  16 threads merge one row; the
+// BF16 latent tile goes through LDS into the B operand of D[v][row] = W^T lat^T, so each
+// lane ends with four adjacent output dims of one row.
+constexpr int kUvDim = 128;
+constexpr int kUvRows = 16;
+constexpr int kUvStride = kVDim + 8;   // BF16 per LDS latent row: 16 B of padding moves
+                                       // each row four banks on (conflict-free B reads)
+constexpr int kUvBatch = 2;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct UvArgs {
+    const float *partial;
+    const float *lse;
+    const int32_t *counts;
+    const int32_t *offsets;
+    const uint16_t *w_uv;
+    uint16_t *attn_out;
+    uint16_t *out;       // merged BF16 latent, or null
+    float *out_lse;      // merged log2 LSE, or null
+    int32_t reqs, rows, heads, k, slots;
+};
+
+__global__ __launch_bounds__(256) void combine_uv_kernel(UvArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lat[kUvRows * kUvStride];
+    __shared__ float wts[kUvRows][AMLA_MAX_SPLITS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = blockIdx.y;
+    const int per_head = a.reqs * a.k;
+    const int j0 = blockIdx.x * kUvRows;
+
+    // W_UV fragments of this wave's 32 output dims for all 16 K-steps, loaded first (they
+    // do not depend on the merge).  A operand of the 16x16x32 MFMA: lane l holds
+    // W[h][v = 32 wave + 16 m + l%16][c = 32 s + 8 (l/16) .. +7].
+    bf16x8 wf[2][16];
+    {
+        const uint16_t *wh = a.w_uv + (size_t)h * kUvDim * kVDim + 8 * (lane >> 4);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const uint16_t *wv = wh + (size_t)(32 * wave + 16 * m + (lane & 15)) * kVDim;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) wf[m][s] = *(const bf16x8 *)(wv + 32 * s);
+        }
+    }
+
+    // merge (the weights of combine_row): thread t16 of row rho holds float4s t16 + 16 jj
+    const int rho = tid >> 4, t16 = tid & 15;
+    const int j = j0 + rho;
+    int r = 0, i = 0, c = 0;
+    int64_t base = 0;
+    if (j < per_head) {
+        r = j / a.k;
+        i = (j - r * a.k) * a.heads + h;
+        c = a.counts[r];
+        base = a.offsets[r];
+    }
+    const bool bad = c < 0 || c > AMLA_MAX_SPLITS || base < 0 || base + c > a.slots;
+    if (bad) c = 0;   // not a plan of these sizes: the row becomes NaN, nothing is read
+    const int64_t g = (int64_t)r * a.rows + i;
+    float mx = -INFINITY;
+    for (int s = t16; s < c; s += 16) mx = fmaxf(mx, a.lse[(base + s) * a.rows + i]);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float sum = 0.f;
+    for (int s = t16; s < c; s += 16) {
+        const float w = __builtin_amdgcn_exp2f(a.lse[(base + s) * a.rows + i] - mx);
+        wts[rho][s] = w;
+        sum += w;
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    __syncthreads();
+    const float inv = 1.0f / sum;
+
+    v4f acc[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[jj] = v4f{0, 0, 0, 0};
+    const float *prow = a.partial + (base * a.rows + i) * kVDim + 4 * t16;
+    for (int s0 = 0; s0 < c; s0 += kUvBatch) {
+        v4f p[kUvBatch][8];
+#pragma unroll
+        for (int b = 0; b < kUvBatch; ++b) {
+            const int s = s0 + b < c ? s0 + b : c - 1;
+            const float *ps = prow + (int64_t)s * a.rows * kVDim;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) p[b][jj] = *(const v4f *)(ps + 64 * jj);
+        }
+#pragma unroll
+        for (int b = 0; b < kUvBatch; ++b) {
+            const float w = s0 + b < c ? wts[rho][s0 + b] * inv : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) acc[jj] += w * p[b][jj];
+        }
+    }
+
+    // one BF16 rounding: the latent tile in LDS (and the optional global copy)
+    uint16_t *lrow = lat + rho * kUvStride + 4 * t16;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        uint32_t lo = 0x7FC07FC0u, hi = 0x7FC07FC0u;
+        if (!bad) {
+            lo = bf16_rne(acc[jj][0]) | ((uint32_t)bf16_rne(acc[jj][1]) << 16);
+            hi = bf16_rne(acc[jj][2]) | ((uint32_t)bf16_rne(acc[jj][3]) << 16);
+        }
+        *(uint2 *)(lrow + 64 * jj) = make_uint2(lo, hi);
+        if (a.out && j < per_head) *(uint2 *)(a.out + g * kVDim + 4 * t16 + 64 * jj) = make_uint2(lo, hi);
+    }
+    if (a.out_lse && j < per_head && t16 == 0)
+        a.out_lse[g] = bad ? NAN : c > 0 ? mx + __builtin_amdgcn_logf(sum) : -INFINITY;
+    __syncthreads();
+
+    // D[v][row] over K = 512 in 16 steps; B operand: lane l holds lat[row l%16][c = 32 s +
+    // 8 (l/16) .. +7]
+    v4f d[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
+    const uint16_t *lb = lat + (lane & 15) * kUvStride + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const bf16x8 bfr = *(const bf16x8 *)(lb + 32 * s);
+        d[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[0][s], bfr, d[0], 0, 0, 0);
+        d[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[1][s], bfr, d[1], 0, 0, 0);
+    }
+    // lane l holds D[v = 32 wave + 16 m + 4 (l/16) + e][row l%16], e < 4
+    const int jr = j0 + (lane & 15);
+    if (jr < per_head) {
+        const int rr = jr / a.k;
+        const int64_t gr = (int64_t)rr * a.rows + (int64_t)(jr - rr * a.k) * a.heads + h;
+        uint16_t *o = a.attn_out + gr * kUvDim + 32 * wave + 4 * (lane >> 4);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const uint32_t lo = bf16_rne(d[m][0]) | ((uint32_t)bf16_rne(d[m][1]) << 16);
+            const uint32_t hi = bf16_rne(d[m][2]) | ((uint32_t)bf16_rne(d[m][3]) << 16);
+            *(uint2 *)(o + 16 * m) = make_uint2(lo, hi);
+        }
+    }
+}
+
 // ----------------------------------------------------------------------- host helpers
 
 bool params_ok(const amla_plan_params *p)
@@ -2157,6 +2303,40 @@ int amla_combine(const void *d_workspace, size_t ws_bytes, const int32_t *d_coun
     a.slots = num_reqs + params->workers;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(rows * bands)), dim3(64), 0,
                        (hipStream_t)stream, a);
+    return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
+}
+
+int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_counts,
+                    const int32_t *d_offsets, int32_t num_reqs, const amla_plan_params *params,
+                    int32_t heads, const uint16_t *d_w_uv, uint16_t *d_attn_out,
+                    uint16_t *d_out, float *d_lse, void *stream)
+{
+    if (!params_ok(params) || num_reqs < 0 || num_reqs > AMLA_MAX_REQS || heads < 1 ||
+        params->rows_per_req % heads != 0 || !d_workspace ||
+        (num_reqs > 0 && (!d_counts || !d_offsets || !d_w_uv || !d_attn_out)) ||
+        ((uintptr_t)d_w_uv & 15) || ((uintptr_t)d_attn_out & 7) || ((uintptr_t)d_out & 7))
+        return AMLA_ERR_INVALID;
+    const WsLayout lay = ws_layout(num_reqs, params->rows_per_req, params->workers);
+    if (ws_bytes < lay.total) return AMLA_ERR_WORKSPACE;
+    if (num_reqs == 0) return AMLA_OK;
+    UvArgs a;
+    a.partial = (const float *)((const char *)d_workspace + lay.partial_off);
+    a.lse = (const float *)((const char *)d_workspace + lay.lse_off);
+    a.counts = d_counts;
+    a.offsets = d_offsets;
+    a.w_uv = d_w_uv;
+    a.attn_out = d_attn_out;
+    a.out = d_out;
+    a.out_lse = d_lse;
+    a.reqs = num_reqs;
+    a.rows = params->rows_per_req;
+    a.heads = heads;
+    a.k = params->rows_per_req / heads;
+    a.slots = num_reqs + params->workers;
+    const int64_t per_head = (int64_t)num_reqs * a.k;
+    hipLaunchKernelGGL(combine_uv_kernel,
+                       dim3((unsigned)((per_head + kUvRows - 1) / kUvRows), (unsigned)heads),
+                       dim3(256), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 

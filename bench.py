@@ -52,6 +52,9 @@ def parse():
                     help="also time a decode step of this many layers as the model runs it: "
                          "one plan, then decode + combine per layer, in one HIP graph "
                          "(0: skip)")
+    ap.add_argument("--uv", action="store_true",
+                    help="end each step with the merge fused with the W_UV up-projection "
+                         "(attention output [R*k, H*128]) instead of the plain merge")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
@@ -157,14 +160,24 @@ def main():
     bmm1, bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
     out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((R, M), dtype=torch.float32, device=dev)
+    H = w.M // w.cfg.k if not args.unfolded else w.M
+    w_uv = torch.from_numpy(wl.uv_weights(H).view(np.int16)).to(dev)
+    attn_out = torch.empty((R * (M // H), H * 128), dtype=torch.bfloat16, device=dev)
+
+    def merge(stream):
+        if args.uv:
+            binding.combine_uv(dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params,
+                               H, w_uv, attn_out, None, None, stream)
+        else:
+            binding.combine(dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params,
+                            dec.compute_units, out, lse, stream)
 
     def step(i):
         stream = torch.cuda.current_stream()
         dec.plan(lengths, bt.shape[1], stream)
         binding.folded_decode(q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2,
                               dec.counts[:R], dec.offsets[:R + 1], dec.work, dec.workspace, stream)
-        binding.combine(dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params,
-                        dec.compute_units, out, lse, stream)
+        merge(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -248,6 +261,9 @@ def main():
     comb_avg = timed(lambda i: binding.combine(
         dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params, dec.compute_units,
         out, lse, stream))
+    uv_avg = timed(lambda i: binding.combine_uv(
+        dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params, H, w_uv, attn_out,
+        None, None, stream))
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record(stream)
     for _ in range(args.steps):
@@ -266,8 +282,7 @@ def main():
                 binding.folded_decode(q, pools[li % len(pools)], bt, lengths, dec.params, bmm1,
                                       bmm2, dec.counts[:R], dec.offsets[:R + 1], dec.work,
                                       dec.workspace, s)
-                binding.combine(dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R,
-                                dec.params, dec.compute_units, out, lse, s)
+                merge(s)
         gl = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -317,6 +332,16 @@ def main():
     roof["algorithmic_bytes_per_launch"] = int(dec_alg_bytes)
     roof["flops_per_launch"] = flops
 
+    # the merge fused with the W_UV up-projection: split partials read, W_UV read once,
+    # BF16 attention output written; 2 * 512 * 128 BF16 MMA flop per row
+    n_items = int(dec.offsets[R].item())
+    uv_bytes = n_items * M * 513 * 4 + H * 128 * 512 * 2 + R * M * 128 * 2
+    value_stage = {"kernel": "combine_uv_kernel", "us": round(uv_avg * 1e3, 2),
+                   "bytes": int(uv_bytes), "gbs": round(uv_bytes / (uv_avg / 1e3) / 1e9, 1),
+                   "hbm_frac": round(uv_bytes / (uv_avg / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "flop": 2 * R * M * 512 * 128,
+                   "in_step": bool(args.uv)}
+
     cfg = w.cfg
     workload = (f"{args.config}: R={cfg.R} k={cfg.k} H={cfg.H} (M={cfg.M}), {cfg.description}"
                 + (" [unfolded R*k rows]" if args.unfolded else ""))
@@ -343,8 +368,9 @@ def main():
         "step_us": round(ms_per_step * 1e3, 2),
         "decode_us": round(dec_avg * 1e3, 2),
         "combine_us": round(comb_avg * 1e3, 2),
+        "value_stage": value_stage,
         "plan_us": round(plan_us, 2),
-        "layer_kv_gbs": round(kv_bytes / ((dec_avg + comb_avg) / 1e3) / 1e9, 1),
+        "layer_kv_gbs": round(kv_bytes / ((dec_avg + (uv_avg if args.uv else comb_avg)) / 1e3) / 1e9, 1),
         "layered_step": amortized,
         "roofline": roof,
         "wall_s": round(wall, 3),

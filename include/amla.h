@@ -41,6 +41,7 @@ extern "C" {
 #define AMLA_PAGE 64          /* tokens per cache page */
 #define AMLA_KDIM 576         /* bytes (E4M3 codes) per token row: 512 latent + 64 rope */
 #define AMLA_VDIM 512         /* value dims: the latent part */
+#define AMLA_UVDIM 128        /* output dims per head of the W_UV up-projection */
 #define AMLA_MAX_ROWS 1024    /* most folded rows per request (k*H) */
 #define AMLA_MAX_REQS 4096    /* most requests one plan takes */
 #define AMLA_MAX_SPLITS 256   /* most splits per request */
@@ -187,6 +188,26 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
 int amla_combine(const void *d_workspace, size_t ws_bytes, const int32_t *d_counts,
                  const int32_t *d_offsets, int32_t num_reqs, const amla_plan_params *params,
                  int32_t compute_units, uint16_t *d_out, float *d_lse, void *stream);
+
+/*
+ * Reducer fused with the W_UV up-projection (the value stage after the merge; page
+ * "drafter.attention", DraftDcp and latent_major).  Each row's split partials are merged
+ * exactly as amla_combine does (one BF16 rounding of the merged latent), then multiplied by
+ * its head's W_UV on BF16 MFMA with FP32 accumulation and rounded to BF16:
+ *   attn_out[r*k + t][h*128 + v] = sum_c latent[r][t*H + h][c] * W_UV[h][c][v]
+ *   d_w_uv      BF16 bits, W_UV [heads][512][128] stored latent-contiguous, i.e. the
+ *               memory is [heads][128][512] (the 512 latent weights of one (h, v) are
+ *               adjacent); 16-byte aligned
+ *   d_attn_out  BF16 [num_reqs * k][heads * 128] (k = rows_per_req / heads), 8-byte aligned
+ *   d_out       optional (NULL: not written): the merged BF16 latent [num_reqs][M][512]
+ *   d_lse       optional (NULL: not written): the merged FP32 log2 LSE [num_reqs][M]
+ * heads must divide rows_per_req.  Requests with count 0 give zero rows (lse -inf).
+ * AMLA_ERR_INVALID for null or misaligned pointers, heads < 1 or heads not dividing M.
+ */
+int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_counts,
+                    const int32_t *d_offsets, int32_t num_reqs, const amla_plan_params *params,
+                    int32_t heads, const uint16_t *d_w_uv, uint16_t *d_attn_out,
+                    uint16_t *d_out, float *d_lse, void *stream);
 
 /* Static text for a host status code or a device status word. */
 const char *amla_status_string(int status);

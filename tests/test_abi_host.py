@@ -42,6 +42,7 @@ def test_header_constants_match_binding():
     consts = dict(re.findall(r"#define (AMLA_\w+) \(?(-?\d+)\)?", text))
     assert int(consts["AMLA_PAGE"]) == b.PAGE and int(consts["AMLA_KDIM"]) == b.KDIM
     assert int(consts["AMLA_VDIM"]) == b.VDIM and int(consts["AMLA_MAX_ROWS"]) == b.MAX_ROWS
+    assert int(consts["AMLA_UVDIM"]) == b.UVDIM
     assert int(consts["AMLA_MAX_REQS"]) == b.MAX_REQS
     assert int(consts["AMLA_ERR_WORKSPACE"]) == b.ERR_WORKSPACE
     assert int(consts["AMLA_DEV_BAD_PAGE"]) == b.DEV_BAD_PAGE
@@ -166,6 +167,26 @@ def test_decode_and_combine_argument_errors():
         assert comb(**bad) == b.ERR_INVALID, bad
     assert comb(ws_bytes=10) == b.ERR_WORKSPACE
     assert comb(reqs=0) == b.OK
+
+
+def test_combine_uv_argument_errors():
+    lib = b.load()
+    p = b.make_params(32, 32, 256)
+    vp = ctypes.c_void_p
+
+    def uv(ws=256, ws_bytes=1 << 30, counts=256, offsets=256, reqs=2, heads=8, w=256, ao=256,
+           out=0, lse=0, params=p):
+        return lib.amla_combine_uv(vp(ws), ws_bytes, vp(counts), vp(offsets), reqs,
+                                   ctypes.byref(params), heads, vp(w), vp(ao), vp(out), vp(lse),
+                                   None)
+
+    for bad in (dict(ws=0), dict(counts=0), dict(offsets=0), dict(w=0), dict(ao=0), dict(reqs=-1),
+                dict(heads=0), dict(heads=3), dict(heads=64), dict(w=264), dict(ao=260),
+                dict(out=258), dict(params=b.make_params(32, 48, 256))):
+        assert uv(**bad) == b.ERR_INVALID, bad
+    assert uv(ws_bytes=10) == b.ERR_WORKSPACE
+    assert uv(reqs=0) == b.OK              # nothing to do, nothing launched
+    assert uv(reqs=0, heads=32) == b.OK
 
 
 def test_status_strings():
