@@ -1987,15 +1987,16 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
 // [R*k, H*128] (the same bytes as [R][M][128] in folded row order).  W_UV is stored
 // latent-contiguous ([H][128][512]; page "drafter.attention", latent_major), so every
 // MFMA operand fragment is 16 adjacent bytes.
-// One workgroup per (head h, 16 rows of that head); row j of head h is draft token
-// t = j % k of request r = j / k, folded row i = t*H + h.  16 threads merge one row; the
-// BF16 latent tile goes through LDS into the B operand of D[v][row] = W^T lat^T, so each
-// lane ends with four adjacent output dims of one row.
+// One workgroup of 8 waves per (head h, 16 rows of that head); row j of head h is draft
+// token t = j % k of request r = j / k, folded row i = t*H + h.  32 threads merge one row;
+// the BF16 latent tile goes through LDS into the B operand of D[v][row] = W^T lat^T, wave w
+// computing output dims [16w, 16w + 16), so each lane ends with four adjacent output dims
+// of one row.
 constexpr int kUvDim = 128;
 constexpr int kUvRows = 16;
 constexpr int kUvStride = kVDim + 8;   // BF16 per LDS latent row: 16 B of padding moves
                                        // each row four banks on (conflict-free B reads)
-constexpr int kUvBatch = 2;
+constexpr int kUvBatch = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -2011,31 +2012,33 @@ struct UvArgs {
     int32_t reqs, rows, heads, k, slots;
 };
 
-__global__ __launch_bounds__(256) void combine_uv_kernel(UvArgs a)
+template <int ROWS>
+__global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
 {
+    constexpr int TPR = 512 / ROWS;        // threads per row: 32 or 64
+    constexpr int NJ = kVDim / 4 / TPR;    // float4s per thread and split: 4 or 2
     __shared__ __attribute__((aligned(16))) uint16_t lat[kUvRows * kUvStride];
     __shared__ float wts[kUvRows][AMLA_MAX_SPLITS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y;
     const int per_head = a.reqs * a.k;
-    const int j0 = blockIdx.x * kUvRows;
+    const int j0 = blockIdx.x * ROWS;
 
-    // W_UV fragments of this wave's 32 output dims for all 16 K-steps, loaded first (they
+    // W_UV fragments of this wave's 16 output dims for all 16 K-steps, loaded first (they
     // do not depend on the merge).  A operand of the 16x16x32 MFMA: lane l holds
-    // W[h][v = 32 wave + 16 m + l%16][c = 32 s + 8 (l/16) .. +7].
-    bf16x8 wf[2][16];
+    // W[h][v = 16 wave + l%16][c = 32 s + 8 (l/16) .. +7].
+    bf16x8 wf[16];
     {
-        const uint16_t *wh = a.w_uv + (size_t)h * kUvDim * kVDim + 8 * (lane >> 4);
+        const uint16_t *wv = a.w_uv + ((size_t)h * kUvDim + 16 * wave + (lane & 15)) * kVDim +
+                             8 * (lane >> 4);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const uint16_t *wv = wh + (size_t)(32 * wave + 16 * m + (lane & 15)) * kVDim;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) wf[m][s] = *(const bf16x8 *)(wv + 32 * s);
-        }
+        for (int s = 0; s < 16; ++s) wf[s] = *(const bf16x8 *)(wv + 32 * s);
     }
 
-    // merge (the weights of combine_row): thread t16 of row rho holds float4s t16 + 16 jj
-    const int rho = tid >> 4, t16 = tid & 15;
+    // merge (the weights of combine_row): TPR threads per row; thread t32 of row rho holds
+    // float4s t32 + TPR jj (jj < NJ).  The row's first LSEs and its first batch of partials
+    // are loaded together, right after the request's count and offset.
+    const int rho = tid / TPR, t32 = tid % TPR;
     const int j = j0 + rho;
     int r = 0, i = 0, c = 0;
     int64_t base = 0;
@@ -2047,81 +2050,101 @@ __global__ __launch_bounds__(256) void combine_uv_kernel(UvArgs a)
     }
     const bool bad = c < 0 || c > AMLA_MAX_SPLITS || base < 0 || base + c > a.slots;
     if (bad) c = 0;   // not a plan of these sizes: the row becomes NaN, nothing is read
+    if (c == 0) base = 0;   // every address formed below stays inside slot 0
     const int64_t g = (int64_t)r * a.rows + i;
-    float mx = -INFINITY;
-    for (int s = t16; s < c; s += 16) mx = fmaxf(mx, a.lse[(base + s) * a.rows + i]);
+    const float *lrow_g = a.lse + base * a.rows + i;              // split s at s * rows
+    const float *prow = a.partial + (base * a.rows + i) * kVDim + 4 * t32;
+    const int64_t pstride = (int64_t)a.rows * kVDim;
+
+    float ls = t32 < c ? lrow_g[(int64_t)t32 * a.rows] : -INFINITY;
+    v4f p[kUvBatch][NJ];
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int b = 0; b < kUvBatch; ++b) {
+        const int sb = b < c ? b : (c > 0 ? c - 1 : 0);
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+            p[b][jj] = c > 0 ? *(const v4f *)(prow + sb * pstride + 4 * TPR * jj) : v4f{0, 0, 0, 0};
+    }
+    float mx = ls;
+    for (int s = t32 + TPR; s < c; s += TPR) mx = fmaxf(mx, lrow_g[(int64_t)s * a.rows]);
+#pragma unroll
+    for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float sum = 0.f;
-    for (int s = t16; s < c; s += 16) {
-        const float w = __builtin_amdgcn_exp2f(a.lse[(base + s) * a.rows + i] - mx);
+    if (t32 < c) {
+        const float w = __builtin_amdgcn_exp2f(ls - mx);
+        wts[rho][t32] = w;
+        sum = w;
+    }
+    for (int s = t32 + TPR; s < c; s += TPR) {
+        const float w = __builtin_amdgcn_exp2f(lrow_g[(int64_t)s * a.rows] - mx);
         wts[rho][s] = w;
         sum += w;
     }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    for (int o = TPR / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
     __syncthreads();
     const float inv = 1.0f / sum;
 
-    v4f acc[8];
+    v4f acc[NJ];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc[jj] = v4f{0, 0, 0, 0};
-    const float *prow = a.partial + (base * a.rows + i) * kVDim + 4 * t16;
+    for (int jj = 0; jj < NJ; ++jj) acc[jj] = v4f{0, 0, 0, 0};
     for (int s0 = 0; s0 < c; s0 += kUvBatch) {
-        v4f p[kUvBatch][8];
+        if (s0 > 0) {
 #pragma unroll
-        for (int b = 0; b < kUvBatch; ++b) {
-            const int s = s0 + b < c ? s0 + b : c - 1;
-            const float *ps = prow + (int64_t)s * a.rows * kVDim;
+            for (int b = 0; b < kUvBatch; ++b) {
+                const int sb = s0 + b < c ? s0 + b : c - 1;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) p[b][jj] = *(const v4f *)(ps + 64 * jj);
+                for (int jj = 0; jj < NJ; ++jj)
+                    p[b][jj] = *(const v4f *)(prow + sb * pstride + 4 * TPR * jj);
+            }
         }
 #pragma unroll
         for (int b = 0; b < kUvBatch; ++b) {
             const float w = s0 + b < c ? wts[rho][s0 + b] * inv : 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) acc[jj] += w * p[b][jj];
+            for (int jj = 0; jj < NJ; ++jj) acc[jj] += w * p[b][jj];
         }
     }
 
     // one BF16 rounding: the latent tile in LDS (and the optional global copy)
-    uint16_t *lrow = lat + rho * kUvStride + 4 * t16;
+    uint16_t *lrow = lat + rho * kUvStride + 4 * t32;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
+    for (int jj = 0; jj < NJ; ++jj) {
         uint32_t lo = 0x7FC07FC0u, hi = 0x7FC07FC0u;
         if (!bad) {
             lo = bf16_rne(acc[jj][0]) | ((uint32_t)bf16_rne(acc[jj][1]) << 16);
             hi = bf16_rne(acc[jj][2]) | ((uint32_t)bf16_rne(acc[jj][3]) << 16);
         }
-        *(uint2 *)(lrow + 64 * jj) = make_uint2(lo, hi);
-        if (a.out && j < per_head) *(uint2 *)(a.out + g * kVDim + 4 * t16 + 64 * jj) = make_uint2(lo, hi);
+        *(uint2 *)(lrow + 4 * TPR * jj) = make_uint2(lo, hi);
+        if (a.out && j < per_head)
+            *(uint2 *)(a.out + g * kVDim + 4 * t32 + 4 * TPR * jj) = make_uint2(lo, hi);
     }
-    if (a.out_lse && j < per_head && t16 == 0)
+    if (ROWS < kUvRows) {   // the MFMA's 16 rows: the tile's unused rows are zero
+        for (int x = tid; x < (kUvRows - ROWS) * kVDim / 4; x += 512)
+            *(uint2 *)(lat + (ROWS + x / (kVDim / 4)) * kUvStride + 4 * (x % (kVDim / 4))) =
+                make_uint2(0u, 0u);
+    }
+    if (a.out_lse && j < per_head && t32 == 0)
         a.out_lse[g] = bad ? NAN : c > 0 ? mx + __builtin_amdgcn_logf(sum) : -INFINITY;
     __syncthreads();
 
     // D[v][row] over K = 512 in 16 steps; B operand: lane l holds lat[row l%16][c = 32 s +
     // 8 (l/16) .. +7]
-    v4f d[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
+    v4f d = v4f{0, 0, 0, 0};
     const uint16_t *lb = lat + (lane & 15) * kUvStride + 8 * (lane >> 4);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
         const bf16x8 bfr = *(const bf16x8 *)(lb + 32 * s);
-        d[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[0][s], bfr, d[0], 0, 0, 0);
-        d[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[1][s], bfr, d[1], 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s], bfr, d, 0, 0, 0);
     }
-    // lane l holds D[v = 32 wave + 16 m + 4 (l/16) + e][row l%16], e < 4
+    // lane l holds D[v = 16 wave + 4 (l/16) + e][row l%16], e < 4
     const int jr = j0 + (lane & 15);
-    if (jr < per_head) {
+    if ((lane & 15) < ROWS && jr < per_head) {
         const int rr = jr / a.k;
         const int64_t gr = (int64_t)rr * a.rows + (int64_t)(jr - rr * a.k) * a.heads + h;
-        uint16_t *o = a.attn_out + gr * kUvDim + 32 * wave + 4 * (lane >> 4);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const uint32_t lo = bf16_rne(d[m][0]) | ((uint32_t)bf16_rne(d[m][1]) << 16);
-            const uint32_t hi = bf16_rne(d[m][2]) | ((uint32_t)bf16_rne(d[m][3]) << 16);
-            *(uint2 *)(o + 16 * m) = make_uint2(lo, hi);
-        }
+        const uint32_t lo = bf16_rne(d[0]) | ((uint32_t)bf16_rne(d[1]) << 16);
+        const uint32_t hi = bf16_rne(d[2]) | ((uint32_t)bf16_rne(d[3]) << 16);
+        *(uint2 *)(a.attn_out + gr * kUvDim + 16 * wave + 4 * (lane >> 4)) = make_uint2(lo, hi);
     }
 }
 
@@ -2334,9 +2357,16 @@ int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_c
     a.k = params->rows_per_req / heads;
     a.slots = num_reqs + params->workers;
     const int64_t per_head = (int64_t)num_reqs * a.k;
-    hipLaunchKernelGGL(combine_uv_kernel,
-                       dim3((unsigned)((per_head + kUvRows - 1) / kUvRows), (unsigned)heads),
-                       dim3(256), 0, (hipStream_t)stream, a);
+    // 16-row tiles, or 8-row tiles when 16-row tiles would leave compute units idle
+    const int64_t tiles16 = (per_head + kUvRows - 1) / kUvRows;
+    if (tiles16 * heads >= 256)
+        hipLaunchKernelGGL(combine_uv_kernel<kUvRows>, dim3((unsigned)tiles16, (unsigned)heads),
+                           dim3(512), 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(combine_uv_kernel<kUvRows / 2>,
+                           dim3((unsigned)((per_head + kUvRows / 2 - 1) / (kUvRows / 2)),
+                                (unsigned)heads),
+                           dim3(512), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 

@@ -114,7 +114,8 @@ SHAPES = [
     (2, 32, [130, 1]),
     (4, 64, [1500, 64]),
     (3, 11, [300, 64]),              # 6 rows per head: one partial 16-row tile
-    (16, 64, [70]),                  # M = 1024
+    (16, 64, [70]),                  # M = 1024 (8-row tiles)
+    (16, 64, [70, 130, 64, 1]),      # 4 x 16-row tiles per head, 256 workgroups: 16-row tiles
     (5, 4, [900, 64, 2000, 7, 333]),  # 25 rows per head: a full and a partial tile
 ]
 
