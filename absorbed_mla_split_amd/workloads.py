@@ -192,3 +192,38 @@ def uv_weights(H: int, seed: int = 0, std: float | None = None) -> np.ndarray:
     s = np.float32(std if std is not None else 1.0 / math.sqrt(VDIM))
     x = rng.standard_normal((H, UV_DIM, VDIM), dtype=np.float32) * s
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def dcp_shards(w: Workload, world: int, interleave: int, seed: int = 0) -> list[Workload]:
+    """Split a workload's KV cache over `world` decode-context-parallel ranks.
+
+    Global position p of a request is stored on rank (p // interleave) % world, at local
+    position (p // (interleave * world)) * interleave + p % interleave: blocks of
+    `interleave` tokens dealt round-robin over the ranks.  Each rank gets its own paged
+    pool (shuffled pages from a seeded permutation, NaN codes past each request's local
+    length and in spare pages), block table and local lengths; every rank keeps the whole
+    query.  Pure data movement: the rows are copied from the global cache unchanged."""
+    rng = np.random.default_rng([seed, 2, world, interleave])
+    R = w.R
+    out = []
+    for d in range(world):
+        locs = []
+        for r in range(R):
+            T = int(w.lengths[r])
+            p = np.arange(T, dtype=np.int64)
+            mine = p[(p // interleave) % world == d]
+            locs.append(mine)
+        lengths = np.array([len(m) for m in locs], dtype=np.int32)
+        pages = (lengths.astype(np.int64) + PAGE - 1) // PAGE
+        pool = int(pages.sum()) + 2
+        bt, used = build_tables(lengths, pool, rng)
+        kv = np.full((pool, PAGE, KDIM), NAN_CODE, dtype=np.uint8)
+        for r in range(R):
+            mine = locs[r]
+            if len(mine) == 0:
+                continue
+            src = w.kv8[w.block_table[r, mine // PAGE], mine % PAGE]     # [L_d, 576]
+            j = np.arange(len(mine))
+            kv[bt[r, j // PAGE], j % PAGE] = src
+        out.append(Workload(w.cfg, lengths, bt, w.q8, kv, w.q_scale, w.k_scale, w.sm_scale))
+    return out

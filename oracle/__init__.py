@@ -245,3 +245,79 @@ def uv_project(latent, w_uv_bits, heads: int) -> np.ndarray:
     for h in range(heads):
         out[:, h::heads, :] = lat[:, h::heads, :] @ w[h].T     # rows i with i % H == h
     return out
+
+
+# ------------------------------------------------- decode context parallelism (DCP)
+
+def dcp_owner(p: int, world: int, interleave: int):
+    """(rank, local position) of global KV position p under DCP.
+
+    Page "...cutedsl.mla.balanced", BalancedMla.decode: a rank holds a shard of each
+    request's KV, described by cp = (world, rank, interleave).  Reading: blocks of
+    `interleave` consecutive positions are dealt round-robin over the ranks, and a rank
+    keeps its positions in global order."""
+    blk = p // interleave
+    return blk % world, (blk // world) * interleave + p % interleave
+
+
+def dcp_local_count(n: int, world: int, rank: int, interleave: int) -> int:
+    """How many of the global positions 0 .. n-1 the rank holds (by enumeration)."""
+    if n <= 0:
+        return 0
+    p = np.arange(n, dtype=np.int64)
+    return int(np.count_nonzero((p // interleave) % world == rank))
+
+
+def visible_keys(total: int, k: int, t: int, causal: bool) -> int:
+    """Global keys visible to draft token t (0 <= t < k) of a request of `total` keys
+    (the block included).  Non-causal (page "drafter.attention", module docstring): the
+    whole cache.  Causal (page "...cutedsl.mla.balanced", module docstring and
+    BalancedMla.decode, the causal mask in global positions from the global lengths):
+    token t sits at position total - k + t and sees positions up to and including it."""
+    return total if not causal else max(0, total - k + t + 1)
+
+
+def decode_causal(q8, kv8, block_table, totals, k, heads, q_scale, k_scale, sm_scale,
+                  causal=True, rows=None):
+    """Unsharded folded decode with each row's own key range [0, visible_keys)."""
+    R, M = q8.shape[0], q8.shape[1]
+    if rows is None:
+        rows = [(r, i) for r in range(R) for i in range(M)]
+    tasks = [(r, i, 0, visible_keys(int(totals[r]), k, i // heads, causal)) for r, i in rows]
+    return attend(q8, kv8, block_table, totals, np.array(tasks, np.int32).reshape(-1, 4),
+                  q_scale, k_scale, sm_scale)
+
+
+def decode_dcp_rank(q8, kv8, block_table, local_lengths, totals, k, heads, q_scale, k_scale,
+                    sm_scale, world, rank, interleave, causal=True, rows=None):
+    """One rank's folded decode over its local shard: row i of request r attends to the
+    rank's local keys whose global positions the row may see (a prefix of the shard,
+    since the rank keeps its positions in global order).  Returns (out, lse) per row;
+    rows that see none of the rank's keys get out 0 and lse -inf."""
+    R, M = q8.shape[0], q8.shape[1]
+    if rows is None:
+        rows = [(r, i) for r in range(R) for i in range(M)]
+    tasks = []
+    for r, i in rows:
+        n = visible_keys(int(totals[r]), k, i // heads, causal)
+        lim = dcp_local_count(n, world, rank, interleave)
+        assert lim <= int(local_lengths[r])
+        tasks.append((r, i, 0, lim))
+    return attend(q8, kv8, block_table, local_lengths, np.array(tasks, np.int32).reshape(-1, 4),
+                  q_scale, k_scale, sm_scale)
+
+
+def merge_sources(outs, lses):
+    """Rows from several DCP sources merged (page "drafter.attention", DraftDcp: exp2
+    weights of lse_s - max over their sum): outs [S, n, 512], lses [S, n] -> (out [n, 512],
+    lse [n]); a row every source leaves empty stays out 0, lse -inf."""
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    n = outs.shape[1]
+    out = np.zeros((n, VDIM))
+    lse = np.full(n, -np.inf)
+    for j in range(n):
+        if np.all(np.isneginf(lses[:, j])):
+            continue
+        out[j], lse[j] = merge(outs[:, j], lses[:, j])
+    return out, lse
