@@ -37,8 +37,9 @@ PLAN_FIXED = 1
 EXPORTS = (
     "amla_fold_plan", "amla_bmm_scales", "amla_decode_config", "amla_reducer_bands",
     "amla_workspace_bytes", "amla_plan_splits", "amla_folded_decode", "amla_combine",
-    "amla_combine_uv", "amla_status_string",
+    "amla_combine_uv", "amla_folded_decode_dcp", "amla_merge_sources", "amla_status_string",
 )
+MAX_SOURCES = 64
 
 
 class PlanParams(ctypes.Structure):
@@ -55,6 +56,17 @@ class PlanParams(ctypes.Structure):
         return ("PlanParams(rows_per_req=%d, mtile=%d, workers=%d, min_split_tokens=%d, "
                 "max_splits=%d, mode=%d)" % (self.rows_per_req, self.mtile, self.workers,
                                              self.min_split_tokens, self.max_splits, self.mode))
+
+
+class DcpParams(ctypes.Structure):
+    """amla_dcp_params: the KV shard of one decode-context-parallel rank."""
+    _fields_ = [
+        ("heads", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("world", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("interleave", ctypes.c_int32),
+    ]
 
 
 class AmlaError(RuntimeError):
@@ -90,6 +102,10 @@ def load() -> ctypes.CDLL:
                                               vp, vp, i32, vp, sz, vp]),
         "amla_combine": (ctypes.c_int, [vp, sz, vp, vp, i32, pp, i32, vp, vp, vp]),
         "amla_combine_uv": (ctypes.c_int, [vp, sz, vp, vp, i32, pp, i32, vp, vp, vp, vp, vp]),
+        "amla_folded_decode_dcp": (ctypes.c_int, [vp, vp, i64, vp, i32, vp, i32, pp, f32, f32,
+                                                  vp, vp, vp, i32, vp, sz,
+                                                  ctypes.POINTER(DcpParams), vp, vp]),
+        "amla_merge_sources": (ctypes.c_int, [i32, vp, vp, i64, vp, vp, vp]),
         "amla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -186,6 +202,26 @@ def combine(workspace, counts, offsets, num_reqs, params: PlanParams, compute_un
     _check("amla_combine", load().amla_combine(
         _ptr(workspace), workspace.numel(), _ptr(counts), _ptr(offsets), num_reqs,
         ctypes.byref(params), compute_units, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def folded_decode_dcp(q, kv, block_table, lengths, params: PlanParams, bmm1, bmm2, counts,
+                      offsets, work, workspace, dcp: DcpParams, totals=None, stream=None):
+    """Decode of one DCP rank's KV shard (``lengths``: local; ``totals``: global lengths,
+    needed for the causal mask)."""
+    _check("amla_folded_decode_dcp", load().amla_folded_decode_dcp(
+        _ptr(q), _ptr(kv), kv.shape[0], _ptr(block_table), block_table.stride(0),
+        _ptr(lengths), lengths.numel(), ctypes.byref(params), bmm1, bmm2, _ptr(counts),
+        _ptr(offsets), _ptr(work), work.numel(), _ptr(workspace), workspace.numel(),
+        ctypes.byref(dcp), _ptr(totals), _stream(stream)))
+
+
+def merge_sources(rows, lse, out, lse_out, stream=None):
+    """Merge BF16 rows [S, n, 512] with log2 LSE [S, n] over the S sources into out
+    [n, 512] BF16 and lse_out [n]."""
+    n_src = rows.shape[0]
+    n_rows = rows[0].numel() // VDIM if n_src else 0
+    _check("amla_merge_sources", load().amla_merge_sources(
+        n_src, _ptr(rows), _ptr(lse), n_rows, _ptr(out), _ptr(lse_out), _stream(stream)))
 
 
 def combine_uv(workspace, counts, offsets, num_reqs, params: PlanParams, heads, w_uv, attn_out,

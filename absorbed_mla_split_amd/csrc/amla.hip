@@ -700,7 +700,37 @@ struct DecodeArgs {
     int32_t bt_stride, reqs, rows, mtile, workers, list_len;
     float score_scale;  // bmm1 * log2(e)
     float out_scale;    // bmm2
+    // causal mask in global positions over a DCP shard (causal == 0: every row sees the
+    // request's whole local length; the other fields are then unused)
+    const int32_t *totals;
+    int32_t causal, heads, k_tokens, cp_world, cp_rank, cp_interleave;
 };
+
+// Keys of the local shard that folded row `row` may see.  Page "...cutedsl.mla.balanced",
+// module docstring and BalancedMla.decode: under DCP the decode reads this rank's shard
+// and masks causally in global positions, from the requests' global lengths.  Draft token
+// t = row / H of a request of `total` global keys sits at position total - k + t and sees
+// the g = total - k + t + 1 positions before it and itself; the rank holds blocks of
+// `interleave` positions dealt round-robin over `world` ranks, in global order, so the
+// visible keys are the first (g / span) * interleave + clamp(g % span - rank * interleave,
+// 0, interleave) of its shard (span = interleave * world).
+__device__ __forceinline__ int shard_count(const DecodeArgs &a, int g)
+{
+    if (g <= 0) return 0;
+    const uint32_t span = (uint32_t)a.cp_interleave * (uint32_t)a.cp_world;
+    const int rem = (int)((uint32_t)g % span) - a.cp_rank * a.cp_interleave;
+    return (int)((uint32_t)g / span) * a.cp_interleave +
+           (rem < 0 ? 0 : rem > a.cp_interleave ? a.cp_interleave : rem);
+}
+
+__device__ __forceinline__ int row_key_limit(const DecodeArgs &a, int total, int L, int row)
+{
+    if (!a.causal) return L;
+    int t = row / a.heads;
+    t = t < a.k_tokens - 1 ? t : a.k_tokens - 1;   // rows past M: any limit will do
+    const int n = shard_count(a, total - a.k_tokens + t + 1);
+    return n < L ? n : L;
+}
 
 // s_waitcnt immediates for gfx9: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 constexpr int waitcnt_imm(int vm, int lgkm)
@@ -941,7 +971,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         // that the loads stay in bounds before r is checked)
         const int rc = r >= 0 && r < R ? r : 0;
         const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r));
+        const int total = a.causal ? ldc(&a.totals[rc]) : L;
+        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
         const int pages = ceil_div(L, kPage);
         const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
         const int first = s * q + (s < rem ? s : rem);
@@ -951,7 +982,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
             if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
             continue;
         }
+        if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
+            atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
         const int row0 = jt * MT + 32 * wave;   // this wave's score rows
+        const int lim = row_key_limit(a, total, L, row0 + l32);   // keys this lane's row sees
         const bool active = row0 < M;
         const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
 
@@ -1020,7 +1054,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         v8i pf;
         float psum = 0.f, qsum = 0.f, bias = 0.f;
         auto probs_begin = [&]() {
-            bias = kPScale - m_run;
+            bias = m_run == -INFINITY ? 0.f : kPScale - m_run;   // no key seen: P = 0
             psum = 0.f;
             qsum = 0.f;
         };
@@ -1096,8 +1130,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
             pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
             if (active) {
                 scores(slot, sc, no_valu);
-                const int valid = L - (first + t) * kPage;
-                if (valid < kPage) {
+                const int valid = lim - (first + t) * kPage;   // keys of the page the row sees
+                if (__any(valid < kPage)) {
 #pragma unroll
                     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1115,7 +1149,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 any_grow = __any(grow);
                 if (any_grow) {
                     const float m_new = grow ? mx : m_run;
-                    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    // rows whose max stays keep factor 1 (exp2(m - m) would be NaN for a
+                    // row that has seen no key yet, m = -inf)
+                    alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
                     l_run *= alpha;
                     lq_run *= alpha;
                     m_run = m_new;
@@ -1183,7 +1219,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
             const int row = jt * MT + 32 * (2 * pair + (own ? hw : 1 - hw)) + l32;
             if (row < M) {
                 float *po = partial + (slot_idx * M + row) * kVDim;
-                const float inv = a.out_scale / (own ? lq_tot : lq_other);
+                const float lq = own ? lq_tot : lq_other;
+                const float inv = lq > 0.f ? a.out_scale / lq : 0.f;   // no key: O = 0
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
                     const int dim = 32 * (8 * hw + n) + 4 * half;
@@ -1273,7 +1310,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
         const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
         const int rc = r >= 0 && r < R ? r : 0;
         const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r));
+        const int total = a.causal ? ldc(&a.totals[rc]) : L;
+        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
         const int pages = ceil_div(L, kPage);
         const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
         const int first = s * q + (s < rem ? s : rem);
@@ -1283,8 +1321,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
             if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
             continue;
         }
+        if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
+            atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
         const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
         const int row = jt * MT + l32;
+        const int lim = row_key_limit(a, total, L, row);   // keys this lane's row sees
 
         bool page_bad = false;
         auto page_at = [&](int32_t pid) {
@@ -1360,7 +1401,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
             const int t = t0 + pair;
             if (t >= size) continue;
             const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-            const int valid = L - (first + t) * kPage;
+            const int valid = lim - (first + t) * kPage;   // keys of the page the row sees
 
             // S^T[64 keys x 32 rows]: 18 MFMAs, K fragment reads two ahead
             v16f sc[2];
@@ -1387,7 +1428,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
                 }
             }
             // page max (masked), lazy running max and O rescale
-            if (valid < kPage) {
+            if (__any(valid < kPage)) {
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1403,7 +1444,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
             const bool grow = mx > m_run + kTau;
             if (__any(grow)) {
                 const float m_new = grow ? mx : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                // rows whose max stays keep factor 1 (exp2(m - m) would be NaN for a
+                // row that has seen no key yet, m = -inf)
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
                 l_run *= alpha;
                 lq_run *= alpha;
 #pragma unroll
@@ -1413,7 +1456,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
             // P = 2^(s*scale - m + kPScale): FP32 into the row sum, E4M3 into P^T
             v8i pf;
             {
-                const float bias = kPScale - m_run;
+                const float bias = m_run == -INFINITY ? 0.f : kPScale - m_run;   // no key seen: P = 0
                 float psum = 0.f, qsum = 0.f;
 #pragma unroll
                 for (int g = 0; g < 8; ++g) {
@@ -1578,7 +1621,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
         const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
         const int rc = r >= 0 && r < R ? r : 0;
         const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r));
+        const int total = a.causal ? ldc(&a.totals[rc]) : L;
+        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
         const int pages = ceil_div(L, kPage);
         const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
         const int first = s * q + (s < rem ? s : rem);
@@ -1588,7 +1632,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
             if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
             continue;
         }
+        if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
+            atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
         const int row0 = jt * MT + 32 * hw;     // this wave's score rows (block hw)
+        const int lim = row_key_limit(a, total, L, row0 + l32);   // keys this lane's row sees
         const bool active = row0 < M;
         const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
 
@@ -1695,8 +1742,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
                     sc[b] = mfma(cur, qf[k], sc[b]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const int valid = L - (first + t) * kPage;
-                if (valid < kPage) {
+                const int valid = lim - (first + t) * kPage;   // keys of the page the row sees
+                if (__any(valid < kPage)) {
 #pragma unroll
                     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1713,12 +1760,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
                 any_grow = __any(grow);
                 if (any_grow) {
                     const float m_new = grow ? mx : m_run;
-                    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    // rows whose max stays keep factor 1 (exp2(m - m) would be NaN for a
+                    // row that has seen no key yet, m = -inf)
+                    alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
                     l_run *= alpha;
                     lq_run *= alpha;
                     m_run = m_new;
                 }
-                const float bias = kPScale - m_run;
+                const float bias = m_run == -INFINITY ? 0.f : kPScale - m_run;   // no key seen: P = 0
                 float psum = 0.f, qsum = 0.f;
 #pragma unroll
                 for (int g = 0; g < 8; ++g) {
@@ -1914,11 +1963,12 @@ __device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int
     float wt[kLsePerLane], sum = 0.f;
 #pragma unroll
     for (int j = 0; j < kLsePerLane; ++j) {
-        wt[j] = lane + 64 * j < c ? __builtin_amdgcn_exp2f(ls[j] - mx) : 0.f;
+        // a row with no key in any split (possible under a causal mask) has mx = -inf
+        wt[j] = lane + 64 * j < c && mx != -INFINITY ? __builtin_amdgcn_exp2f(ls[j] - mx) : 0.f;
         sum += wt[j];
     }
     sum = wave_allf<false>(sum);
-    const float inv = 1.0f / sum;
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
 
     v4f acc[PER_LANE];
 #pragma unroll
@@ -2071,19 +2121,20 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
     for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float sum = 0.f;
     if (t32 < c) {
-        const float w = __builtin_amdgcn_exp2f(ls - mx);
+        // a row with no key in any split (possible under a causal mask) has mx = -inf
+        const float w = mx != -INFINITY ? __builtin_amdgcn_exp2f(ls - mx) : 0.f;
         wts[rho][t32] = w;
         sum = w;
     }
     for (int s = t32 + TPR; s < c; s += TPR) {
-        const float w = __builtin_amdgcn_exp2f(lrow_g[(int64_t)s * a.rows] - mx);
+        const float w = mx != -INFINITY ? __builtin_amdgcn_exp2f(lrow_g[(int64_t)s * a.rows] - mx) : 0.f;
         wts[rho][s] = w;
         sum += w;
     }
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
     __syncthreads();
-    const float inv = 1.0f / sum;
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
 
     v4f acc[NJ];
 #pragma unroll
@@ -2146,6 +2197,63 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
         const uint32_t hi = bf16_rne(d[2]) | ((uint32_t)bf16_rne(d[3]) << 16);
         *(uint2 *)(a.attn_out + gr * kUvDim + 16 * wave + 4 * (lane >> 4)) = make_uint2(lo, hi);
     }
+}
+
+// ------------------------------------------------------------ merge over DCP sources
+
+// Page "drafter.attention", DraftDcp (value stage): a head owner merges each row over the
+// DCP sources that computed it on their KV shards, with the combine math (exp2(lse_s - max)
+// weights over their sum in FP32, one BF16 rounding).  One wave per row: lane s holds
+// source s's LSE, and every lane merges 8 adjacent dims (16 bytes per source row), four
+// source rows in flight at a time.
+constexpr int kMaxSources = 64;
+
+__global__ __launch_bounds__(256) void merge_sources_kernel(const uint16_t *__restrict__ rows,
+                                                            const float *__restrict__ lse,
+                                                            int n_src, int64_t n_rows,
+                                                            uint16_t *__restrict__ out,
+                                                            float *__restrict__ out_lse)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= n_rows) return;   // whole waves
+    const float ls = lane < n_src ? lse[(int64_t)lane * n_rows + g] : -INFINITY;
+    const float mx = wave_allf<true>(ls);
+    const float w = lane < n_src && mx != -INFINITY ? __builtin_amdgcn_exp2f(ls - mx) : 0.f;
+    const float sum = wave_allf<false>(w);
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const uint16_t *src = rows + g * kVDim + 8 * lane;
+    for (int s0 = 0; s0 < n_src; s0 += 4) {
+        uint4 v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int sb = s0 + b < n_src ? s0 + b : n_src - 1;
+            v[b] = *(const uint4 *)(src + (int64_t)sb * n_rows * kVDim);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float ws =
+                s0 + b < n_src
+                    ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + b)) * inv
+                    : 0.f;
+            const uint32_t u[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += ws * __uint_as_float(u[e] << 16);
+                acc[2 * e + 1] += ws * __uint_as_float(u[e] & 0xFFFF0000u);
+            }
+        }
+    }
+    uint4 o;
+    o.x = bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
+    o.y = bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
+    o.z = bf16_rne(acc[4]) | ((uint32_t)bf16_rne(acc[5]) << 16);
+    o.w = bf16_rne(acc[6]) | ((uint32_t)bf16_rne(acc[7]) << 16);
+    *(uint4 *)(out + g * kVDim + 8 * lane) = o;
+    if (lane == 0) out_lse[g] = mx == -INFINITY ? -INFINITY : mx + __builtin_amdgcn_logf(sum);
 }
 
 // ----------------------------------------------------------------------- host helpers
@@ -2259,13 +2367,21 @@ int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 
-int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
-                       const int32_t *d_block_table, int32_t bt_stride, const int32_t *d_lengths,
-                       int32_t num_reqs, const amla_plan_params *params, float bmm1_scale,
-                       float bmm2_scale, const int32_t *d_counts, const int32_t *d_offsets,
-                       const int32_t *d_work, int32_t list_len, void *d_workspace,
-                       size_t ws_bytes, void *stream)
+static int decode_launch(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                         const int32_t *d_block_table, int32_t bt_stride,
+                         const int32_t *d_lengths, int32_t num_reqs,
+                         const amla_plan_params *params, float bmm1_scale, float bmm2_scale,
+                         const int32_t *d_counts, const int32_t *d_offsets,
+                         const int32_t *d_work, int32_t list_len, void *d_workspace,
+                         size_t ws_bytes, const amla_dcp_params *dcp, const int32_t *d_totals,
+                         void *stream)
 {
+    if (dcp && (dcp->heads < 1 || dcp->causal < 0 || dcp->causal > 1 || dcp->world < 1 ||
+                dcp->rank < 0 || dcp->rank >= dcp->world || dcp->interleave < 1 ||
+                (int64_t)dcp->interleave * dcp->world > (1 << 30) || !params ||
+                params->rows_per_req % dcp->heads != 0 ||
+                (dcp->causal && num_reqs > 0 && !d_totals)))
+        return AMLA_ERR_INVALID;
     if (!params_ok(params) || num_reqs < 0 || num_reqs > AMLA_MAX_REQS || pool_pages < 1 ||
         bt_stride < 1 || !d_kv || !d_offsets || !d_work || !d_workspace ||
         (num_reqs > 0 && (!d_q || !d_block_table || !d_lengths || !d_counts)) ||
@@ -2285,6 +2401,13 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
     a.list_len = list_len;
     a.score_scale = bmm1_scale * kLog2e;
     a.out_scale = bmm2_scale;
+    a.totals = d_totals;
+    a.causal = dcp ? dcp->causal : 0;
+    a.heads = dcp ? dcp->heads : 1;
+    a.k_tokens = dcp ? params->rows_per_req / dcp->heads : 1;
+    a.cp_world = dcp ? dcp->world : 1;
+    a.cp_rank = dcp ? dcp->rank : 0;
+    a.cp_interleave = dcp ? dcp->interleave : 1;
     int32_t *hdr = (int32_t *)d_workspace;
     float *part = (float *)((char *)d_workspace + lay.partial_off);
     float *lse = (float *)((char *)d_workspace + lay.lse_off);
@@ -2297,6 +2420,47 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
     default: hipLaunchKernelGGL(decode128_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
     }
 #undef AMLA_DECODE_ARGS
+    return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
+}
+
+int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                       const int32_t *d_block_table, int32_t bt_stride, const int32_t *d_lengths,
+                       int32_t num_reqs, const amla_plan_params *params, float bmm1_scale,
+                       float bmm2_scale, const int32_t *d_counts, const int32_t *d_offsets,
+                       const int32_t *d_work, int32_t list_len, void *d_workspace,
+                       size_t ws_bytes, void *stream)
+{
+    return decode_launch(d_q, d_kv, pool_pages, d_block_table, bt_stride, d_lengths, num_reqs,
+                         params, bmm1_scale, bmm2_scale, d_counts, d_offsets, d_work, list_len,
+                         d_workspace, ws_bytes, nullptr, nullptr, stream);
+}
+
+int amla_folded_decode_dcp(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                           const int32_t *d_block_table, int32_t bt_stride,
+                           const int32_t *d_lengths, int32_t num_reqs,
+                           const amla_plan_params *params, float bmm1_scale, float bmm2_scale,
+                           const int32_t *d_counts, const int32_t *d_offsets,
+                           const int32_t *d_work, int32_t list_len, void *d_workspace,
+                           size_t ws_bytes, const amla_dcp_params *dcp, const int32_t *d_totals,
+                           void *stream)
+{
+    if (!dcp) return AMLA_ERR_INVALID;
+    return decode_launch(d_q, d_kv, pool_pages, d_block_table, bt_stride, d_lengths, num_reqs,
+                         params, bmm1_scale, bmm2_scale, d_counts, d_offsets, d_work, list_len,
+                         d_workspace, ws_bytes, dcp, d_totals, stream);
+}
+
+int amla_merge_sources(int32_t n_src, const uint16_t *d_rows, const float *d_lse, int64_t n_rows,
+                       uint16_t *d_out, float *d_lse_out, void *stream)
+{
+    if (n_src < 1 || n_src > kMaxSources || n_rows < 0 ||
+        (n_rows > 0 && (!d_rows || !d_lse || !d_out || !d_lse_out)) ||
+        ((uintptr_t)d_rows & 15) || ((uintptr_t)d_out & 15) ||
+        n_rows > ((int64_t)1 << 40) / n_src)
+        return AMLA_ERR_INVALID;
+    if (n_rows == 0) return AMLA_OK;
+    hipLaunchKernelGGL(merge_sources_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0,
+                       (hipStream_t)stream, d_rows, d_lse, (int)n_src, n_rows, d_out, d_lse_out);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 

@@ -46,6 +46,8 @@ extern "C" {
 #define AMLA_MAX_REQS 4096    /* most requests one plan takes */
 #define AMLA_MAX_SPLITS 256   /* most splits per request */
 
+#define AMLA_MAX_SOURCES 64   /* most DCP sources amla_merge_sources takes */
+
 /* Host status codes. */
 #define AMLA_OK 0
 #define AMLA_ERR_INVALID (-1)   /* null pointer, size or parameter out of range */
@@ -176,6 +178,58 @@ int amla_folded_decode(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pag
                        const int32_t *d_counts, const int32_t *d_offsets,
                        const int32_t *d_work, int32_t list_len, void *d_workspace,
                        size_t ws_bytes, void *stream);
+
+/*
+ * Decode context parallelism (page "...cutedsl.mla.balanced", module docstring and
+ * BalancedMla.decode: under DCP the decode reads this rank's KV shard, masks causally in
+ * global positions from the requests' global lengths, and returns the log2 LSE the head
+ * owner merges; page "drafter.attention", DraftDcp).  A rank holds the global positions p
+ * with (p / interleave) % world == rank, in global order: local position
+ * (p / (interleave * world)) * interleave + p % interleave.
+ *   heads       H: folded row i = t*H + h is draft token t = i / H (rows_per_req % H == 0)
+ *   causal      0: every row sees the rank's whole shard (the draft block is non-causal);
+ *               1: token t of a request of `total` global keys sits at position
+ *               total - k + t (k = rows_per_req / H) and sees the positions up to it
+ *   world, rank, interleave: the shard, 0 <= rank < world, interleave >= 1,
+ *               interleave * world <= 2^30
+ */
+typedef struct amla_dcp_params {
+    int32_t heads;
+    int32_t causal;
+    int32_t world;
+    int32_t rank;
+    int32_t interleave;
+} amla_dcp_params;
+
+/*
+ * amla_folded_decode over one rank's KV shard: d_lengths are the local lengths (keys of
+ * the shard, what the plan was made from), d_block_table the shard's pages, d_totals int32
+ * [num_reqs] the global lengths (needed when causal; may be NULL otherwise).  A row that
+ * sees none of a split's keys gets partial 0 and LSE -inf.  The device status word gets
+ * AMLA_DEV_BAD_LENGTH when a local length is not the shard's share of its total.
+ * AMLA_ERR_INVALID for a NULL dcp, out-of-range fields, or causal without d_totals; the
+ * other arguments and errors are those of amla_folded_decode.
+ */
+int amla_folded_decode_dcp(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                           const int32_t *d_block_table, int32_t bt_stride,
+                           const int32_t *d_lengths, int32_t num_reqs,
+                           const amla_plan_params *params, float bmm1_scale, float bmm2_scale,
+                           const int32_t *d_counts, const int32_t *d_offsets,
+                           const int32_t *d_work, int32_t list_len, void *d_workspace,
+                           size_t ws_bytes, const amla_dcp_params *dcp, const int32_t *d_totals,
+                           void *stream);
+
+/*
+ * Merge over DCP sources (page "drafter.attention", DraftDcp: the head owner merges each
+ * row over the sources, exp2(lse_s - max) weights over their sum in FP32, one BF16
+ * rounding):
+ *   d_rows     BF16 [n_src][n_rows][512], 16-byte aligned: each source's merged rows
+ *   d_lse      FP32 log2 [n_src][n_rows]; -inf marks a row a source has no key for
+ *   d_out      BF16 [n_rows][512], 16-byte aligned;  d_lse_out FP32 [n_rows]
+ * Rows every source leaves empty get 0 and -inf.  1 <= n_src <= 64.
+ */
+int amla_merge_sources(int32_t n_src, const uint16_t *d_rows, const float *d_lse, int64_t n_rows,
+                       uint16_t *d_out, float *d_lse_out, void *stream);
 
 /*
  * Reducer: merges each row's split partials (page "drafter.attention", DraftDcp: exp2

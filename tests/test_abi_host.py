@@ -43,6 +43,7 @@ def test_header_constants_match_binding():
     assert int(consts["AMLA_PAGE"]) == b.PAGE and int(consts["AMLA_KDIM"]) == b.KDIM
     assert int(consts["AMLA_VDIM"]) == b.VDIM and int(consts["AMLA_MAX_ROWS"]) == b.MAX_ROWS
     assert int(consts["AMLA_UVDIM"]) == b.UVDIM
+    assert int(consts["AMLA_MAX_SOURCES"]) == b.MAX_SOURCES
     assert int(consts["AMLA_MAX_REQS"]) == b.MAX_REQS
     assert int(consts["AMLA_ERR_WORKSPACE"]) == b.ERR_WORKSPACE
     assert int(consts["AMLA_DEV_BAD_PAGE"]) == b.DEV_BAD_PAGE
@@ -187,6 +188,36 @@ def test_combine_uv_argument_errors():
     assert uv(ws_bytes=10) == b.ERR_WORKSPACE
     assert uv(reqs=0) == b.OK              # nothing to do, nothing launched
     assert uv(reqs=0, heads=32) == b.OK
+
+
+def test_dcp_argument_errors():
+    lib = b.load()
+    p = b.make_params(32, 32, 256)
+    vp = ctypes.c_void_p
+
+    def dec(dcp, totals=256, reqs=2, params=p):
+        return lib.amla_folded_decode_dcp(vp(256), vp(256), 16, vp(256), 4, vp(256), reqs,
+                                          ctypes.byref(params), 1.0, 1.0, vp(256), vp(256),
+                                          vp(256), 1024, vp(256), 1 << 30,
+                                          ctypes.byref(dcp) if dcp is not None else None,
+                                          vp(totals), None)
+
+    ok = dict(heads=8, causal=1, world=2, rank=1, interleave=64)
+    for bad in (dict(heads=0), dict(heads=3), dict(world=0), dict(rank=2), dict(rank=-1),
+                dict(interleave=0), dict(causal=2), dict(world=1 << 16, interleave=1 << 15)):
+        assert dec(b.DcpParams(**dict(ok, **bad))) == b.ERR_INVALID, bad
+    assert dec(None) == b.ERR_INVALID
+    assert dec(b.DcpParams(**ok), totals=0) == b.ERR_INVALID          # causal needs totals
+    assert dec(b.DcpParams(**ok), reqs=0) == b.OK
+    assert dec(b.DcpParams(**dict(ok, causal=0)), totals=0, reqs=0) == b.OK
+
+    def merge(n_src=2, rows=256, lse=256, n=4, out=256, lo=256):
+        return lib.amla_merge_sources(n_src, vp(rows), vp(lse), n, vp(out), vp(lo), None)
+
+    for bad in (dict(n_src=0), dict(n_src=b.MAX_SOURCES + 1), dict(rows=0), dict(lse=0),
+                dict(out=0), dict(lo=0), dict(rows=264), dict(out=248), dict(n=-1)):
+        assert merge(**bad) == b.ERR_INVALID, bad
+    assert merge(n=0) == b.OK
 
 
 def test_status_strings():
