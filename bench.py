@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--uv", action="store_true",
                     help="end each step with the merge fused with the W_UV up-projection "
                          "(attention output [R*k, H*128]) instead of the plain merge")
+    ap.add_argument("--dcp", type=int, default=0,
+                    help="decode the workload as rank 0's KV shard of this many interleaved "
+                         "DCP ranks (interleave 1) with the causal mask in global positions, "
+                         "and time the merge of as many source rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="target CPU time of the oracle sample")
@@ -163,6 +167,22 @@ def main():
     H = w.M // w.cfg.k if not args.unfolded else w.M
     w_uv = torch.from_numpy(wl.uv_weights(H).view(np.int16)).to(dev)
     attn_out = torch.empty((R * (M // H), H * 128), dtype=torch.bfloat16, device=dev)
+    k_tok = M // H
+    dcp = None
+    if args.dcp > 1:
+        # the lengths are rank 0's shard of global lengths N * L (interleave 1: rank 0
+        # holds positions 0, N, 2N, ...: ceil(N L / N) = L of them)
+        dcp = binding.DcpParams(H, 1, args.dcp, 0, 1)
+        totals = torch.from_numpy(w.lengths.astype(np.int64) * args.dcp).to(torch.int32).to(dev)
+
+    def decode(pool, stream):
+        if dcp is None:
+            binding.folded_decode(q, pool, bt, lengths, dec.params, bmm1, bmm2, dec.counts[:R],
+                                  dec.offsets[:R + 1], dec.work, dec.workspace, stream)
+        else:
+            binding.folded_decode_dcp(q, pool, bt, lengths, dec.params, bmm1, bmm2,
+                                      dec.counts[:R], dec.offsets[:R + 1], dec.work,
+                                      dec.workspace, dcp, totals, stream)
 
     def merge(stream):
         if args.uv:
@@ -175,8 +195,7 @@ def main():
     def step(i):
         stream = torch.cuda.current_stream()
         dec.plan(lengths, bt.shape[1], stream)
-        binding.folded_decode(q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2,
-                              dec.counts[:R], dec.offsets[:R + 1], dec.work, dec.workspace, stream)
+        decode(pools[i % len(pools)], stream)
         merge(stream)
 
     for i in range(args.warmup):
@@ -255,9 +274,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps
 
-    dec_avg = timed(lambda i: binding.folded_decode(
-        q, pools[i % len(pools)], bt, lengths, dec.params, bmm1, bmm2, dec.counts[:R],
-        dec.offsets[:R + 1], dec.work, dec.workspace, stream))
+    dec_avg = timed(lambda i: decode(pools[i % len(pools)], stream))
     comb_avg = timed(lambda i: binding.combine(
         dec.workspace, dec.counts[:R], dec.offsets[:R + 1], R, dec.params, dec.compute_units,
         out, lse, stream))
@@ -279,9 +296,7 @@ def main():
         def layered(s):
             dec.plan(lengths, bt.shape[1], s)
             for li in range(args.layers):
-                binding.folded_decode(q, pools[li % len(pools)], bt, lengths, dec.params, bmm1,
-                                      bmm2, dec.counts[:R], dec.offsets[:R + 1], dec.work,
-                                      dec.workspace, s)
+                decode(pools[li % len(pools)], s)
                 merge(s)
         gl = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -342,9 +357,25 @@ def main():
                    "flop": 2 * R * M * 512 * 128,
                    "in_step": bool(args.uv)}
 
+    # the head owner's merge over the DCP sources: N BF16 source rows per folded row
+    dcp_res = None
+    if dcp is not None:
+        n = R * M
+        src_rows = torch.randn((args.dcp, n, 512), device=dev).to(torch.bfloat16)
+        src_lse = torch.randn((args.dcp, n), device=dev)
+        m_out = torch.empty((n, 512), dtype=torch.bfloat16, device=dev)
+        m_lse = torch.empty((n,), dtype=torch.float32, device=dev)
+        m_avg = timed(lambda i: binding.merge_sources(src_rows, src_lse, m_out, m_lse, stream))
+        m_bytes = args.dcp * n * (512 * 2 + 4) + n * (512 * 2 + 4)
+        dcp_res = {"world": args.dcp, "interleave": 1, "rank": 0, "causal": True,
+                   "merge_kernel": "merge_sources_kernel", "merge_us": round(m_avg * 1e3, 2),
+                   "merge_bytes": int(m_bytes),
+                   "merge_gbs": round(m_bytes / (m_avg / 1e3) / 1e9, 1)}
+
     cfg = w.cfg
     workload = (f"{args.config}: R={cfg.R} k={cfg.k} H={cfg.H} (M={cfg.M}), {cfg.description}"
-                + (" [unfolded R*k rows]" if args.unfolded else ""))
+                + (" [unfolded R*k rows]" if args.unfolded else "")
+                + (f" [rank 0 of {args.dcp} DCP ranks, causal]" if args.dcp > 1 else ""))
     res = {
         "metric": "KV-cache HBM GB/s and folded query rows/s (R*k*H per s) per MI355X",
         "value": round(value, 2),
@@ -369,6 +400,7 @@ def main():
         "decode_us": round(dec_avg * 1e3, 2),
         "combine_us": round(comb_avg * 1e3, 2),
         "value_stage": value_stage,
+        "dcp": dcp_res,
         "plan_us": round(plan_us, 2),
         "layer_kv_gbs": round(kv_bytes / ((dec_avg + (uv_avg if args.uv else comb_avg)) / 1e3) / 1e9, 1),
         "layered_step": amortized,
