@@ -227,3 +227,45 @@ def dcp_shards(w: Workload, world: int, interleave: int, seed: int = 0) -> list[
             kv[bt[r, j // PAGE], j % PAGE] = src
         out.append(Workload(w.cfg, lengths, bt, w.q8, kv, w.q_scale, w.k_scale, w.sm_scale))
     return out
+
+
+@dataclasses.dataclass
+class QueryBuildInputs:
+    q: np.ndarray            # BF16 bits [n, H, 192]: q_nope (128) then q_pe (64) per head
+    w_uk: np.ndarray         # BF16 bits [H, 512, 128]: W_UK_T [H, 128, 512] stored c-contiguous
+    kv_c: np.ndarray         # BF16 bits [n, 512]: the normalised latent of each new token
+    k_pe: np.ndarray         # BF16 bits [n, 64]: its rope key, before the rotation
+    positions: np.ndarray    # int64 [n]
+    cos_sin: np.ndarray      # float32 [max_pos, 64]: cos of 32 angles, then their sin
+    neox: bool
+    q_scale: float
+    k_scale: float
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def query_build_inputs(n: int, H: int, seed: int = 0, max_pos: int = 1 << 17,
+                       neox: bool = False) -> QueryBuildInputs:
+    """Synthetic inputs of the step before the decode: the projected query of n new tokens
+    and H heads, W_UK_T, the tokens' latent and rope key, their positions and a rotary
+    table (angle i of position p: p * 10000^(-i/32)).  Scales are per tensor, amax / 448 of
+    values bounded by construction (|ql_nope| <= sum |q_nope| |W|, |rope| <= |x| sqrt 2)."""
+    rng = np.random.default_rng([seed, 3])
+    q = _bf16_bits(rng.standard_normal((n, H, 192), dtype=np.float32))
+    w = _bf16_bits(rng.standard_normal((H, VDIM, 128), dtype=np.float32) / np.float32(math.sqrt(128)))
+    kv_c = _bf16_bits(rng.standard_normal((n, VDIM), dtype=np.float32))
+    k_pe = _bf16_bits(rng.standard_normal((n, 64), dtype=np.float32))
+    positions = rng.integers(0, max_pos, n).astype(np.int64)
+    inv = 10000.0 ** (-np.arange(32) / 32.0)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    cos_sin = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    # scales from a bound of the largest value (the query: 6 sigma of a 128-term dot product
+    # with unit-variance terms; the cache: the drawn amax, times sqrt 2 for the rotation)
+    q_scale = 6.0 * 1.05 / E4M3_MAX
+    kvf = torch.from_numpy(kv_c.view(np.int16)).view(torch.bfloat16).float().abs().max().item()
+    kpf = torch.from_numpy(k_pe.view(np.int16)).view(torch.bfloat16).float().abs().max().item()
+    k_scale = max(kvf, kpf * math.sqrt(2.0)) / E4M3_MAX
+    return QueryBuildInputs(q, w, kv_c, k_pe, positions, cos_sin, neox, q_scale, k_scale)

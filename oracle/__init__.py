@@ -321,3 +321,73 @@ def merge_sources(outs, lses):
             continue
         out[j], lse[j] = merge(outs[:, j], lses[:, j])
     return out, lse
+
+
+# ------------------------------------------------ query build and cache write
+
+def e4m3_encode(y) -> np.ndarray:
+    """E4M3FN codes of real values y, rounded to nearest with ties to the even code and
+    saturated at +-448 (the cast convention of the inputs: clip, then cast); NaN -> 0x7F.
+    Written from the format's definition: the nearest of the decoded code values."""
+    y = np.asarray(y, dtype=np.float64)
+    table = e4m3_table()
+    pos = np.arange(0, 0x7F)                  # codes 0x00 .. 0x7E: 0 .. 448, increasing
+    vals = table[pos]
+    a = np.minimum(np.abs(y), 448.0)
+    j = np.clip(np.searchsorted(vals, a), 1, len(vals) - 1)
+    lo, hi = vals[j - 1], vals[j]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & ((pos[j - 1] & 1) == 1))
+    code = np.where(pick_hi, pos[j], pos[j - 1]).astype(np.uint8)
+    code = np.where(a == 0, 0, code).astype(np.uint8)
+    code = np.where(np.signbit(y), code | 0x80, code)      # negative values keep the sign,
+    return np.where(np.isnan(y), 0x7F, code).astype(np.uint8)   # zero included
+
+
+def rope(x, cos, sin, neox: bool):
+    """Rotary embedding of the last axis (64 dims) with per-row cos/sin [.., 32].
+    Non-NeoX: pairs (2i, 2i+1) turn by angle i; NeoX: pairs (i, i + 32)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    if neox:
+        a, b = x[..., :32], x[..., 32:]
+        out[..., :32] = a * cos - b * sin
+        out[..., 32:] = b * cos + a * sin
+    else:
+        a, b = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2] = a * cos - b * sin
+        out[..., 1::2] = b * cos + a * sin
+    return out
+
+
+def build_query_and_cache(q_bits, w_uk_bits, kv_c_bits, k_pe_bits, positions, cos_sin, neox):
+    """Exact (FP64) values of the absorbed decode query and of the cache rows, before the
+    FP8 cast.  Page "drafter.attention", DraftDcp._forward: q [n, H, 192] splits into
+    q_nope (128) and q_pe (64); ql_nope = q_nope times W_UK_T per head ([H, 128, 512],
+    given here stored [H][512][128]); the query row is ql_nope ++ rope(q_pe) (576) and the
+    cache row kv_c_normed ++ rope(k_pe) (576), at each token's position (cos/sin from the
+    table row of that position: 32 cos then 32 sin).  Returns (query [n, H, 576], cache
+    rows [n, 576])."""
+    q = bf16_values(q_bits)                                   # [n, H, 192]
+    n, H = q.shape[0], q.shape[1]
+    w = bf16_values(w_uk_bits).reshape(H, VDIM, 128)          # [h][l][c]
+    kvc = bf16_values(kv_c_bits).reshape(n, VDIM)
+    kpe = bf16_values(k_pe_bits).reshape(n, 64)
+    cs = np.asarray(cos_sin, dtype=np.float64)[np.asarray(positions)]   # [n, 64]
+    cos, sin = cs[:, :32], cs[:, 32:]
+    query = np.empty((n, H, KDIM))
+    for h in range(H):
+        query[:, h, :VDIM] = q[:, h, :128] @ w[h].T
+    query[:, :, VDIM:] = rope(q[:, :, 128:], cos[:, None, :], sin[:, None, :], neox)
+    rows = np.empty((n, KDIM))
+    rows[:, :VDIM] = kvc
+    rows[:, VDIM:] = rope(kpe, cos, sin, neox)
+    return query, rows
+
+
+def e4m3_valid_codes(y, rel: float):
+    """The E4M3 codes a cast of any value within a relative distance `rel` of y may give:
+    (low, high) codes of the interval's ends (the cast is monotone)."""
+    y = np.asarray(y, dtype=np.float64)
+    lo = e4m3_encode(y - np.abs(y) * rel)
+    hi = e4m3_encode(y + np.abs(y) * rel)
+    return lo, hi
