@@ -30,6 +30,7 @@ ERR_HIP = -4
 DEV_BAD_LENGTH = 1
 DEV_BAD_PAGE = 2
 DEV_BAD_ITEM = 4
+DEV_BAD_POSITION = 8
 
 PLAN_BALANCED = 0
 PLAN_FIXED = 1
@@ -37,7 +38,8 @@ PLAN_FIXED = 1
 EXPORTS = (
     "amla_fold_plan", "amla_bmm_scales", "amla_decode_config", "amla_reducer_bands",
     "amla_workspace_bytes", "amla_plan_splits", "amla_folded_decode", "amla_combine",
-    "amla_combine_uv", "amla_folded_decode_dcp", "amla_merge_sources", "amla_status_string",
+    "amla_combine_uv", "amla_folded_decode_dcp", "amla_merge_sources", "amla_build_query_cache",
+    "amla_status_string",
 )
 MAX_SOURCES = 64
 
@@ -106,6 +108,8 @@ def load() -> ctypes.CDLL:
                                                   vp, vp, vp, i32, vp, sz,
                                                   ctypes.POINTER(DcpParams), vp, vp]),
         "amla_merge_sources": (ctypes.c_int, [i32, vp, vp, i64, vp, vp, vp]),
+        "amla_build_query_cache": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                                  f32, f32, vp, vp, i64, vp, vp]),
         "amla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -222,6 +226,17 @@ def merge_sources(rows, lse, out, lse_out, stream=None):
     n_rows = rows[0].numel() // VDIM if n_src else 0
     _check("amla_merge_sources", load().amla_merge_sources(
         n_src, _ptr(rows), _ptr(lse), n_rows, _ptr(out), _ptr(lse_out), _stream(stream)))
+
+
+def build_query_cache(q, w_uk, kv_c, k_pe, positions, cos_sin, slot_mapping, neox, q_scale,
+                      k_scale, q_out, kv_cache, status=None, stream=None):
+    """The absorbed decode query q_out [n, H, 576] (E4M3) and the new tokens' cache rows,
+    written into kv_cache [pages, 64, 576] at slot_mapping (see amla.h)."""
+    n, H = q.shape[0], q.shape[1]
+    _check("amla_build_query_cache", load().amla_build_query_cache(
+        _ptr(q), _ptr(w_uk), _ptr(kv_c), _ptr(k_pe), _ptr(positions), _ptr(cos_sin),
+        cos_sin.shape[0], _ptr(slot_mapping), n, H, int(bool(neox)), q_scale, k_scale,
+        _ptr(q_out), _ptr(kv_cache), kv_cache.shape[0], _ptr(status), _stream(stream)))
 
 
 def combine_uv(workspace, counts, offsets, num_reqs, params: PlanParams, heads, w_uv, attn_out,

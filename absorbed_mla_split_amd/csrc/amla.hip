@@ -2256,6 +2256,158 @@ __global__ __launch_bounds__(256) void merge_sources_kernel(const uint16_t *__re
     if (lane == 0) out_lse[g] = mx == -INFINITY ? -INFINITY : mx + __builtin_amdgcn_logf(sum);
 }
 
+// --------------------------------------------- absorbed query build and cache write
+
+// Page "drafter.attention", DraftDcp._forward (the step before the decode): per head,
+// ql_nope = q_nope W_UK_T ([H, 128, 512]; BF16 MMA, FP32 accumulation), the query row is
+// ql_nope ++ rope(q_pe) and each new token's cache row is kv_c ++ rope(k_pe), both cast to
+// E4M3 with their per-tensor scales; the cache row goes to its slot (page slot / 64, row
+// slot % 64), the query row to [n, H, 576].  Every value passes through BF16 (the model
+// dtype) before the cast.  W_UK_T arrives stored [H][512][128] (the 128 nope weights of a
+// latent dim adjacent), so MFMA operand fragments are 16 adjacent bytes.
+// One launch, two roles: blocks [0, query_blocks) build the query of (16 tokens, head h);
+// the others write the cache rows of 4 tokens (one wave each).
+constexpr int kQbTokens = 16;
+
+struct BuildArgs {
+    const uint16_t *q;          // [n][H][192]
+    const uint16_t *w_uk;       // [H][512][128]
+    const uint16_t *kv_c;       // [n][512]
+    const uint16_t *k_pe;       // [n][64]
+    const int64_t *positions;   // [n]
+    const float *cos_sin;       // [max_pos][64]
+    const int64_t *slots;       // [n]
+    uint8_t *q_out;             // [n][H][576]
+    uint8_t *cache;             // [pool_pages][64][576]
+    int32_t *status;            // device status word or null
+    int64_t pool_pages;
+    int32_t n, heads, neox, max_pos, query_blocks;
+    float q_inv, k_inv;         // 1 / scale
+};
+
+__device__ __forceinline__ float bf16_round(float x) { return __uint_as_float((uint32_t)bf16_rne(x) << 16); }
+
+// four values -> four E4M3 bytes (x * inv_scale, saturated at +-448, nearest even)
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float inv)
+{
+    auto sat = [&](float v) { return fminf(fmaxf(v * inv, -448.f), 448.f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+    return (uint32_t)w;
+}
+
+// rotary pair i of a 64-dim rope vector: its two dims
+__device__ __forceinline__ void rope_dims(int i, bool neox, int &d0, int &d1)
+{
+    d0 = neox ? i : 2 * i;
+    d1 = neox ? i + 32 : 2 * i + 1;
+}
+
+__global__ __launch_bounds__(256) void build_query_cache_kernel(BuildArgs a)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool neox = a.neox != 0;
+    auto bf = [](uint16_t u) { return __uint_as_float((uint32_t)u << 16); };
+    auto cos_sin_row = [&](int64_t tok) {
+        int64_t p = a.positions[tok];
+        if (p < 0 || p >= a.max_pos) {
+            if (a.status) atomicOr(a.status, AMLA_DEV_BAD_POSITION);
+            p = 0;
+        }
+        return a.cos_sin + p * 64;
+    };
+
+    if ((int)blockIdx.x < a.query_blocks) {
+        const int h = blockIdx.x % a.heads;
+        const int t0 = (blockIdx.x / a.heads) * kQbTokens;
+        // B operand (q_nope^T): lane l holds q_nope[token t0 + l%16][c = 32 ks + 8 (l/16) ..+7]
+        const int tok = t0 + (lane & 15);
+        bf16x8 qb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (tok < a.n)
+                qb[ks] = *(const bf16x8 *)(a.q + ((int64_t)tok * a.heads + h) * 192 + 32 * ks + 8 * (lane >> 4));
+            else
+                qb[ks] = bf16x8{};
+        }
+        // A operand (W_UK): lane l holds W[h][l = 128 wave + 16 mt + l%16][c = 32 ks + 8 (l/16) ..]
+        const uint16_t *wh = a.w_uk + ((int64_t)h * kVDim + 128 * wave + (lane & 15)) * 128 + 8 * (lane >> 4);
+        v4f d[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            d[mt] = v4f{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 wa = *(const bf16x8 *)(wh + 16 * 128 * mt + 32 * ks);
+                d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, qb[ks], d[mt], 0, 0, 0);
+            }
+        }
+        // lane l holds ql[token t0 + l%16][latent 128 wave + 16 mt + 4 (l/16) + e]
+        if (tok < a.n) {
+            uint8_t *qo = a.q_out + ((int64_t)tok * a.heads + h) * kKDim + 128 * wave + 4 * (lane >> 4);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                *(uint32_t *)(qo + 16 * mt) =
+                    e4m3x4(bf16_round(d[mt][0]), bf16_round(d[mt][1]), bf16_round(d[mt][2]),
+                           bf16_round(d[mt][3]), a.q_inv);
+        }
+        // rope(q_pe): thread (token t0 + tid/16, pairs 2 (tid%16) and 2 (tid%16) + 1)
+        const int rt = t0 + (tid >> 4);
+        if (rt < a.n) {
+            const float *cs = cos_sin_row(rt);
+            const uint16_t *pe = a.q + ((int64_t)rt * a.heads + h) * 192 + 128;
+            uint8_t *qo = a.q_out + ((int64_t)rt * a.heads + h) * kKDim + kVDim;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int i = 2 * (tid & 15) + u;
+                int d0, d1;
+                rope_dims(i, neox, d0, d1);
+                const float x0 = bf(pe[d0]), x1 = bf(pe[d1]), c = cs[i], sn = cs[32 + i];
+                const float y0 = bf16_round(x0 * c - x1 * sn), y1 = bf16_round(x1 * c + x0 * sn);
+                const uint32_t w = e4m3x4(y0, y1, 0.f, 0.f, a.q_inv);
+                qo[d0] = (uint8_t)(w & 0xFF);
+                qo[d1] = (uint8_t)((w >> 8) & 0xFF);
+            }
+        }
+        return;
+    }
+
+    // cache rows: one wave per token
+    const int64_t tok = ((int64_t)blockIdx.x - a.query_blocks) * 4 + wave;
+    if (tok >= a.n) return;
+    const int64_t slot = a.slots[tok];
+    if (slot < 0) return;                       // a padding token: no cache row
+    const int64_t page = slot >> 6;
+    if (page >= a.pool_pages) {
+        if (lane == 0 && a.status) atomicOr(a.status, AMLA_DEV_BAD_PAGE);
+        return;
+    }
+    uint8_t *dst = a.cache + slot * kKDim;      // page * 64 + row, rows of 576 bytes
+    {
+        const uint4 v = *(const uint4 *)(a.kv_c + tok * kVDim + 8 * lane);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = __uint_as_float(u[e] << 16);
+            f[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+        }
+        *(uint2 *)(dst + 8 * lane) = make_uint2(e4m3x4(f[0], f[1], f[2], f[3], a.k_inv),
+                                                e4m3x4(f[4], f[5], f[6], f[7], a.k_inv));
+    }
+    if (lane < 32) {
+        const float *cs = cos_sin_row(tok);
+        int d0, d1;
+        rope_dims(lane, neox, d0, d1);
+        const uint16_t *pe = a.k_pe + tok * 64;
+        const float x0 = bf(pe[d0]), x1 = bf(pe[d1]), c = cs[lane], sn = cs[32 + lane];
+        const float y0 = bf16_round(x0 * c - x1 * sn), y1 = bf16_round(x1 * c + x0 * sn);
+        const uint32_t w = e4m3x4(y0, y1, 0.f, 0.f, a.k_inv);
+        dst[kVDim + d0] = (uint8_t)(w & 0xFF);
+        dst[kVDim + d1] = (uint8_t)((w >> 8) & 0xFF);
+    }
+}
+
 // ----------------------------------------------------------------------- host helpers
 
 bool params_ok(const amla_plan_params *p)
@@ -2464,6 +2616,50 @@ int amla_merge_sources(int32_t n_src, const uint16_t *d_rows, const float *d_lse
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 
+int amla_build_query_cache(const uint16_t *d_q, const uint16_t *d_w_uk, const uint16_t *d_kv_c,
+                           const uint16_t *d_k_pe, const int64_t *d_positions,
+                           const float *d_cos_sin, int32_t max_pos,
+                           const int64_t *d_slot_mapping, int32_t n_tokens, int32_t heads,
+                           int32_t neox, float q_scale, float k_scale, uint8_t *d_q_out,
+                           uint8_t *d_kv_cache, int64_t pool_pages, int32_t *d_status,
+                           void *stream)
+{
+    if (n_tokens < 0 || heads < 1 || heads > 1024 || max_pos < 1 || pool_pages < 0 ||
+        (neox != 0 && neox != 1) || !std::isfinite(q_scale) || !(q_scale > 0.f) ||
+        !std::isfinite(k_scale) || !(k_scale > 0.f) ||
+        (n_tokens > 0 && (!d_q || !d_w_uk || !d_kv_c || !d_k_pe || !d_positions || !d_cos_sin ||
+                          !d_slot_mapping || !d_q_out || !d_kv_cache)) ||
+        ((uintptr_t)d_q & 15) || ((uintptr_t)d_w_uk & 15) || ((uintptr_t)d_kv_c & 15) ||
+        ((uintptr_t)d_q_out & 3) || ((uintptr_t)d_kv_cache & 7))
+        return AMLA_ERR_INVALID;
+    if (n_tokens == 0) return AMLA_OK;
+    BuildArgs a;
+    a.q = d_q;
+    a.w_uk = d_w_uk;
+    a.kv_c = d_kv_c;
+    a.k_pe = d_k_pe;
+    a.positions = d_positions;
+    a.cos_sin = d_cos_sin;
+    a.slots = d_slot_mapping;
+    a.q_out = d_q_out;
+    a.cache = d_kv_cache;
+    a.status = d_status;
+    a.pool_pages = pool_pages;
+    a.n = n_tokens;
+    a.heads = heads;
+    a.neox = neox;
+    a.max_pos = max_pos;
+    a.q_inv = 1.0f / q_scale;
+    a.k_inv = 1.0f / k_scale;
+    const int64_t qblocks = (int64_t)((n_tokens + kQbTokens - 1) / kQbTokens) * heads;
+    const int64_t cblocks = (n_tokens + 3) / 4;
+    if (qblocks + cblocks > 0x7FFFFFFF) return AMLA_ERR_INVALID;
+    a.query_blocks = (int32_t)qblocks;
+    hipLaunchKernelGGL(build_query_cache_kernel, dim3((unsigned)(qblocks + cblocks)), dim3(256), 0,
+                       (hipStream_t)stream, a);
+    return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
+}
+
 int amla_combine(const void *d_workspace, size_t ws_bytes, const int32_t *d_counts,
                  const int32_t *d_offsets, int32_t num_reqs, const amla_plan_params *params,
                  int32_t compute_units, uint16_t *d_out, float *d_lse, void *stream)
@@ -2548,6 +2744,7 @@ const char *amla_status_string(int status)
         if (status & AMLA_DEV_BAD_LENGTH) return "device: bad length (plan is empty)";
         if (status & AMLA_DEV_BAD_PAGE) return "device: block-table entry out of range";
         if (status & AMLA_DEV_BAD_ITEM) return "device: work item or plan does not match";
+        if (status & AMLA_DEV_BAD_POSITION) return "device: position outside the rotary table";
     }
     return "unknown status";
 }

@@ -61,6 +61,8 @@ extern "C" {
                                    the plan is then empty (every count 0) */
 #define AMLA_DEV_BAD_PAGE 2     /* decode: a block-table entry outside [0, pool_pages) */
 #define AMLA_DEV_BAD_ITEM 4     /* decode: a work item or plan that does not match the call */
+#define AMLA_DEV_BAD_POSITION 8 /* query build: a position outside the rotary table (row 0
+                                   used instead) */
 
 /* Split-plan modes (page "...cutedsl.mla.balanced", module docstring). */
 #define AMLA_PLAN_BALANCED 0    /* split counts planned from the lengths */
@@ -262,6 +264,37 @@ int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_c
                     const int32_t *d_offsets, int32_t num_reqs, const amla_plan_params *params,
                     int32_t heads, const uint16_t *d_w_uv, uint16_t *d_attn_out,
                     uint16_t *d_out, float *d_lse, void *stream);
+
+/*
+ * The step before the decode (page "drafter.attention", DraftDcp._forward): the absorbed
+ * decode query and the new tokens' cache rows, in one launch.
+ *   d_q          BF16 [n][H][192]: per head q_nope (128) then q_pe (64); 16-byte aligned
+ *   d_w_uk       BF16 W_UK_T [H][128][512] stored [H][512][128] (element (h, l, c) =
+ *                W_UK_T[h][c][l]: the 128 nope weights of a latent dim adjacent);
+ *                16-byte aligned
+ *   d_kv_c       BF16 [n][512]: each token's normalised latent; 16-byte aligned
+ *   d_k_pe       BF16 [n][64]: its rope key before the rotation
+ *   d_positions  int64 [n]: rotary positions, in [0, max_pos)
+ *   d_cos_sin    FP32 [max_pos][64]: cos of the 32 angles of a position, then their sin
+ *   d_slot_mapping int64 [n]: cache slot of each token (page = slot / 64, row = slot % 64);
+ *                negative: no cache row (padding)
+ *   neox         0: rotary pairs (2i, 2i+1); 1: pairs (i, i + 32)
+ *   q_scale, k_scale  per-tensor FP8 scales (code = E4M3(x / scale), saturated at 448)
+ *   d_q_out      E4M3 [n][H][576]: ql_nope = q_nope W_UK_T (512) then rope(q_pe) (64);
+ *                4-byte aligned
+ *   d_kv_cache   E4M3 [pool_pages][64][576]: rows kv_c (512) then rope(k_pe) (64) are
+ *                written at the tokens' slots, nothing else; 8-byte aligned
+ *   d_status     int32 status word or NULL: AMLA_DEV_BAD_PAGE for a slot past the pool (row
+ *                skipped), AMLA_DEV_BAD_POSITION for a position outside the table
+ * Every value is rounded to BF16 before the cast (ql_nope after its FP32 accumulation).
+ */
+int amla_build_query_cache(const uint16_t *d_q, const uint16_t *d_w_uk, const uint16_t *d_kv_c,
+                           const uint16_t *d_k_pe, const int64_t *d_positions,
+                           const float *d_cos_sin, int32_t max_pos,
+                           const int64_t *d_slot_mapping, int32_t n_tokens, int32_t heads,
+                           int32_t neox, float q_scale, float k_scale, uint8_t *d_q_out,
+                           uint8_t *d_kv_cache, int64_t pool_pages, int32_t *d_status,
+                           void *stream);
 
 /* Static text for a host status code or a device status word. */
 const char *amla_status_string(int status);

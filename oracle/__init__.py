@@ -325,6 +325,14 @@ def merge_sources(outs, lses):
 
 # ------------------------------------------------ query build and cache write
 
+def bf16_round(x) -> np.ndarray:
+    """x rounded to the nearest BF16 value (8 significant bits), ties to even; written from
+    the format's definition for normal-range values."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                         # x = m 2^e, 1/2 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0), e - 8)   # numpy rounds halves to even
+
+
 def e4m3_encode(y) -> np.ndarray:
     """E4M3FN codes of real values y, rounded to nearest with ties to the even code and
     saturated at +-448 (the cast convention of the inputs: clip, then cast); NaN -> 0x7F.
@@ -382,6 +390,16 @@ def build_query_and_cache(q_bits, w_uk_bits, kv_c_bits, k_pe_bits, positions, co
     rows[:, :VDIM] = kvc
     rows[:, VDIM:] = rope(kpe, cos, sin, neox)
     return query, rows
+
+
+def e4m3_cast_scaled(x, scale: float) -> np.ndarray:
+    """E4M3 codes of x / scale with the scaling decided in FP32 as the kernels decide it:
+    x (a BF16 value, exact in FP32) times the FP32 reciprocal of the FP32 scale, rounded
+    to FP32, then cast.  (An exact division would settle exact ties differently when the
+    scale makes x / scale land on one.)"""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = np.asarray(x, dtype=np.float64).astype(np.float32) * inv
+    return e4m3_encode(y.astype(np.float64))
 
 
 def e4m3_valid_codes(y, rel: float):

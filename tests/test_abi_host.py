@@ -47,6 +47,7 @@ def test_header_constants_match_binding():
     assert int(consts["AMLA_MAX_REQS"]) == b.MAX_REQS
     assert int(consts["AMLA_ERR_WORKSPACE"]) == b.ERR_WORKSPACE
     assert int(consts["AMLA_DEV_BAD_PAGE"]) == b.DEV_BAD_PAGE
+    assert int(consts["AMLA_DEV_BAD_POSITION"]) == b.DEV_BAD_POSITION
     assert int(consts["AMLA_PLAN_FIXED"]) == b.PLAN_FIXED
 
 
@@ -220,8 +221,27 @@ def test_dcp_argument_errors():
     assert merge(n=0) == b.OK
 
 
+def test_build_query_cache_argument_errors():
+    lib = b.load()
+    vp = ctypes.c_void_p
+
+    def call(q=256, w=256, kv=256, pe=256, pos=256, cs=256, max_pos=16, slots=256, n=4, heads=8,
+             neox=0, qs=1.0, ks=1.0, qo=256, cache=256, pool=4):
+        return lib.amla_build_query_cache(vp(q), vp(w), vp(kv), vp(pe), vp(pos), vp(cs), max_pos,
+                                          vp(slots), n, heads, neox, qs, ks, vp(qo), vp(cache),
+                                          pool, None, None)
+
+    for bad in (dict(q=0), dict(w=0), dict(kv=0), dict(pe=0), dict(pos=0), dict(cs=0),
+                dict(slots=0), dict(qo=0), dict(cache=0), dict(n=-1), dict(heads=0),
+                dict(max_pos=0), dict(neox=2), dict(qs=0.0), dict(ks=float("nan")),
+                dict(q=264), dict(w=260), dict(kv=258), dict(qo=257), dict(cache=260),
+                dict(pool=-1)):
+        assert call(**bad) == b.ERR_INVALID, bad
+    assert call(n=0) == b.OK
+
+
 def test_status_strings():
     for code in (b.OK, b.ERR_INVALID, b.ERR_WORKSPACE, b.ERR_LIST, b.ERR_HIP, b.DEV_BAD_LENGTH,
-                 b.DEV_BAD_PAGE, b.DEV_BAD_ITEM):
+                 b.DEV_BAD_PAGE, b.DEV_BAD_ITEM, b.DEV_BAD_POSITION):
         assert b.status_string(code) and b.status_string(code) != "unknown status"
     assert b.status_string(-99) == "unknown status"

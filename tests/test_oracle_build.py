@@ -32,6 +32,17 @@ def test_e4m3_encode_matches_torch_cast():
     assert oracle.e4m3_encode(np.array([1e6, -500.0])).tolist() == [0x7E, 0xFE]
 
 
+def test_bf16_round_matches_torch_cast():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))).astype(np.float32)
+    # exact ties between neighbouring BF16 values, both parities
+    b = oracle.bf16_values(rng.integers(0x0080, 0x7F00, 2000).astype(np.uint16))
+    ties = (b * (1 + 2.0 ** -8)).astype(np.float32)
+    for v in (x, ties, np.array([0.0, -0.0, 1.0, -3.0], np.float32)):
+        ref = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(oracle.bf16_round(v.astype(np.float64)), ref)
+
+
 def test_rope_closed_forms():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((3, 64))
@@ -119,3 +130,16 @@ def test_pins_catch_build_mutants(monkeypatch):
                 break
         monkeypatch.setattr(oracle, "rope", real_rope)
         assert caught, name
+
+
+def test_scaled_cast_decides_in_fp32():
+    # 50 * (9/640) / (9/640) is exactly a tie between the E4M3 values 48 and 52: an exact
+    # division rounds it to even (48), the FP32 reciprocal product lands just off the tie
+    scale = 6.3 / 448
+    x = np.array([50.0 * np.float32(scale)], np.float64)
+    inv = np.float32(1.0) / np.float32(scale)
+    y32 = (x.astype(np.float32) * inv).astype(np.float64)
+    assert oracle.e4m3_cast_scaled(x, scale)[0] == oracle.e4m3_encode(y32)[0]
+    # away from ties both agree with the plain cast of the quotient
+    v = np.linspace(-400, 400, 1001) * 0.37
+    assert np.mean(oracle.e4m3_cast_scaled(v, 0.37) == oracle.e4m3_encode(v / 0.37)) > 0.99
