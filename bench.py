@@ -357,6 +357,33 @@ def main():
                    "flop": 2 * R * M * 512 * 128,
                    "in_step": bool(args.uv)}
 
+    # the step before the decode: the absorbed query of the step's R*k tokens (H heads) and
+    # their cache rows, from synthetic projections (the new rows go to the pool's last page
+    # slots of a scratch pool so the workload's cache stays as generated)
+    n_tok = R * k_tok
+    qb = wl.query_build_inputs(n_tok, H, seed=1, max_pos=1 << 16)
+    qb_t = dict(
+        q=torch.from_numpy(qb.q.view(np.int16)).to(dev),
+        w_uk=torch.from_numpy(qb.w_uk.view(np.int16)).to(dev),
+        kv_c=torch.from_numpy(qb.kv_c.view(np.int16)).to(dev),
+        k_pe=torch.from_numpy(qb.k_pe.view(np.int16)).to(dev),
+        positions=torch.from_numpy(qb.positions % (1 << 16)).to(dev),
+        cos_sin=torch.from_numpy(qb.cos_sin).to(dev))
+    scratch_pages = (n_tok + 63) // 64
+    scratch = torch.zeros((scratch_pages, 64, 576), dtype=torch.uint8, device=dev)
+    qb_slots = torch.from_numpy(np.random.default_rng(5).permutation(scratch_pages * 64)[:n_tok]
+                                .astype(np.int64)).to(dev)
+    qb_out = torch.empty((n_tok, H, 576), dtype=torch.uint8, device=dev)
+    b_avg = timed(lambda i: binding.build_query_cache(
+        qb_t["q"], qb_t["w_uk"], qb_t["kv_c"], qb_t["k_pe"], qb_t["positions"], qb_t["cos_sin"],
+        qb_slots, qb.neox, qb.q_scale, qb.k_scale, qb_out, scratch, None, stream))
+    b_bytes = (n_tok * H * 192 * 2 + H * 512 * 128 * 2 + n_tok * (512 + 64) * 2
+               + n_tok * 64 * 4 + n_tok * H * 576 + n_tok * 576)
+    query_build = {"kernel": "build_query_cache_kernel", "tokens": n_tok, "heads": H,
+                   "us": round(b_avg * 1e3, 2), "bytes": int(b_bytes),
+                   "gbs": round(b_bytes / (b_avg / 1e3) / 1e9, 1),
+                   "flop": 2 * n_tok * H * 128 * 512}
+
     # the head owner's merge over the DCP sources: N BF16 source rows per folded row
     dcp_res = None
     if dcp is not None:
@@ -401,6 +428,7 @@ def main():
         "combine_us": round(comb_avg * 1e3, 2),
         "value_stage": value_stage,
         "dcp": dcp_res,
+        "query_build": query_build,
         "plan_us": round(plan_us, 2),
         "layer_kv_gbs": round(kv_bytes / ((dec_avg + (uv_avg if args.uv else comb_avg)) / 1e3) / 1e9, 1),
         "layered_step": amortized,
