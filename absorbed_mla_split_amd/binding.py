@@ -34,6 +34,7 @@ DEV_BAD_POSITION = 8
 
 PLAN_BALANCED = 0
 PLAN_FIXED = 1
+PLAN_SLACK = 2      # a plan may hold num_reqs + PLAN_SLACK * workers splits
 
 EXPORTS = (
     "amla_fold_plan", "amla_bmm_scales", "amla_decode_config", "amla_reducer_bands",
@@ -273,7 +274,7 @@ class FoldedDecoder:
         i32 = dict(dtype=torch.int32, device=self.device)
         self.counts = torch.zeros(max(max_reqs, 1), **i32)
         self.offsets = torch.zeros(max_reqs + 1, **i32)
-        self.work = torch.full((2 * (max_reqs + self.params.workers),), -1, **i32)
+        self.work = torch.full((2 * (max_reqs + PLAN_SLACK * self.params.workers),), -1, **i32)
         nbytes = workspace_bytes(max_reqs, rows_per_req, self.params.workers)
         if nbytes == 0:
             raise ValueError("unsupported sizes")

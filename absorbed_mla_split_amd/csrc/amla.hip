@@ -45,6 +45,9 @@ constexpr int kDecodeThreads = 256;            // 4 waves
 constexpr int kChunksPerWave = kPageBytes / (4 * 1024);  // 9 x 1 KiB DMA per wave per page
 constexpr int kHeaderBytes = 256;
 constexpr int kPlanThreads = 256;
+// A plan may use up to kPlanSlack * W units (see the rebalancing rule in the plan kernels):
+// the work list and the workspace hold num_reqs + kPlanSlack * workers splits.
+constexpr int kPlanSlack = 2;
 constexpr int kMaxRuns = 2 * AMLA_MAX_REQS;    // two split-size runs per request
 constexpr float kLog2e = 1.4426950408889634f;
 // Lazy max: the running row max is only raised when a page's max exceeds it by more
@@ -105,7 +108,7 @@ struct WsLayout {
 __host__ __device__ inline WsLayout ws_layout(int64_t reqs, int64_t rows, int64_t workers)
 {
     WsLayout w;
-    const int64_t slots = reqs + workers;
+    const int64_t slots = reqs + kPlanSlack * workers;
     w.partial_off = kHeaderBytes;
     w.lse_off = w.partial_off + (size_t)(slots * rows * kVDim * 4);
     w.total = w.lse_off + (size_t)(((slots * rows * 4) + 255) / 256 * 256);
@@ -267,6 +270,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
     const int R = a.reqs;
     const int64_t mt = ceil_div(a.rows, a.mtile);
     const int64_t budget = (int64_t)a.workers / mt;  // most splits the workers take at once
+    const int64_t budget2 = (int64_t)kPlanSlack * a.workers / mt;
 
     // 1. pages per request, validity, longest request, total pages, non-empty requests
     int64_t bad = 0, pmax = 0, total = 0, nz = 0;
@@ -285,14 +289,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
     // 2. BALANCED: the smallest chunk c with sum_r ceil(pages_r / c) <= budget.  Since
     //    total/c <= sum <= total/c + nz, it lies in [ceil(total/budget),
     //    ceil(total/(budget - nz))]; a 16-way search (one candidate per wave) narrows that.
-    int64_t chunk = 1, fixed = 1;
-    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
-        if (budget < nz) {
+    // the smallest chunk with sum_r ceil(pages_r / c) <= b, at least the minimum split
+    auto search = [&](int64_t b) {
+        int64_t chunk;
+        __syncthreads();   // the candidate flags of an earlier search are read by now
+        if (b < nz) {
             chunk = pmax;                         // no chunk fits: one split per request
         } else {
-            int64_t lo = (total + budget - 1) / budget, hi = pmax;
-            if (budget > nz) {
-                const int64_t h = (total + (budget - nz) - 1) / (budget - nz);
+            int64_t lo = (total + b - 1) / b, hi = pmax;
+            if (b > nz) {
+                const int64_t h = (total + (b - nz) - 1) / (b - nz);
                 hi = h < hi ? h : hi;
             }
             lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
                     int64_t u = 0;
                     for (int r = lane; r < R; r += 64) u += ((uint32_t)pg[r] + c - 1u) / c;
                     u = wave_all64<false>(u);
-                    if (lane == 0) ok[round & 1][cand] = u <= budget;
+                    if (lane == 0) ok[round & 1][cand] = u <= b;
                 }
                 __syncthreads();
                 int first = -1;
@@ -325,7 +331,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
             }
             chunk = hi;
         }
-        chunk = chunk > a.min_pages ? chunk : a.min_pages;
+        return chunk > a.min_pages ? chunk : (int64_t)a.min_pages;
+    };
+    int64_t chunk = 1, fixed = 1;
+    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
+        chunk = search(budget);
+        // rebalance (see plan_small_kernel): the longest split against the mean per worker
+        int64_t longest = 0;
+        for (int r = tid; r < R; r += kPlanThreads) {
+            const uint32_t p = (uint32_t)pg[r];
+            if (p == 0) continue;
+            uint32_t cc = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
+            cc = cc < (uint32_t)a.max_splits ? cc : (uint32_t)a.max_splits;
+            const int64_t sz = (p + cc - 1u) / cc;
+            longest = sz > longest ? sz : longest;
+        }
+        longest = wave_all64<true>(longest);
+        if (lane == 0) red32[wave] = (int32_t)longest;
+        __syncthreads();
+        longest = 0;
+        for (int w = 0; w < kPlanThreads / 64; ++w) longest = red32[w] > longest ? red32[w] : longest;
+        __syncthreads();   // red32 is reused below
+        if (4 * longest * (int64_t)a.workers > 5 * mt * total) chunk = search(budget2);
     } else if (!bad && a.mode == AMLA_PLAN_FIXED) {
         fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
         fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
@@ -503,7 +530,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = a.reqs;
     const int64_t mt = ceil_div(a.rows, a.mtile);
-    const int64_t budget = (int64_t)a.workers / mt;
+    const int64_t budget = (int64_t)a.workers / mt;          // splits W workers take at once
+    const int64_t budget2 = (int64_t)kPlanSlack * a.workers / mt;
 
     // 1. pages per request (every wave reads all lengths); kn = request groups in use
     const int kn = (R + 63) >> 6;
@@ -555,27 +583,46 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
             return (int64_t)((uint32_t)(x - 1) / (uint32_t)y) + 1;
         return (x - 1) / y + 1;
     };
-    int64_t chunk = 1, fixed = 1;
-    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
-        if (budget < nz) {
-            chunk = pmax;
+    // the smallest chunk with units(c) <= b, at least the minimum split
+    auto search = [&](int64_t b) {
+        int64_t c;
+        if (b < nz) {
+            c = pmax;
         } else {
-            int64_t lo = cdiv(total, budget), hi = pmax;
-            if (budget > nz) {
-                const int64_t h = cdiv(total, budget - nz);
+            int64_t lo = cdiv(total, b), hi = pmax;
+            if (b > nz) {
+                const int64_t h = cdiv(total, b - nz);
                 hi = h < hi ? h : hi;
             }
             lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
-            if (lo < hi && units(lo) <= budget) hi = lo;
+            if (lo < hi && units(lo) <= b) hi = lo;
             else if (lo < hi) ++lo;
             while (lo < hi) {
                 const int64_t mid = lo + (hi - lo) / 2;
-                if (units(mid) <= budget) hi = mid;
+                if (units(mid) <= b) hi = mid;
                 else lo = mid + 1;
             }
-            chunk = hi;
+            c = hi;
         }
-        chunk = chunk > a.min_pages ? chunk : a.min_pages;
+        return c > a.min_pages ? c : (int64_t)a.min_pages;
+    };
+    int64_t chunk = 1, fixed = 1;
+    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
+        chunk = search(budget);
+        // rebalance: when the longest split exceeds the mean work per worker by more than a
+        // quarter, plan for twice the workers (about two units per worker)
+        int64_t longest = 0;
+#pragma unroll
+        for (int k = 0; k < kSmallPer; ++k) {
+            if (k >= kn || pg[k] == 0) continue;
+            const uint32_t p = (uint32_t)pg[k];
+            uint32_t cc = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
+            cc = cc < (uint32_t)a.max_splits ? cc : (uint32_t)a.max_splits;
+            const int64_t sz = (p + cc - 1u) / cc;
+            longest = sz > longest ? sz : longest;
+        }
+        longest = wave_all64<true>(longest);
+        if (4 * longest * (int64_t)a.workers > 5 * mt * total) chunk = search(budget2);
     } else if (!bad && a.mode == AMLA_PLAN_FIXED) {
         fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
         fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
@@ -926,7 +973,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 
     // The plan summary, the item count and the first unit's work pair do not depend on
     // each other, so they are loaded together and their latencies overlap.  The pair is
-    // inside the list: its item is below W and list_len >= 2 * (reqs + workers).
+    // inside the list: its item is below W and list_len >= 2 * (reqs + 2 * workers).
     const int vw = virtual_worker(blockIdx.x, W, mt);
     const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
     const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
@@ -939,7 +986,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                  "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
                  "s"(lengths), "s"(counts));
     if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
         return;
     }
@@ -1282,7 +1329,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
                  "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
                  "s"(lengths), "s"(counts));
     if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
         return;
     }
@@ -1596,7 +1643,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
                  "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
                  "s"(lengths), "s"(counts));
     if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + W) {
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
         if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
         return;
     }
@@ -2496,7 +2543,7 @@ int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols
         return AMLA_ERR_INVALID;
     if (ws_bytes < amla_workspace_bytes(num_reqs, params->rows_per_req, params->workers))
         return AMLA_ERR_WORKSPACE;
-    if ((int64_t)list_len < 2 * ((int64_t)num_reqs + params->workers)) return AMLA_ERR_LIST;
+    if ((int64_t)list_len < 2 * ((int64_t)num_reqs + kPlanSlack * params->workers)) return AMLA_ERR_LIST;
     PlanArgs a;
     a.lengths = d_lengths;
     a.counts = d_counts;
@@ -2541,7 +2588,7 @@ static int decode_launch(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_p
         return AMLA_ERR_INVALID;
     const WsLayout lay = ws_layout(num_reqs, params->rows_per_req, params->workers);
     if (ws_bytes < lay.total) return AMLA_ERR_WORKSPACE;
-    if ((int64_t)list_len < 2 * ((int64_t)num_reqs + params->workers)) return AMLA_ERR_LIST;
+    if ((int64_t)list_len < 2 * ((int64_t)num_reqs + kPlanSlack * params->workers)) return AMLA_ERR_LIST;
     if (num_reqs == 0) return AMLA_OK;
     DecodeArgs a;
     a.pool_pages = pool_pages;
@@ -2683,7 +2730,7 @@ int amla_combine(const void *d_workspace, size_t ws_bytes, const int32_t *d_coun
     a.reqs = num_reqs;
     a.rows = params->rows_per_req;
     a.bands = bands;
-    a.slots = num_reqs + params->workers;
+    a.slots = num_reqs + kPlanSlack * params->workers;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(rows * bands)), dim3(64), 0,
                        (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
@@ -2715,7 +2762,7 @@ int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_c
     a.rows = params->rows_per_req;
     a.heads = heads;
     a.k = params->rows_per_req / heads;
-    a.slots = num_reqs + params->workers;
+    a.slots = num_reqs + kPlanSlack * params->workers;
     const int64_t per_head = (int64_t)num_reqs * a.k;
     // 16-row tiles, or 8-row tiles when 16-row tiles would leave compute units idle
     const int64_t tiles16 = (per_head + kUvRows - 1) / kUvRows;

@@ -52,7 +52,7 @@ extern "C" {
 #define AMLA_OK 0
 #define AMLA_ERR_INVALID (-1)   /* null pointer, size or parameter out of range */
 #define AMLA_ERR_WORKSPACE (-2) /* workspace smaller than amla_workspace_bytes() */
-#define AMLA_ERR_LIST (-3)      /* list_len < 2 * (num_reqs + workers) */
+#define AMLA_ERR_LIST (-3)      /* list_len < 2 * (num_reqs + 2 * workers) */
 #define AMLA_ERR_HIP (-4)       /* a kernel launch failed */
 
 /* Device status word (int32 at byte AMLA_WS_STATUS of the workspace), bit flags. */
@@ -127,9 +127,9 @@ int amla_reducer_bands(int32_t rows, int32_t compute_units, int32_t *bands_out);
 
 /*
  * Workspace bytes for up to num_reqs requests (host only): a 256-byte header (device
- * status, plan summary), then FP32 partials [num_reqs + workers][rows_per_req][512] and
- * FP32 log2 LSE [num_reqs + workers][rows_per_req] (every plan has at most
- * num_reqs + workers splits).  Returns 0 for arguments out of range.
+ * status, plan summary), then FP32 partials [num_reqs + 2 * workers][rows_per_req][512] and
+ * FP32 log2 LSE [num_reqs + 2 * workers][rows_per_req] (every plan has at most
+ * num_reqs + 2 * workers splits).  Returns 0 for arguments out of range.
  */
 size_t amla_workspace_bytes(int32_t num_reqs, int32_t rows_per_req, int32_t workers);
 
@@ -145,11 +145,13 @@ size_t amla_workspace_bytes(int32_t num_reqs, int32_t rows_per_req, int32_t work
  *              offsets[r] + s; offsets[num_reqs] = items in the work list
  *   d_work     int32 [list_len] out: (r, s) pairs, longest split first (ties: lower r,
  *              then lower s), then -1
- *   list_len   >= 2 * (num_reqs + workers)
+ *   list_len   >= 2 * (num_reqs + 2 * workers)
  *   d_workspace / ws_bytes: the workspace (header written here)
- * The split rule: pages_r = ceil(L_r/64), mt = ceil(M/MT).  BALANCED: chunk = the
- * smallest c >= 1 with mt * sum_r ceil(pages_r/c) <= W (the longest request if none),
- * at least ceil(min_split_tokens/64); count_r = min(max_splits, ceil(pages_r/chunk)).
+ * The split rule: pages_r = ceil(L_r/64), mt = ceil(M/MT).  BALANCED: chunk(B) = the
+ * smallest c >= 1 with mt * sum_r ceil(pages_r/c) <= B (the longest request if none), at
+ * least ceil(min_split_tokens/64); count_r = min(max_splits, ceil(pages_r/chunk)) with
+ * chunk = chunk(W), unless the longest split then exceeds 5/4 of the mean work per worker
+ * (4 * max_r ceil(pages_r/count_r) * W > 5 * mt * sum_r pages_r): then chunk = chunk(2W).
  * FIXED: count_r = min(pages_r, clamp(floor(W/(R*mt)), 1, max_splits)).  Split s of r has
  * q + (s < rem) pages starting at page s*q + min(s, rem), q = pages_r / count_r,
  * rem = pages_r % count_r.

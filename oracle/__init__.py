@@ -152,7 +152,7 @@ def plan(lengths, bt_cols, M, MT, W, min_split_tokens=256, max_splits=256, mode=
     lengths = np.ascontiguousarray(lengths, dtype=np.int32)
     R = lengths.shape[0]
     if list_len is None:
-        list_len = 2 * (R + W)
+        list_len = 2 * (R + 2 * W)
     counts = np.zeros(R, dtype=np.int32)
     offsets = np.zeros(R + 1, dtype=np.int32)
     work = np.zeros(max(list_len, 1), dtype=np.int32)

@@ -214,9 +214,14 @@ static int oracle_item_order(const void *x, const void *y)
  * The split plan (this project's reading; the pages leave the formula open).
  *
  *   pages_r = ceil(L_r / 64); mt = ceil(M / MT) row tiles per split.
- *   BALANCED: chunk = the smallest c >= 1 with mt * sum_r ceil(pages_r / c) <= W
+ *   BALANCED: chunk(B) = the smallest c >= 1 with mt * sum_r ceil(pages_r / c) <= B
  *             (c = max pages if none), raised to at least ceil(min_split_tokens / 64);
- *             count_r = min(max_splits, ceil(pages_r / chunk)).
+ *             count_r = min(max_splits, ceil(pages_r / chunk)), with chunk = chunk(W);
+ *             but when the longest split, max_r ceil(pages_r / count_r), exceeds 5/4 of the
+ *             mean work per worker, mt * sum_r pages_r / W (that is, 4 * longest * W >
+ *             5 * mt * total), chunk = chunk(2 W): finer splits, about two per worker,
+ *             so that a batch of very different lengths does not wait on its longest
+ *             split.
  *   FIXED:    count_r = min(pages_r, clamp(floor(W / (R * mt)), 1, max_splits)).
  *   count_r = 0 when pages_r = 0.
  *   offsets = exclusive prefix sum of counts (workspace slot of (r, s) = offsets[r] + s).
@@ -229,6 +234,26 @@ static int oracle_item_order(const void *x, const void *y)
  * Returns the number of items, -1 on invalid arguments (negative length,
  * pages_r > bt_cols, bad sizes), -2 if list_len < 2 * items.
  */
+/* The smallest chunk c >= 1 with mt * sum_r ceil(pages_r / c) <= budget (the longest
+   request's pages if none), raised to min_pages; by trying every c in turn. */
+static int32_t oracle_chunk(const int32_t *lengths, int32_t R, int32_t mt, int64_t pmax,
+                            int64_t budget, int32_t min_pages)
+{
+    int32_t chunk = (int32_t)(pmax > 0 ? pmax : 1);
+    for (int64_t c = 1; c <= pmax; ++c) {
+        int64_t units = 0;
+        for (int32_t r = 0; r < R; ++r) {
+            int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
+            units += mt * ((pages + c - 1) / c);
+        }
+        if (units <= budget) {
+            chunk = (int32_t)c;
+            break;
+        }
+    }
+    return chunk < min_pages ? min_pages : chunk;
+}
+
 int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, int32_t MT,
                 int32_t W, int32_t min_split_tokens, int32_t max_splits, int32_t mode,
                 int32_t *counts, int32_t *offsets, int32_t *work, int32_t list_len)
@@ -254,20 +279,22 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
     }
 
     if (mode == 0) {
-        chunk = (int32_t)(pmax > 0 ? pmax : 1);
-        for (int64_t c = 1; c <= pmax; ++c) {
-            int64_t units = 0;
-            for (int32_t r = 0; r < R; ++r) {
-                int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-                units += mt * ((pages + c - 1) / c);
-            }
-            if (units <= W) {
-                chunk = (int32_t)c;
-                break;
-            }
+        int64_t total = 0, longest = 0;
+        chunk = oracle_chunk(lengths, R, mt, pmax, (int64_t)W, min_pages);
+        for (int32_t r = 0; r < R; ++r) {
+            int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
+            int64_t c = (pages + chunk - 1) / chunk, size;
+            total += pages;
+            if (pages == 0)
+                continue;
+            if (c > max_splits)
+                c = max_splits;
+            size = (pages + c - 1) / c;
+            if (size > longest)
+                longest = size;
         }
-        if (chunk < min_pages)
-            chunk = min_pages;
+        if (4 * longest * (int64_t)W > 5 * (int64_t)mt * total)
+            chunk = oracle_chunk(lengths, R, mt, pmax, 2 * (int64_t)W, min_pages);
         for (int32_t r = 0; r < R; ++r) {
             int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
             int64_t c = pages == 0 ? 0 : (pages + chunk - 1) / chunk;

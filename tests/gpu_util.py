@@ -87,7 +87,7 @@ def compare(w, out, lse, rows=None, tag=""):
 def ws_partials(dec, w):
     """FP32 partials [slots, M, 512] and LSE [slots, M] from the decoder's workspace."""
     W = dec.params.workers
-    slots = dec.max_reqs + W
+    slots = dec.max_reqs + binding.PLAN_SLACK * W
     ws = dec.workspace.cpu().numpy()
     part = ws[256:256 + slots * w.M * 512 * 4].view(np.float32).reshape(slots, w.M, 512)
     off = 256 + slots * w.M * 512 * 4

@@ -105,10 +105,11 @@ def test_decode_config():
 
 
 def test_workspace_bytes_formula():
-    # header 256 B + FP32 partials (R+W)*M*512*4 + FP32 LSE (R+W)*M*4 rounded to 256 B
+    # header 256 B + FP32 partials (R+2W)*M*512*4 + FP32 LSE (R+2W)*M*4 rounded to 256 B
     R, M, W = 64, 32, 256
-    lse = ((R + W) * M * 4 + 255) // 256 * 256
-    assert b.workspace_bytes(R, M, W) == 256 + (R + W) * M * 512 * 4 + lse
+    S = R + 2 * W
+    lse = (S * M * 4 + 255) // 256 * 256
+    assert b.workspace_bytes(R, M, W) == 256 + S * M * 512 * 4 + lse
     assert b.workspace_bytes(-1, 32, 256) == 0
     assert b.workspace_bytes(4, 0, 256) == 0
     assert b.workspace_bytes(b.MAX_REQS + 1, 32, 256) == 0
@@ -135,7 +136,7 @@ def test_plan_argument_errors():
     assert _call_plan(lib, params=b.make_params(32, 32, 256, mode=7)) == b.ERR_INVALID
     assert _call_plan(lib, params=b.make_params(32, 32, 256, max_splits=0)) == b.ERR_INVALID
     assert _call_plan(lib, ws_bytes=100) == b.ERR_WORKSPACE
-    assert _call_plan(lib, list_len=2 * (2 + 256) - 1) == b.ERR_LIST
+    assert _call_plan(lib, list_len=2 * (2 + 2 * 256) - 1) == b.ERR_LIST
 
 
 def test_decode_and_combine_argument_errors():

@@ -34,7 +34,9 @@ MUTANTS = {
     "merge weight base": ("double w = exp2(lse[s] - *lse_out);", "double w = exp(lse[s] - *lse_out);"),
     "plan ties by request descending": ("return p->r < q->r ? -1 : 1;", "return p->r > q->r ? -1 : 1;"),
     "plan shortest first": ("return p->size > q->size ? -1 : 1;", "return p->size < q->size ? -1 : 1;"),
-    "plan ignores min split": ("if (chunk < min_pages)\n            chunk = min_pages;", ""),
+    "plan ignores min split": ("return chunk < min_pages ? min_pages : chunk;", "return chunk;"),
+    "plan never rebalances": ("if (4 * longest * (int64_t)W > 5 * (int64_t)mt * total)",
+                              "if (0)"),
     "split remainder to the end": ("items[n].size = (int32_t)(q + (s < rem));",
                                    "items[n].size = (int32_t)(q + (s >= count_r_dummy));"),
 }
@@ -51,6 +53,7 @@ PIN_TESTS = [
     plan_pins.test_plan_worked_example_two_requests,
     lambda: plan_pins.test_plan_properties_random(3),
     plan_pins.test_plan_exhaustive_small,
+    plan_pins.test_plan_rebalances_a_skewed_batch,
 ]
 
 

@@ -65,7 +65,7 @@ def check_plan(lengths, M, MT, W, min_tokens=256, max_splits=256, mode=oracle.BA
     pages = pages_of(lengths)
     mt = -(-M // MT)
     assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts) and offsets[R] == n
-    assert n <= R + W
+    assert n <= R + 2 * W
     sizes = {}
     for r in range(R):
         if pages[r] == 0:
@@ -127,6 +127,15 @@ def best_uniform_chunk(pages, mt, W, min_pages, max_splits):
     return best
 
 
+def expected_longest(pages, mt, W, min_pages, max_splits):
+    """The plan's longest split by exhaustive search: the best uniform chunk within W
+    workers, or within 2W when that longest split exceeds 5/4 of the mean per worker."""
+    best = best_uniform_chunk(pages, mt, W, min_pages, max_splits)
+    if best is not None and 4 * best * W > 5 * mt * sum(pages):
+        best = best_uniform_chunk(pages, mt, 2 * W, min_pages, max_splits)
+    return best
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_properties_random(seed):
     rng = np.random.default_rng(seed)
@@ -139,7 +148,7 @@ def test_plan_properties_random(seed):
     min_tokens = int(rng.choice([0, 64, 256, 1000]))
     counts, offsets, work, n, sizes, mt = check_plan(lengths, M, MT, W, min_tokens)
     pages = pages_of(lengths)
-    best = best_uniform_chunk(pages, mt, W, -(-min_tokens // 64), 256)
+    best = expected_longest(pages, mt, W, -(-min_tokens // 64), 256)
     longest = max(sizes.values()) if sizes else 0
     if best is not None:
         assert longest == best
@@ -153,7 +162,7 @@ def test_plan_exhaustive_small():
             for W in (1, 3, 8):
                 counts, offsets, work, n, sizes, mt = check_plan(list(lengths), 32, 32, W, 0)
                 pages = pages_of(lengths)
-                best = best_uniform_chunk(pages, 1, W, 0, 256)
+                best = expected_longest(pages, 1, W, 0, 256)
                 if best is not None and sizes:
                     assert max(sizes.values()) == best
                 check_plan(list(lengths), 32, 32, W, 0, mode=oracle.FIXED)
@@ -166,3 +175,19 @@ def test_plan_rejects_bad_input():
         oracle.plan([64 * 5], 4, 32, 32, 256)          # more pages than table columns
     with pytest.raises(ValueError):
         oracle.plan([64] * 4, 4, 32, 32, 256, list_len=3)
+
+
+def test_plan_rebalances_a_skewed_batch():
+    # pages [7, 1], 4 workers: chunk(4) = 3 gives splits 3, 2, 2 and 1 page, the longest (3)
+    # above 5/4 of the mean per worker (8 / 4 = 2), so the plan takes chunk(8) = 1: eight
+    # one-page splits, two per worker
+    counts, offsets, work, n = oracle.plan(np.array([7 * 64, 64], np.int32), 8, 32, 32, 4,
+                                           min_split_tokens=0)
+    assert counts.tolist() == [7, 1] and offsets.tolist() == [0, 7, 8] and n == 8
+    assert work[:16].tolist() == [0, 0, 0, 1, 0, 2, 0, 3, 0, 4, 0, 5, 0, 6, 1, 0]
+    assert np.all(work[16:] == -1)
+    # pages [10, 1, 1, 1], 8 workers: chunk(8) = 2, longest 2 against a mean of 13/8 (not
+    # above 5/4 of it): no rebalancing
+    counts, _, _, n = oracle.plan(np.array([640, 64, 64, 64], np.int32), 16, 32, 32, 8,
+                                  min_split_tokens=0)
+    assert counts.tolist() == [5, 1, 1, 1] and n == 8
