@@ -86,6 +86,37 @@ def test_over_64_splits_per_request():
     compare(w, out, lse, tag="201-splits")
 
 
+def test_most_splits_per_request():
+    # 300 pages, one-page minimum and 600 workers: the split count hits its cap of 256, so
+    # the reducer holds four LSEs on every lane
+    w = wl.small(2, 4, 8, [64 * 300, 64 * 3], seed=9)
+    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=600)
+    assert dec.plan_host()[0].tolist() == [binding.MAX_SPLITS, 3]
+    compare(w, out, lse, tag="256-splits")
+
+
+def test_more_requests_than_the_small_plan_takes():
+    # 300 requests (the block-reduction plan kernel) of mixed short lengths, some empty
+    rng = np.random.default_rng(21)
+    lengths = rng.integers(0, 900, 300)
+    lengths[rng.random(300) < 0.1] = 0
+    w = wl.small(300, 4, 8, lengths.tolist(), seed=21)
+    out, lse, dec = run_gpu(w)
+    assert dec.device_status() == 0
+    compare(w, out, lse, rows=sample_rows(w, 2), tag="R300")
+
+
+def test_most_requests():
+    # the largest batch one plan takes: 4096 requests of 1..130 keys
+    rng = np.random.default_rng(22)
+    lengths = rng.integers(1, 131, binding.MAX_REQS)
+    w = wl.small(binding.MAX_REQS, 2, 8, lengths.tolist(), seed=22)
+    out, lse, dec = run_gpu(w)
+    assert dec.device_status() == 0
+    rows = [(r, i) for r in range(0, binding.MAX_REQS, 97) for i in (0, 15)]
+    compare(w, out, lse, rows=rows, tag="R4096")
+
+
 @pytest.mark.parametrize("mode", [binding.PLAN_BALANCED, binding.PLAN_FIXED])
 def test_plans_agree(mode):
     w = wl.small(5, 7, 8, [3000, 100, 6000, 64, 9000], seed=2)
