@@ -1,5 +1,5 @@
 // Folded split-KV absorbed-MLA decode for MI355X (gfx950): plan, decode and combine
-// kernels behind the C ABI declared in include/amla.h.
+// kernels, and the steps next to them, behind the C ABI declared in include/amla.h.
 //
 // Method (page "vllm.models.kimi_k3.nvidia.specialized_decode.drafter.attention", module
 // docstring; page "...cutedsl.mla.balanced", module docstring): MQA over one latent head
@@ -13,10 +13,8 @@
 //             equal-size splits by counting the runs that sort before it.  More requests:
 //             block reductions and scans, a rank or bitonic sort of the runs.
 //   * decode  one persistent 256-thread workgroup per CU.  A work unit is (request, split,
-//             row tile of MT = 32*G rows).  The four waves share one page stream: pages
-//             (64 tokens x 576 B) go HBM -> LDS by global_load_lds_dwordx4 into a ring of
-//             four page slots, three pages ahead of the one being computed.  Wave w owns
-//             the 32-row group w / (4/G) and 512*G/4 of the output dims.  Per page:
+//             row tile of MT rows).  Pages (64 tokens x 576 B) go HBM -> LDS by
+//             global_load_lds_dwordx4 into a ring of four page slots.  Per page and 32 rows:
 //               S^T[64 keys x 32 rows] = K Q^T : 18 x v_mfma_f32_32x32x64_f8f6f4, K read
 //                                                 from LDS, Q^T resident in VGPRs;
 //               softmax in log2 units, lazy row max (rescale O only when the page max
@@ -24,8 +22,16 @@
 //               O^T[dims x 32 rows] += V^T P^T : V^T fragments come from LDS through
 //                                                 ds_read_b64_tr_b8 transposed reads.
 //             The accumulator layout puts one query row per lane, so the running max,
-//             sum and rescale are lane-local; one lane-swap merges the two key halves.
+//             sum, rescale and the per-row key limit (causal mask over a DCP shard) are
+//             lane-local; one lane-swap merges the two key halves.  Three kernels:
+//             decode32 (MT = 32: wave pairs on alternate pages), decode64 (MT = 64: pairs
+//             on alternate pages, partners swapping P) and decode128 (MT = 128: the four
+//             waves on every page, partners swapping P).
 //   * combine one wave per (row, band); merges the splits of a row with exp2 weights.
+//   * combine_uv  the merge fused with the W_UV up-projection (BF16 MFMA).
+//   * merge_sources  a head owner's merge of rows computed on several DCP shards.
+//   * build_query_cache  the step before the decode: the absorbed query (W_UK_T on BF16
+//             MFMA, rotary embedding, E4M3 cast) and the new tokens' cache rows.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
