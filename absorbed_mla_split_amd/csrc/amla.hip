@@ -2138,10 +2138,10 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
         for (int s = 0; s < 16; ++s) wf[s] = *(const bf16x8 *)(wv + 32 * s);
     }
 
-    // merge (the weights of combine_row): TPR threads per row; thread t32 of row rho holds
-    // float4s t32 + TPR jj (jj < NJ).  The row's first LSEs and its first batch of partials
+    // merge (the weights of combine_row): TPR threads per row; thread tr of row rho holds
+    // float4s tr + TPR jj (jj < NJ).  The row's first LSEs and its first batch of partials
     // are loaded together, right after the request's count and offset.
-    const int rho = tid / TPR, t32 = tid % TPR;
+    const int rho = tid / TPR, tr = tid % TPR;
     const int j = j0 + rho;
     int r = 0, i = 0, c = 0;
     int64_t base = 0;
@@ -2156,10 +2156,10 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
     if (c == 0) base = 0;   // every address formed below stays inside slot 0
     const int64_t g = (int64_t)r * a.rows + i;
     const float *lrow_g = a.lse + base * a.rows + i;              // split s at s * rows
-    const float *prow = a.partial + (base * a.rows + i) * kVDim + 4 * t32;
+    const float *prow = a.partial + (base * a.rows + i) * kVDim + 4 * tr;
     const int64_t pstride = (int64_t)a.rows * kVDim;
 
-    float ls = t32 < c ? lrow_g[(int64_t)t32 * a.rows] : -INFINITY;
+    float ls = tr < c ? lrow_g[(int64_t)tr * a.rows] : -INFINITY;
     v4f p[kUvBatch][NJ];
 #pragma unroll
     for (int b = 0; b < kUvBatch; ++b) {
@@ -2169,17 +2169,17 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
             p[b][jj] = c > 0 ? *(const v4f *)(prow + sb * pstride + 4 * TPR * jj) : v4f{0, 0, 0, 0};
     }
     float mx = ls;
-    for (int s = t32 + TPR; s < c; s += TPR) mx = fmaxf(mx, lrow_g[(int64_t)s * a.rows]);
+    for (int s = tr + TPR; s < c; s += TPR) mx = fmaxf(mx, lrow_g[(int64_t)s * a.rows]);
 #pragma unroll
     for (int o = TPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     float sum = 0.f;
-    if (t32 < c) {
+    if (tr < c) {
         // a row with no key in any split (possible under a causal mask) has mx = -inf
         const float w = mx != -INFINITY ? __builtin_amdgcn_exp2f(ls - mx) : 0.f;
-        wts[rho][t32] = w;
+        wts[rho][tr] = w;
         sum = w;
     }
-    for (int s = t32 + TPR; s < c; s += TPR) {
+    for (int s = tr + TPR; s < c; s += TPR) {
         const float w = mx != -INFINITY ? __builtin_amdgcn_exp2f(lrow_g[(int64_t)s * a.rows] - mx) : 0.f;
         wts[rho][s] = w;
         sum += w;
@@ -2211,7 +2211,7 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
     }
 
     // one BF16 rounding: the latent tile in LDS (and the optional global copy)
-    uint16_t *lrow = lat + rho * kUvStride + 4 * t32;
+    uint16_t *lrow = lat + rho * kUvStride + 4 * tr;
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
         uint32_t lo = 0x7FC07FC0u, hi = 0x7FC07FC0u;
@@ -2221,14 +2221,14 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
         }
         *(uint2 *)(lrow + 4 * TPR * jj) = make_uint2(lo, hi);
         if (a.out && j < per_head)
-            *(uint2 *)(a.out + g * kVDim + 4 * t32 + 4 * TPR * jj) = make_uint2(lo, hi);
+            *(uint2 *)(a.out + g * kVDim + 4 * tr + 4 * TPR * jj) = make_uint2(lo, hi);
     }
     if (ROWS < kUvRows) {   // the MFMA's 16 rows: the tile's unused rows are zero
         for (int x = tid; x < (kUvRows - ROWS) * kVDim / 4; x += 512)
             *(uint2 *)(lat + (ROWS + x / (kVDim / 4)) * kUvStride + 4 * (x % (kVDim / 4))) =
                 make_uint2(0u, 0u);
     }
-    if (a.out_lse && j < per_head && t32 == 0)
+    if (a.out_lse && j < per_head && tr == 0)
         a.out_lse[g] = bad ? NAN : c > 0 ? mx + __builtin_amdgcn_logf(sum) : -INFINITY;
     __syncthreads();
 
