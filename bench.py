@@ -119,9 +119,16 @@ def cpu_baseline(w, target_s):
                       rows=rows)
     dt = time.perf_counter() - t
     full_s = dt * keys_total / max(pairs, 1.0)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(w.kv_bytes / full_s / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "sample": f"{sample}; {dt:.1f} s measured, scaled to the workload",
-            "rows_per_s": round(R * M / full_s, 2)}
+            "rows_per_s": round(R * M / full_s, 2), "cpu_model": cpu_model,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -239,13 +246,22 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    # events between graph replays (or eager steps) give the per-step spread; the value
+    # itself is the total over exactly `steps` steps between `start` and `end`
+    marks = []
     start.record(stream)
     if plan_graphs:
-        for g, _ in plan_graphs:
+        for g, n in plan_graphs:
             g.replay()
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            marks.append((e, n))
     else:
         for i in range(args.steps):
             step(i)
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(stream)
+            marks.append((e, 1))
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -256,6 +272,12 @@ def main():
         sys.exit(1)
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    per_step_us, prev = [], start
+    for e, n in marks:
+        per_step_us.append(prev.elapsed_time(e) * 1e3 / n)
+        prev = e
+    spread = {f"p{q}": round(float(np.percentile(per_step_us, q)), 2) for q in (10, 50, 90)}
+    spread["samples"] = len(per_step_us)
 
     # Each kernel's own average duration, measured live with HIP events on the stream its
     # launches run on: after one plan, `steps` launches of the kernel back to back between
@@ -424,6 +446,7 @@ def main():
                    f"hip_graph x{plan_graphs[0][1]} steps" if plan_graphs else "hip_graph"},
         "rows_per_s": round(rows_per_s, 1),
         "step_us": round(ms_per_step * 1e3, 2),
+        "step_us_spread": spread,
         "decode_us": round(dec_avg * 1e3, 2),
         "combine_us": round(comb_avg * 1e3, 2),
         "value_stage": value_stage,
