@@ -71,6 +71,18 @@ def test_small_shapes_every_row(k, H, lengths, min_split_tokens):
     assert dec.device_status() == 0
 
 
+@pytest.mark.parametrize("k,H,mtile", [(4, 8, 64), (4, 8, 128), (7, 8, 32), (7, 8, 128),
+                                        (4, 64, 32), (4, 64, 64), (3, 11, 128)])
+def test_every_tile_size_for_any_rows(k, H, mtile):
+    # the row tile is a free parameter of the ABI: every kernel on shapes it is not picked
+    # for by default (several tiles per split, or most of a tile idle)
+    w = wl.small(3, k, H, [1000, 64 * 7 + 3, 2500], seed=k * H + mtile)
+    out, lse, dec = run_gpu(w, mtile=mtile)
+    assert dec.params.mtile == mtile
+    compare(w, out, lse, tag=f"M{k * H} MT{mtile}")
+    assert dec.device_status() == 0
+
+
 def test_many_splits_small_workers():
     # few workers and no minimum split: long requests cut into many 1-page splits
     w = wl.small(3, 4, 8, [2000, 64 * 40, 90], seed=3)
