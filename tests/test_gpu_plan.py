@@ -87,3 +87,14 @@ def test_plan_request_count_boundaries(R):
         plan_both(lengths, M, binding.PLAN_FIXED, 0, workers=workers)
     plan_both(np.full(R, 8192, np.int32), 32)            # uniform: the lower bound is the chunk
     plan_both(np.full(R, 8192, np.int32), 32, max_splits=3)
+
+
+@pytest.mark.parametrize("R", [100, 300, 1000])
+def test_plan_rebalanced_skewed_batches(R):
+    # log-uniform lengths: the longest split at one unit per worker exceeds 5/4 of the mean,
+    # so the plan takes the finer chunk (more items than workers); both planners, bit-exact
+    rng = np.random.default_rng(R)
+    lengths = np.floor(np.exp(rng.uniform(np.log(64), np.log(65536), R))).astype(np.int32)
+    dec = plan_both(lengths, 32)
+    n = dec.plan_host()[3]
+    assert n > dec.params.workers
