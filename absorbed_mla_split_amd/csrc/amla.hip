@@ -2484,21 +2484,20 @@ int amla_fold_plan(int32_t causal, int32_t num_reqs, int32_t num_rows, int32_t n
 {
     if (!k_out || !fold_out || heads < 1 || (need_lse && max_fold_heads < heads))
         return AMLA_ERR_INVALID;
-    *k_out = 0;
-    *fold_out = 0;
-    if (causal || num_reqs <= 0 || num_rows != num_decode_tokens || num_rows % num_reqs != 0)
-        return AMLA_OK;
-    const int32_t k = num_rows / num_reqs;
-    if (k < 2 || block_table_rows < num_reqs || max_query_len != k) return AMLA_OK;
-    int32_t f = 1;
-    if (!need_lse) {
-        f = k;
-    } else {
-        for (int32_t d = 1; d <= k; ++d)
-            if (k % d == 0 && (int64_t)d * heads <= max_fold_heads) f = d;
-    }
-    *k_out = k;
-    *fold_out = f;
+    // A non-causal draft block folds when every request has the same k >= 2 decode tokens
+    // (the rows split evenly over the requests and the longest block is that share) and a
+    // block-table row.
+    const int32_t k = num_reqs > 0 ? num_rows / num_reqs : 0;
+    const bool uniform = num_reqs > 0 && (int64_t)k * num_reqs == num_rows &&
+                         max_query_len == k && num_rows == num_decode_tokens;
+    const bool folds = !causal && uniform && k >= 2 && block_table_rows >= num_reqs;
+    // Tokens per folded row: all k without an LSE; with one, the largest divisor of k
+    // that keeps the row within max_fold_heads heads.
+    int32_t f = k;
+    if (need_lse)
+        while (f > 1 && (k % f != 0 || (int64_t)f * heads > max_fold_heads)) --f;
+    *k_out = folds ? k : 0;
+    *fold_out = folds ? f : 0;
     return AMLA_OK;
 }
 

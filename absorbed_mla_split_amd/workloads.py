@@ -132,21 +132,12 @@ def build_tables(lengths: np.ndarray, pool: int, rng: np.random.Generator, cols:
     return bt, perm[:used]
 
 
-def generate(cfg: Config | str, seed: int = 0, lengths: np.ndarray | None = None,
-             pool_pages: int | None = None, poison: bool = True) -> Workload:
-    """Draw one workload.  ``lengths``/``pool_pages`` override the config (for tests)."""
-    if isinstance(cfg, str):
-        cfg = CONFIGS[cfg]
-    rng = np.random.default_rng(seed)
-    if lengths is None:
-        lengths = draw_lengths(cfg.lengths, cfg.R, rng)
-    lengths = np.asarray(lengths, dtype=np.int32)
+def _draw_values(cfg: Config, lengths, bt, used, pool: int, rng: np.random.Generator,
+                 poison: bool = True):
+    """Query rows, then the cache pool, of one layer; NaN codes in unused pages and past
+    each request's length (steps 3 and 4 of the recipe)."""
     R = lengths.shape[0]
     pages = (lengths.astype(np.int64) + PAGE - 1) // PAGE
-    pool = pool_pages if pool_pages is not None else (cfg.pool_pages or int(pages.sum()))
-    pool = max(pool, int(pages.sum()), 1)
-    bt, used = build_tables(lengths, pool, rng)
-
     xq = rng.standard_normal((R, cfg.M, KDIM), dtype=np.float32) * np.float32(cfg.value_std)
     q_scale = cfg.scale or float(np.abs(xq).max()) / E4M3_MAX
     q8 = _codes(xq, q_scale)
@@ -167,7 +158,43 @@ def generate(cfg: Config | str, seed: int = 0, lengths: np.ndarray | None = None
             tail = int(lengths[r]) % PAGE
             if pages[r] > 0 and tail:
                 kv8[bt[r, pages[r] - 1], tail:, :] = NAN_CODE
+    return q8, kv8, float(q_scale), float(k_scale)
+
+
+def generate(cfg: Config | str, seed: int = 0, lengths: np.ndarray | None = None,
+             pool_pages: int | None = None, poison: bool = True) -> Workload:
+    """Draw one workload.  ``lengths``/``pool_pages`` override the config (for tests)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lengths = draw_lengths(cfg.lengths, cfg.R, rng)
+    lengths = np.asarray(lengths, dtype=np.int32)
+    R = lengths.shape[0]
+    pages = (lengths.astype(np.int64) + PAGE - 1) // PAGE
+    pool = pool_pages if pool_pages is not None else (cfg.pool_pages or int(pages.sum()))
+    pool = max(pool, int(pages.sum()), 1)
+    bt, used = build_tables(lengths, pool, rng)
+
+    q8, kv8, q_scale, k_scale = _draw_values(cfg, lengths, bt, used, pool, rng, poison)
     return Workload(cfg, lengths, bt, q8, kv8, float(q_scale), float(k_scale))
+
+
+def layers(w: Workload, n: int, seed: int = 0) -> list[Workload]:
+    """The caches of n model layers over one batch: every layer shares the requests'
+    lengths and block tables (one page id names the same token slot in every layer's
+    pool) and has its own query rows and cache pool, drawn from the stream (seed, 3, layer)
+    by steps 3 and 4 of the recipe.  Layer 0 is ``w`` itself."""
+    pool = w.kv8.shape[0]
+    pages = (w.lengths.astype(np.int64) + PAGE - 1) // PAGE
+    used = np.concatenate([w.block_table[r, :pages[r]] for r in range(w.R)]) \
+        if w.R else np.zeros(0, np.int32)
+    out = [w]
+    for li in range(1, n):
+        rng = np.random.default_rng([seed, 3, li])
+        q8, kv8, qs, ks = _draw_values(w.cfg, w.lengths, w.block_table, used, pool, rng)
+        out.append(Workload(w.cfg, w.lengths, w.block_table, q8, kv8, qs, ks, w.sm_scale))
+    return out
 
 
 def small(R: int, k: int, H: int, lengths, seed: int = 0, extra_pages: int = 3,

@@ -113,8 +113,16 @@ int amla_bmm_scales(float softmax_scale, float q_scale, float k_scale,
                     float *bmm1_out, float *bmm2_out);
 
 /*
- * Decode launch shape for a device (host only): workers = compute_units (one persistent
- * workgroup per CU), mtile = 32 for rows <= 32, 64 for rows <= 64, else 128.
+ * Decode launch shape for a device (host only).  No passage of the pages fixes it: this is
+ * the library's own choice for gfx950 (the pages' counterpart, the worker count of the
+ * balanced core's persistent launch, page "...cutedsl.mla.balanced", module docstring, is
+ * a property of their GPU).  The pages' device query becomes an argument so that a plan
+ * can be reproduced off the device.
+ *   compute_units  CUs of the device (hipDeviceProp_t::multiProcessorCount), >= 1
+ *   rows_per_req   M, 1..AMLA_MAX_ROWS
+ *   workers_out    = compute_units: one persistent workgroup per CU
+ *   mtile_out      rows per work unit: 32 for M <= 32, 64 for M <= 64, else 128
+ * Returns AMLA_ERR_INVALID for null outputs or arguments out of range.
  */
 int amla_decode_config(int32_t compute_units, int32_t rows_per_req,
                        int32_t *workers_out, int32_t *mtile_out);
@@ -126,10 +134,14 @@ int amla_decode_config(int32_t compute_units, int32_t rows_per_req,
 int amla_reducer_bands(int32_t rows, int32_t compute_units, int32_t *bands_out);
 
 /*
- * Workspace bytes for up to num_reqs requests (host only): a 256-byte header (device
- * status, plan summary), then FP32 partials [num_reqs + 2 * workers][rows_per_req][512] and
- * FP32 log2 LSE [num_reqs + 2 * workers][rows_per_req] (every plan has at most
- * num_reqs + 2 * workers splits).  Returns 0 for arguments out of range.
+ * Workspace bytes for up to num_reqs requests (host only).  Precedent: page
+ * "drafter.attention", tier_workspace_bytes (the split-KV workspace is sized on the host
+ * from the batch shape before any launch, so it can be allocated once, ahead of graph
+ * capture); the layout is the library's own: a 256-byte header (device status, plan
+ * summary), then FP32 partials [num_reqs + 2 * workers][rows_per_req][512] and FP32 log2
+ * LSE [num_reqs + 2 * workers][rows_per_req] (every plan has at most
+ * num_reqs + 2 * workers splits).  The caller allocates and owns the workspace.
+ * Returns 0 for arguments out of range.
  */
 size_t amla_workspace_bytes(int32_t num_reqs, int32_t rows_per_req, int32_t workers);
 

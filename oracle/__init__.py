@@ -40,6 +40,8 @@ def _load():
         f64p = ctypes.POINTER(ctypes.c_double)
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
+        lib.oracle_set_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_table.restype = None
@@ -70,6 +72,11 @@ def _ptr(a: np.ndarray, ctype):
 def threads() -> int:
     """Host threads the oracle's parallel loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> int:
+    """Use n host threads from now on; returns the previous count."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 # --------------------------------------------------------------------------- E4M3FN
@@ -182,34 +189,32 @@ def foldable(causal: bool, num_reqs: int, num_rows: int, num_decode_tokens: int,
              block_table_rows: int, max_query_len: int) -> int:
     """Query tokens per request when a decode batch can be folded, else 0.
 
-    Page "drafter.attention", foldable: only a non-causal batch folds; the rows must be
-    the batch's decode tokens and split evenly over the requests; one token per request
-    leaves nothing to fold; there must be a block-table row per request; and an even
-    split is only proof of uniform blocks when the longest block is exactly k tokens.
+    Page "drafter.attention", section foldable.  The rule: a batch folds into k tokens
+    per request exactly when it is a non-causal draft block in which every request
+    contributes a block of the same k >= 2 query tokens, every row is a decode token, and
+    each request has a block-table row.  Uniform blocks are known from the shape alone:
+    the rows split evenly over the requests and the longest block is that share.
     """
-    if causal:
-        return 0
-    if num_reqs <= 0 or num_rows != num_decode_tokens:
-        return 0
-    if num_rows % num_reqs != 0:
-        return 0
-    k = num_rows // num_reqs
-    if k < 2 or block_table_rows < num_reqs:
-        return 0
-    if max_query_len != k:
-        return 0
-    return k
+    k = num_rows // num_reqs if num_reqs > 0 else 0
+    uniform_blocks = (num_reqs > 0 and k * num_reqs == num_rows
+                      and max_query_len == k and num_rows == num_decode_tokens)
+    folds = (not causal) and uniform_blocks and k >= 2 and block_table_rows >= num_reqs
+    return k if folds else 0
 
 
 def fold_plan(k: int, heads: int, need_lse: bool, max_fold_heads: int) -> int:
     """Tokens folded into one decode row.
 
-    Page "drafter.attention", fold_plan: without an LSE all k tokens fold; with one, the
-    largest divisor f of k with f * heads within the kernel's head limit.
+    Page "drafter.attention", section fold_plan: with no LSE to return all k tokens fold
+    into one row; a kernel that returns an LSE takes at most `max_fold_heads` heads per
+    row, so the fold is the largest divisor f of k whose f * heads stays within it.
     """
     if not need_lse:
         return k
-    return max(d for d in range(1, k + 1) if k % d == 0 and d * heads <= max_fold_heads)
+    f = k
+    while f > 1 and (k % f != 0 or f * heads > max_fold_heads):
+        f -= 1
+    return f
 
 
 # ------------------------------------------------------------ value stage (W_UV)

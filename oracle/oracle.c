@@ -54,6 +54,14 @@ int oracle_threads(void)
     return omp_get_max_threads();
 }
 
+/* Sets the threads later parallel loops use (n >= 1); returns the previous count. */
+int oracle_set_threads(int n)
+{
+    const int prev = omp_get_max_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return prev;
+}
+
 /* ---------------------------------------------------------------- E4M3FN */
 
 double oracle_e4m3_value(uint8_t code)

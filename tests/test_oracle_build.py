@@ -132,14 +132,46 @@ def test_pins_catch_build_mutants(monkeypatch):
         assert caught, name
 
 
-def test_scaled_cast_decides_in_fp32():
-    # 50 * (9/640) / (9/640) is exactly a tie between the E4M3 values 48 and 52: an exact
-    # division rounds it to even (48), the FP32 reciprocal product lands just off the tie
+def _torch_scaled_cast(x, scale):
+    """The FP32-scaled E4M3 cast computed by torch alone: the FP32 value times the FP32
+    reciprocal of the FP32 scale (torch's FP32 product), clipped to +-448 (torch's cast
+    turns larger values into NaN), then torch's float8_e4m3fn cast."""
+    xt = torch.tensor(np.asarray(x, dtype=np.float64), dtype=torch.float32)
+    inv = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32)
+    y = torch.clamp(xt * inv, -448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _cast_cases(scale):
+    """BF16 values whose scaled quotient lands on or next to every E4M3 rounding midpoint,
+    plus random BF16 values of every magnitude up to past saturation."""
+    t = oracle.e4m3_table()[:0x7F]
+    mids = (t[:-1] + t[1:]) / 2
+    near = np.concatenate([mids, -mids, mids * (1 + 2.0 ** -9), mids * (1 - 2.0 ** -9)])
+    rng = np.random.default_rng(7)
+    rand = rng.standard_normal(20000) * np.exp2(rng.uniform(-12, 10, 20000))
+    return oracle.bf16_round(np.concatenate([near, rand]) * scale)
+
+
+@pytest.mark.parametrize("scale", [6.3 / 448, 1.0 / 64, 0.37, 2.5e-3])
+def test_scaled_cast_matches_torch_fp32_route(scale):
+    # pins e4m3_cast_scaled by a route that shares none of its code: every code equal to
+    # torch's FP32 product and float8 cast, on tie-adjacent and random values
+    x = _cast_cases(scale)
+    got = oracle.e4m3_cast_scaled(x, scale)
+    ref = _torch_scaled_cast(x, scale)
+    assert np.array_equal(got, ref), np.count_nonzero(got != ref)
+
+
+def test_scaled_cast_cases_tell_fp32_from_exact_division():
+    # the case set above is sharp: with the synthetic query scale an exact division settles
+    # some of its ties differently from the FP32 product (so a cast written with one would
+    # fail the pin written with the other)
     scale = 6.3 / 448
-    x = np.array([50.0 * np.float32(scale)], np.float64)
-    inv = np.float32(1.0) / np.float32(scale)
-    y32 = (x.astype(np.float32) * inv).astype(np.float64)
-    assert oracle.e4m3_cast_scaled(x, scale)[0] == oracle.e4m3_encode(y32)[0]
-    # away from ties both agree with the plain cast of the quotient
-    v = np.linspace(-400, 400, 1001) * 0.37
-    assert np.mean(oracle.e4m3_cast_scaled(v, 0.37) == oracle.e4m3_encode(v / 0.37)) > 0.99
+    x = _cast_cases(scale)
+    exact = oracle.e4m3_encode(np.asarray(x, dtype=np.float64) / scale)
+    assert np.count_nonzero(exact != _torch_scaled_cast(x, scale)) > 0
+    # a known tie: 50 * fp32(scale) / scale is exactly between 48 and 52; the FP32 product
+    # lands just off it
+    x1 = np.array([50.0 * np.float32(scale)])
+    assert oracle.e4m3_cast_scaled(x1, scale)[0] == _torch_scaled_cast(x1, scale)[0]
