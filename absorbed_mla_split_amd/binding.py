@@ -40,8 +40,9 @@ EXPORTS = (
     "amla_fold_plan", "amla_bmm_scales", "amla_decode_config", "amla_reducer_bands",
     "amla_workspace_bytes", "amla_plan_splits", "amla_folded_decode", "amla_combine",
     "amla_combine_uv", "amla_folded_decode_dcp", "amla_merge_sources", "amla_build_query_cache",
-    "amla_status_string",
+    "amla_status_string", "amla_folded_decode_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MAX_SOURCES = 64
 
 
@@ -112,6 +113,8 @@ def load() -> ctypes.CDLL:
         "amla_build_query_cache": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                                   f32, f32, vp, vp, i64, vp, vp]),
         "amla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "amla_folded_decode_noalloc": (ctypes.c_int, [vp, vp, i64, vp, i32, vp, i32, pp, f32,
+                                                      f32, i32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -218,6 +221,17 @@ def folded_decode_dcp(q, kv, block_table, lengths, params: PlanParams, bmm1, bmm
         _ptr(lengths), lengths.numel(), ctypes.byref(params), bmm1, bmm2, _ptr(counts),
         _ptr(offsets), _ptr(work), work.numel(), _ptr(workspace), workspace.numel(),
         ctypes.byref(dcp), _ptr(totals), _stream(stream)))
+
+
+def folded_decode_noalloc(q, kv, block_table, lengths, params: PlanParams, bmm1, bmm2,
+                          compute_units, out, lse, status=None, stream=None):
+    """Plan, decode and merge in one call with the library's static device scratch (no
+    workspace, nothing allocated): out [R, M, 512] BF16, lse [R, M]; ``status`` (one int32,
+    optional) receives the device status word."""
+    _check("amla_folded_decode_noalloc", load().amla_folded_decode_noalloc(
+        _ptr(q), _ptr(kv), kv.shape[0], _ptr(block_table), block_table.stride(0),
+        _ptr(lengths), lengths.numel(), ctypes.byref(params), bmm1, bmm2, compute_units,
+        _ptr(out), _ptr(lse), _ptr(status), _stream(stream)))
 
 
 def merge_sources(rows, lse, out, lse_out, stream=None):

@@ -36,6 +36,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/amla.h"
@@ -2472,6 +2473,62 @@ bool params_ok(const amla_plan_params *p)
            (p->mode == AMLA_PLAN_BALANCED || p->mode == AMLA_PLAN_FIXED);
 }
 
+// ------------------------------------------------- allocation-free entry: static scratch
+
+// The plan buffers and the split workspace of amla_folded_decode_noalloc live in this
+// file-scope array, one copy per device the library runs on, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it is only a stand-in
+// for the symbol): it uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)AMLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchLayout {
+    size_t counts, offsets, work, workspace, ws_bytes, total;
+    int32_t list_len;
+};
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+inline ScratchLayout scratch_layout(int32_t reqs, int32_t rows, int32_t workers)
+{
+    ScratchLayout l;
+    l.list_len = 2 * (reqs + kPlanSlack * workers);
+    l.counts = 0;
+    l.offsets = align256((size_t)(reqs > 0 ? reqs : 1) * 4);
+    l.work = l.offsets + align256((size_t)(reqs + 1) * 4);
+    l.workspace = l.work + align256((size_t)l.list_len * 4);
+    l.ws_bytes = ws_layout(reqs, rows, workers).total;
+    l.total = l.workspace + l.ws_bytes;
+    return l;
+}
+
+__global__ void copy_status_kernel(const int32_t *__restrict__ header, int32_t *__restrict__ out)
+{
+    if (threadIdx.x == 0) *out = header[kHdrStatus];
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices];
+
+// The device address of `scratch` on the current device, looked up on the first call made
+// with that device current and kept for the later ones.
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return AMLA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxScratchDevices) return AMLA_ERR_INVALID;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return AMLA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return AMLA_OK;
+}
+
 }  // namespace
 
 // ============================================================================ C ABI
@@ -2780,6 +2837,48 @@ int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_c
                                 (unsigned)heads),
                            dim3(512), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
+}
+
+int amla_folded_decode_noalloc(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                               const int32_t *d_block_table, int32_t bt_stride,
+                               const int32_t *d_lengths, int32_t num_reqs,
+                               const amla_plan_params *params, float bmm1_scale,
+                               float bmm2_scale, int32_t compute_units, uint16_t *d_out,
+                               float *d_lse, int32_t *d_status, void *stream)
+{
+    // every argument is checked before the first launch, so an error enqueues nothing
+    if (!params_ok(params) || num_reqs < 0 || num_reqs > AMLA_MAX_REQS || pool_pages < 1 ||
+        bt_stride < 1 || compute_units < 1 || !d_kv ||
+        (num_reqs > 0 && (!d_q || !d_block_table || !d_lengths || !d_out || !d_lse)) ||
+        !std::isfinite(bmm1_scale) || !(bmm1_scale > 0.f) || !std::isfinite(bmm2_scale))
+        return AMLA_ERR_INVALID;
+    const ScratchLayout l = scratch_layout(num_reqs, params->rows_per_req, params->workers);
+    if (l.total > kScratchBytes) return AMLA_ERR_WORKSPACE;
+    void *base = nullptr;
+    const int rc = scratch_address(&base);
+    if (rc != AMLA_OK) return rc;
+    uint8_t *b = (uint8_t *)base;
+    int32_t *counts = (int32_t *)(b + l.counts), *offsets = (int32_t *)(b + l.offsets);
+    int32_t *work = (int32_t *)(b + l.work);
+    void *ws = b + l.workspace;
+    // the plan rewrites the header (status included), the counts, offsets and the whole
+    // work list, and the decode writes every planned slot the merge reads: nothing left
+    // by an earlier call is read
+    int st = amla_plan_splits(d_lengths, num_reqs, bt_stride, params, counts, offsets, work,
+                              l.list_len, ws, l.ws_bytes, stream);
+    if (st == AMLA_OK)
+        st = amla_folded_decode(d_q, d_kv, pool_pages, d_block_table, bt_stride, d_lengths,
+                                num_reqs, params, bmm1_scale, bmm2_scale, counts, offsets, work,
+                                l.list_len, ws, l.ws_bytes, stream);
+    if (st == AMLA_OK)
+        st = amla_combine(ws, l.ws_bytes, counts, offsets, num_reqs, params, compute_units,
+                          d_out, d_lse, stream);
+    if (st == AMLA_OK && d_status) {
+        hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           (const int32_t *)ws, d_status);
+        st = hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
+    }
+    return st;
 }
 
 const char *amla_status_string(int status)

@@ -19,8 +19,9 @@
  * Calling convention for every entry point:
  *   - pointers named d_* are device pointers, owned by the caller;
  *   - the library never allocates device memory, never synchronises and keeps no global
- *     state; all work is enqueued on `stream` (a hipStream_t, NULL = the null stream), so
- *     the calls can be captured into a HIP graph;
+ *     state (except the static device scratch of amla_folded_decode_noalloc); all work is
+ *     enqueued on `stream` (a hipStream_t, NULL = the null stream), so the calls can be
+ *     captured into a HIP graph;
  *   - the return value is AMLA_OK (0) or a negative AMLA_ERR_* code; on error nothing has
  *     been enqueued;
  *   - values that only live on the device (lengths, block-table entries, the work list)
@@ -309,6 +310,37 @@ int amla_build_query_cache(const uint16_t *d_q, const uint16_t *d_w_uk, const ui
                            int32_t neox, float q_scale, float k_scale, uint8_t *d_q_out,
                            uint8_t *d_kv_cache, int64_t pool_pages, int32_t *d_status,
                            void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): amla_plan_splits, amla_folded_decode and
+ * amla_combine in one call, with the plan buffers and the split workspace in the library's
+ * own static device scratch (AMLA_NOALLOC_SCRATCH_BYTES per device, held by every device
+ * the library runs on until the process ends) instead of caller memory.  It allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine.
+ *   arguments   as amla_folded_decode (bt_stride is also the plan's table width) and
+ *               amla_combine; d_out BF16 [num_reqs][rows_per_req][512], d_lse FP32 log2
+ *               [num_reqs][rows_per_req]
+ *   d_status    NULL, or one int32 that receives the call's device status word (the bits
+ *               of AMLA_DEV_*), written on the stream after the merge
+ *   stream      must belong to the current device (the scratch copy used is the current
+ *               device's)
+ * Every call on one device shares that device's scratch, and each call leaves its plan and
+ * partials there: calls that overlap in time on one device (several streams or host
+ * threads) race and must not be issued.  Each call rewrites all the scratch state it reads.
+ * The scratch a call needs is amla_workspace_bytes(num_reqs, rows_per_req, workers) plus
+ * the plan buffers (counts, offsets and the work list of 2 * (num_reqs + 2 * workers)
+ * entries, each rounded up to 256 bytes).  Returns AMLA_ERR_WORKSPACE when that exceeds
+ * AMLA_NOALLOC_SCRATCH_BYTES, AMLA_ERR_INVALID for bad arguments (nothing enqueued),
+ * AMLA_ERR_HIP when the scratch address cannot be found or a launch fails.
+ */
+#define AMLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int amla_folded_decode_noalloc(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_pages,
+                               const int32_t *d_block_table, int32_t bt_stride,
+                               const int32_t *d_lengths, int32_t num_reqs,
+                               const amla_plan_params *params, float bmm1_scale,
+                               float bmm2_scale, int32_t compute_units, uint16_t *d_out,
+                               float *d_lse, int32_t *d_status, void *stream);
 
 /* Static text for a host status code or a device status word. */
 const char *amla_status_string(int status);

@@ -172,6 +172,31 @@ def test_decode_and_combine_argument_errors():
     assert comb(reqs=0) == b.OK
 
 
+def test_noalloc_argument_errors():
+    # rejected on the host before the scratch is looked up or anything is launched
+    lib = b.load()
+    vp = ctypes.c_void_p
+    good = dict(q=1, kv=1, pool=16, bt=1, stride=4, lengths=1, reqs=2, b1=1.0, b2=1.0, cus=256,
+                out=1, lse=1, M=32, W=256)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        p = b.make_params(a["M"], 32 if a["M"] <= 32 else 128, a["W"])
+        return lib.amla_folded_decode_noalloc(vp(a["q"]), vp(a["kv"]), a["pool"], vp(a["bt"]),
+                                              a["stride"], vp(a["lengths"]), a["reqs"],
+                                              ctypes.byref(p), a["b1"], a["b2"], a["cus"],
+                                              vp(a["out"]), vp(a["lse"]), None, None)
+
+    for bad in (dict(q=0), dict(kv=0), dict(bt=0), dict(lengths=0), dict(out=0), dict(lse=0),
+                dict(pool=0), dict(stride=0), dict(cus=0), dict(reqs=-1), dict(reqs=b.MAX_REQS + 1),
+                dict(b1=float("nan")), dict(b1=0.0), dict(b2=float("inf")), dict(M=0),
+                dict(M=b.MAX_ROWS + 1)):
+        assert call(**bad) == b.ERR_INVALID, bad
+    # past the static scratch: 4096 requests of 1024 rows need far more than 64 MiB
+    assert call(reqs=b.MAX_REQS, M=b.MAX_ROWS) == b.ERR_WORKSPACE
+    assert call(reqs=64, M=256) == b.ERR_WORKSPACE
+
+
 def test_combine_uv_argument_errors():
     lib = b.load()
     p = b.make_params(32, 32, 256)
