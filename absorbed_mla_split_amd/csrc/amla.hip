@@ -7,27 +7,22 @@
 // folded into its head axis, each request's keys cut into planned splits that produce
 // FP32 partials and a log2 LSE, and a reducer merging the splits into BF16 rows.
 //
-// gfx950 mapping (this file's design, not the pages'):
-//   * plan    one 256-thread workgroup.  Up to 256 requests: every wave derives the chunk
-//             and the scans by itself (DPP, no barrier), then each thread places one run of
-//             equal-size splits by counting the runs that sort before it.  More requests:
-//             block reductions and scans, a rank or bitonic sort of the runs.
-//   * decode  one persistent 256-thread workgroup per CU.  A work unit is (request, split,
-//             row tile of MT rows).  Pages (64 tokens x 576 B) go HBM -> LDS by
-//             global_load_lds_dwordx4 into a ring of four page slots.  Per page and 32 rows:
-//               S^T[64 keys x 32 rows] = K Q^T : 18 x v_mfma_f32_32x32x64_f8f6f4, K read
-//                                                 from LDS, Q^T resident in VGPRs;
-//               softmax in log2 units, lazy row max (rescale O only when the page max
-//               exceeds it by more than 2^TAU), P = exp2(t - m) to E4M3 in-lane;
-//               O^T[dims x 32 rows] += V^T P^T : V^T fragments come from LDS through
-//                                                 ds_read_b64_tr_b8 transposed reads.
-//             The accumulator layout puts one query row per lane, so the running max,
-//             sum, rescale and the per-row key limit (causal mask over a DCP shard) are
-//             lane-local; one lane-swap merges the two key halves.  Three kernels:
-//             decode32 (MT = 32: wave pairs on alternate pages), decode64 (MT = 64: pairs
-//             on alternate pages, partners swapping P) and decode128 (MT = 128: the four
-//             waves on every page, partners swapping P).
-//   * combine one wave per (row, band); merges the splits of a row with exp2 weights.
+// gfx950 mapping (this library's design, not the pages'):
+//   * plan    (this file) one 256-thread workgroup.  Up to 256 requests: every wave derives
+//             the chunk and the scans by itself (DPP, no barrier), then each thread places one
+//             run of equal-size splits by counting the runs that sort before it.  More
+//             requests: block reductions and scans, a rank or bitonic sort of the runs.
+//   * decode  one persistent workgroup per CU; a work unit is (request, split, row tile of
+//             MT rows); pages (64 tokens x 576 B) go HBM -> LDS by global_load_lds_dwordx4
+//             into a ring of four page slots; S^T = K Q^T and O^T += V^T P^T on
+//             v_mfma_f32_32x32x64_f8f6f4 (the accumulator layout puts one query row per
+//             lane); P in E4M3 against a per-row reference, each key block's P scaled by its
+//             own E8M0 byte in the P V MFMA.  decode_stream.hip: MT = 32, 64 (score and
+//             value waves one entry apart, two waves per SIMD, a stream of entries across
+//             work units); decode128.hip: MT = 128 (four waves per page, key blocks split
+//             between wave pairs, 256 output accumulators per lane in AGPRs).
+//   * combine (this file) one wave per (row, band); merges the splits of a row with exp2
+//             weights.
 //   * combine_uv  the merge fused with the W_UV up-projection (BF16 MFMA).
 //   * merge_sources  a head owner's merge of rows computed on several DCP shards.
 //   * build_query_cache  the step before the decode: the absorbed query (W_UK_T on BF16
@@ -39,90 +34,12 @@
 #include <mutex>
 #include <type_traits>
 
-#include "../../include/amla.h"
+#include "common.h"
+
 
 namespace {
 
-constexpr int kPage = AMLA_PAGE;
-constexpr int kKDim = AMLA_KDIM;
-constexpr int kVDim = AMLA_VDIM;
-constexpr int kPageBytes = kPage * kKDim;      // 36864
-constexpr int kSlots = 4;                      // LDS page ring
-constexpr int kDecodeThreads = 256;            // 4 waves
-constexpr int kChunksPerWave = kPageBytes / (4 * 1024);  // 9 x 1 KiB DMA per wave per page
-constexpr int kHeaderBytes = 256;
-constexpr int kPlanThreads = 256;
-// A plan may use up to kPlanSlack * W units (see the rebalancing rule in the plan kernels):
-// the work list and the workspace hold num_reqs + kPlanSlack * workers splits.
-constexpr int kPlanSlack = 2;
-constexpr int kMaxRuns = 2 * AMLA_MAX_REQS;    // two split-size runs per request
-constexpr float kLog2e = 1.4426950408889634f;
-// Lazy max: the running row max is only raised when a page's max exceeds it by more
-// than 2^kTau, so p = 2^(t - m) <= 2^kTau; P is scaled by 2^kPScale before the E4M3
-// cast (kTau + kPScale <= 8 keeps it <= 256 < 448) to keep small weights out of the
-// subnormal range.
-constexpr float kTau = 2.0f;
-constexpr float kPScale = 6.0f;
-
-// Workspace header words (int32).
-enum HeaderWord {
-    kHdrStatus = 0,
-    kHdrItems = 1,
-    kHdrRows = 2,
-    kHdrMtile = 3,
-    kHdrWorkers = 4,
-    kHdrMode = 5,
-    kHdrReqs = 6,
-    kHdrPlanned = 7,  // 0x600DF00D after a successful plan
-};
-constexpr int kPlannedMagic = 0x600DF00D;
-
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-#define LDS_AS __attribute__((address_space(3)))
-#define CONST_AS __attribute__((address_space(4)))
-
-// A uniform read of memory that no kernel of this file writes while reading it: through
-// the constant address space it is always a scalar load (lgkmcnt), never a vector load,
-// whose vmcnt wait would also wait for the page DMAs in flight.
-template <typename T>
-__device__ __forceinline__ T ldc(const T *p)
-{
-    return *(const CONST_AS T *)p;
-}
-
-// f(std::integral_constant<int, I>) for I in [I0, N): a loop whose index is a constant in
-// every step, so register arrays indexed by it stay in registers.
-template <int I0, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (I0 < N) {
-        f(std::integral_constant<int, I0>{});
-        static_for<I0 + 1, N>(f);
-    }
-}
-
-struct WsLayout {
-    size_t partial_off;  // FP32 [slots][M][512]
-    size_t lse_off;      // FP32 [slots][M]
-    size_t total;
-};
-
-__host__ __device__ inline WsLayout ws_layout(int64_t reqs, int64_t rows, int64_t workers)
-{
-    WsLayout w;
-    const int64_t slots = reqs + kPlanSlack * workers;
-    w.partial_off = kHeaderBytes;
-    w.lse_off = w.partial_off + (size_t)(slots * rows * kVDim * 4);
-    w.total = w.lse_off + (size_t)(((slots * rows * 4) + 255) / 256 * 256);
-    return w;
-}
-
-__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+using namespace amla;
 
 // ------------------------------------------------------------------ block utilities
 
@@ -744,1216 +661,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
         a.header[kHdrMode] = a.mode;
         a.header[kHdrReqs] = R;
         a.header[kHdrPlanned] = kPlannedMagic;
-    }
-}
-
-// -------------------------------------------------------------------- decode kernel
-
-struct DecodeArgs {
-    int64_t pool_pages;
-    int32_t bt_stride, reqs, rows, mtile, workers, list_len;
-    float score_scale;  // bmm1 * log2(e)
-    float out_scale;    // bmm2
-    // causal mask in global positions over a DCP shard (causal == 0: every row sees the
-    // request's whole local length; the other fields are then unused)
-    const int32_t *totals;
-    int32_t causal, heads, k_tokens, cp_world, cp_rank, cp_interleave;
-};
-
-// Keys of the local shard that folded row `row` may see.  Page "...cutedsl.mla.balanced",
-// module docstring and BalancedMla.decode: under DCP the decode reads this rank's shard
-// and masks causally in global positions, from the requests' global lengths.  Draft token
-// t = row / H of a request of `total` global keys sits at position total - k + t and sees
-// the g = total - k + t + 1 positions before it and itself; the rank holds blocks of
-// `interleave` positions dealt round-robin over `world` ranks, in global order, so the
-// visible keys are the first (g / span) * interleave + clamp(g % span - rank * interleave,
-// 0, interleave) of its shard (span = interleave * world).
-__device__ __forceinline__ int shard_count(const DecodeArgs &a, int g)
-{
-    if (g <= 0) return 0;
-    const uint32_t span = (uint32_t)a.cp_interleave * (uint32_t)a.cp_world;
-    const int rem = (int)((uint32_t)g % span) - a.cp_rank * a.cp_interleave;
-    return (int)((uint32_t)g / span) * a.cp_interleave +
-           (rem < 0 ? 0 : rem > a.cp_interleave ? a.cp_interleave : rem);
-}
-
-__device__ __forceinline__ int row_key_limit(const DecodeArgs &a, int total, int L, int row)
-{
-    if (!a.causal) return L;
-    int t = row / a.heads;
-    t = t < a.k_tokens - 1 ? t : a.k_tokens - 1;   // rows past M: any limit will do
-    const int n = shard_count(a, total - a.k_tokens + t + 1);
-    return n < L ? n : L;
-}
-
-// s_waitcnt immediates for gfx9: vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
-constexpr int waitcnt_imm(int vm, int lgkm)
-{
-    return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | ((lgkm & 0xF) << 8);
-}
-
-__device__ __forceinline__ void wait_pages_then_barrier(int pages_after)
-{
-    // Every wave waits for its own page DMAs except the `pages_after` newest pages, and
-    // for its LDS traffic, then the workgroup meets.  No release fence: it would also
-    // wait for the in-flight prefetch.
-    if (pages_after >= 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kChunksPerWave, 0));
-    else if (pages_after == 1)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(kChunksPerWave, 0));
-    else
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    asm volatile("s_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-    asm volatile("s_barrier" ::: "memory");
-}
-
-// LDS page layout: token row t occupies bytes [576t, 576t+576) of its slot, and within
-// the row the 16-byte chunk c is stored at chunk position c ^ ((t >> 2) & 3).  Rows are
-// 576 B apart, so without the swizzle 16 lanes reading one chunk of 16 consecutive rows
-// hit only 4 of the 16 bank groups; with it they hit all 16, and so do the transposed V
-// reads (8 keys x 2 chunks per 16 lanes).
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
-
-// One wave's 9 KiB share of a page, HBM -> LDS (global_load_lds_dwordx4: lane i's 16 bytes
-// land at M0 + 16*i, the source is the page base in SGPRs plus the lane's offset).  LDS
-// chunk position p of the slot receives the page's chunk (p / 36, (p % 36) ^ swz(p / 36));
-// the per-lane source offsets are the same for every page and are computed once.  Issued as
-// inline asm so that the compiler does not count these loads (it would otherwise wait for
-// all of them before every transposed LDS read); completion is awaited explicitly with
-// s_waitcnt vmcnt before the barrier that publishes a page.  The s_nop covers the
-// SALU-write-M0 -> LDS-DMA hazard.  M0 is not listed as clobbered (clang reserves it); no
-// compiler-generated code in these kernels reads M0.
-struct DmaOffsets {
-    uint32_t v[(kChunksPerWave + 1) / 2];   // two 16-bit offsets per register
-    __device__ __forceinline__ uint32_t get(int i) const
-    {
-        return (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xFFFFu);
-    }
-};
-
-__device__ __forceinline__ DmaOffsets dma_offsets(int wave, int lane)
-{
-    DmaOffsets o;
-#pragma unroll
-    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) o.v[i] = 0;
-#pragma unroll
-    for (int i = 0; i < kChunksPerWave; ++i) {
-        const int p = (wave * kChunksPerWave + i) * 64 + lane;
-        const int row = p / (kKDim / 16), q = p - row * (kKDim / 16);
-        o.v[i >> 1] |= (uint32_t)(row * kKDim + 16 * (q ^ swz(row))) << (16 * (i & 1));
-    }
-    return o;
-}
-
-// A wave-uniform pointer, pinned to scalar registers for an inline-asm "s" operand.
-__device__ __forceinline__ const uint8_t *uniform_ptr(const uint8_t *p)
-{
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ void issue_page(const uint8_t *page_base, uint32_t lds_dst,
-                                           const DmaOffsets &o)
-{
-    page_base = uniform_ptr(page_base);
-    lds_dst = __builtin_amdgcn_readfirstlane(lds_dst);
-    asm volatile(
-        "s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o2], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o3], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o4], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x1400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o5], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x1800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o6], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x1c00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o7], %[b]\n\t"
-        "s_add_u32 m0, %[m], 0x2000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o8], %[b]"
-        :
-        : [o0] "v"(o.get(0)), [o1] "v"(o.get(1)), [o2] "v"(o.get(2)), [o3] "v"(o.get(3)),
-          [o4] "v"(o.get(4)), [o5] "v"(o.get(5)), [o6] "v"(o.get(6)), [o7] "v"(o.get(7)),
-          [o8] "v"(o.get(8)), [b] "s"(page_base), [m] "s"(lds_dst)
-        : "memory");
-}
-static_assert(kChunksPerWave == 9, "issue_page is written for 9 DMA instructions per wave");
-
-// A work unit's Q rows (MT rows x 576 B, contiguous in q) HBM -> LDS at `lds_dst`, same
-// layout; chunks of rows at or past `valid_rows` are not loaded.
-template <int MT>
-__device__ __forceinline__ void issue_q(const uint8_t *q_rows, uint32_t lds_dst, int valid_rows,
-                                        int wave, int lane)
-{
-    constexpr int kChunks = MT * (kKDim / 16);
-    constexpr int kPerWave = (kChunks / 4 + 63) / 64;
-    static_assert(kChunks * 16 <= kPageBytes, "Q rows must fit one ring slot");
-    q_rows = uniform_ptr(q_rows);
-    lds_dst = __builtin_amdgcn_readfirstlane(lds_dst);
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int p = (wave * kPerWave + i) * 64 + lane;
-        if (p < kChunks && p < valid_rows * (kKDim / 16)) {
-            asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o], %[b]"
-                         :
-                         : [o] "v"(p * 16), [b] "s"(q_rows),
-                           [m] "s"(lds_dst + (uint32_t)((wave * kPerWave + i) * 1024))
-                         : "memory");
-        }
-    }
-}
-
-__device__ __forceinline__ v8i lds_read2x16(const uint8_t *p0, const uint8_t *p1)
-{
-    const v4i a = *(const v4i *)p0;
-    const v4i b = *(const v4i *)p1;
-    return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// Lanes l and l ^ 32 hold the two key halves of one row: v_permlane32_swap gives every
-// lane both values.
-__device__ __forceinline__ float half_pair_max(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float half_pair_sum(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ v2i lds_read_tr8(const uint8_t *p)
-{
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i *)p);
-}
-
-// blockIdx -> virtual worker: hardware hands workgroups to the 8 XCDs round-robin, so
-// virtual workers v and v+1 (the row tiles of one split) are put on the same XCD and
-// share its L2.
-__device__ __forceinline__ int virtual_worker(int b, int W, int mt)
-{
-    // with one row tile per split there is nothing to share: workgroups take the list in
-    // order, so those that start first (and those started as CUs free up) take the
-    // longest items
-    if (mt == 1 || W % 8 != 0) return b;
-    return (b % 8) * (W / 8) + b / 8;
-}
-
-__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c)
-{
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// 128-row tiles, paired waves sharing each page: wave w computes the scores, running
-// max/sum and P of row block w; it accumulates O^T for the rows of blocks {2p, 2p+1}
-// (p = w/2) and the dims [256h, +256) (h = w%2), so every V^T fragment read from LDS feeds
-// two MFMAs.  Partners (w, w^1) swap P, the per-row rescale factor and a rescale flag
-// through LDS each page.  The DMA of page t+3 goes into the slot page t-1 used.  Read-only
-// inputs are separate __restrict__ arguments; their uniform reads go through the constant
-// address space (scalar loads, which do not wait on the in-flight page DMAs).
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
-    const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
-    const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
-    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
-    float *__restrict__ lse_out, DecodeArgs a)
-{
-    constexpr int MT = 128;          // rows per work unit
-    constexpr int NT = 16;           // accumulator tiles per wave: 2 row blocks x 8 dim tiles
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
-    // per wave: its P fragment (64 lanes x 32 B), per-row rescale factor, rescale flag
-    __shared__ __attribute__((aligned(16))) int32_t xch_p[4][64 * 8];
-    __shared__ float xch_alpha[4][32];
-    __shared__ int32_t xch_flag[4];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, half = lane >> 5;
-    const int R = a.reqs, M = a.rows;
-    const int mt = ceil_div(M, MT);
-    const int W = a.workers;
-
-    // The plan summary, the item count and the first unit's work pair do not depend on
-    // each other, so they are loaded together and their latencies overlap.  The pair is
-    // inside the list: its item is below W and list_len >= 2 * (reqs + 2 * workers).
-    const int vw = virtual_worker(blockIdx.x, W, mt);
-    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
-    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
-    const int h_reqs = ldc(&header[kHdrReqs]);
-    const int n_items = ldc(&offsets[R]);
-    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
-    // consume every value here so that the compiler cannot sink a load past the checks
-    // below (it would otherwise chain them one behind the other)
-    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
-                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
-                 "s"(lengths), "s"(counts));
-    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
-        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-        return;
-    }
-    const int units = n_items * mt;
-
-    const DmaOffsets dmao = dma_offsets(wave, lane);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
-
-    // V^T fragment reads (ds_read_b64_tr_b8): within each 16-lane group, source lane i
-    // supplies key row b = i/2 and dims [8*(i%2), +8) of a 16-dim column block.  Keys are
-    // tr_key + 16*w2; dims [32*tile + 16*(g16&1) + 8*(i16&1), +8) lie in chunk
-    // 2*tile + (g16&1), swizzled by the key row (the same for the four w2 rows).
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
-    int tr_off[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1);
-    // K fragment reads: row l32 (+32 per key block), chunks 4k + 2*half + e, e = 0, 1
-    int k_off[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
-
-    for (int u = vw; u < units; u += W) {
-        const int item = u / mt, jt = u - item * mt;
-        const int r = u == vw ? r_first : ldc(&work[2 * item]);
-        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
-        // the request's count, length and slot offset, loaded together (index clamped so
-        // that the loads stay in bounds before r is checked)
-        const int rc = r >= 0 && r < R ? r : 0;
-        const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
-        const int total = a.causal ? ldc(&a.totals[rc]) : L;
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
-        const int pages = ceil_div(L, kPage);
-        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
-        const int first = s * q + (s < rem ? s : rem);
-        const int size = q + (s < rem ? 1 : 0);
-        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
-            off_r + s >= n_items) {
-            if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-            continue;
-        }
-        if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
-            atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
-        const int row0 = jt * MT + 32 * wave;   // this wave's score rows
-        const int lim = row_key_limit(a, total, L, row0 + l32);   // keys this lane's row sees
-        const bool active = row0 < M;
-        const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
-
-        v8i qf[9];   // Q^T fragments, loaded below once the first pages are in flight
-
-        bool page_bad = false;
-        auto page_at = [&](int32_t pid) {
-            if (pid < 0 || pid >= a.pool_pages) {
-                page_bad = true;
-                pid = 0;
-            }
-            return kv_in + (int64_t)pid * kPageBytes;
-        };
-        // block-table entry of page min(t, size - 1)
-        auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
-        // keys past the request's length (only on its last page): zero the rows in LDS so
-        // that P*V stays finite; scores there are masked by key index
-        auto zero_tail = [&](int t) {
-            const int valid = L - (first + t) * kPage;
-            if (valid < kPage) {
-                uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-                for (int off = valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
-                    *(v4i *)(slot + off) = v4i{0, 0, 0, 0};
-                lds_barrier();
-            }
-        };
-
-        // l_run: row sum of the FP32 P (for the LSE); lq_run: of the E4M3 P that the MMA
-        // uses (O is normalised by it, so the weights of the output rows sum to one)
-        float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
-        v16f acc[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
-        v16f sc[2];          // the scores of the page
-
-        // S^T[64 keys x 32 rows] of the page in `slot`: 9 MFMAs per 32-key block, each fed
-        // by two 16-byte LDS reads of a key row.  Step j issues the reads of fragment j+2,
-        // then MFMA j, then `valu(j)` (other work to overlap with the MFMA); a scheduling
-        // fence after each step keeps that order, so the reads stay two MFMAs ahead.
-        auto scores = [&](const uint8_t *slot, v16f (&out)[2], auto &&valu) {
-            const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
-            out[0] = v16f{0};
-            out[1] = v16f{0};
-            v8i kf0 = lds_read2x16(kp0, kp1);
-            v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < 18; ++j) {
-                const int b = j / 9, k = j % 9;
-                const v8i cur = (j & 1) ? kf1 : kf0;
-                if (j + 2 < 18) {
-                    const int o = 32 * ((j + 2) / 9) * kKDim + 64 * ((j + 2) % 9);
-                    if (j & 1)
-                        kf1 = lds_read2x16(kp0 + o, kp1 + o);
-                    else
-                        kf0 = lds_read2x16(kp0 + o, kp1 + o);
-                }
-                out[b] = mfma(cur, qf[k], out[b]);
-                valu(j);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        // P = 2^(s*scale - m + kPScale): FP32 into the row sum, E4M3 into the P^T operand;
-        // lane (l32, half) byte 16b + e holds key 32b + 8(e/4) + 4*half + e%4.  Group g of 8
-        // makes fragment dword g (four keys).
-        v8i pf;
-        float psum = 0.f, qsum = 0.f, bias = 0.f;
-        auto probs_begin = [&]() {
-            bias = m_run == -INFINITY ? 0.f : kPScale - m_run;   // no key seen: P = 0
-            psum = 0.f;
-            qsum = 0.f;
-        };
-        auto probs_group = [&](const v16f (&sv)[2], int g) {
-            const int b = g >> 2, qd = g & 3;
-            float p[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[b][4 * qd + e], a.score_scale, bias));
-                psum += p[e];
-            }
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-            pf[g] = w;
-            const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-            const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-            qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
-        };
-        auto probs_end = [&]() {
-            l_run += psum;
-            lq_run += qsum;
-        };
-        // The first pages' block-table entries, loaded together.
-        int32_t pid0[kSlots - 1];
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
-        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
-        // the entry of the next page to fetch, read one fetch ahead
-        int32_t pid_next = page_id(kSlots - 1);
-        // The first pages' DMA, then the Q^T fragments from global memory, so that
-        // both latencies overlap; then wait for all of it (the compiler tracks the Q
-        // loads, not the DMA).
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d)
-            if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
-        const int row = row0 + l32;
-        if (row < M) {
-            const uint8_t *qp = q_in + ((size_t)r * M + row) * kKDim + 32 * half;
-#pragma unroll
-            for (int k = 0; k < 9; ++k) {
-                const v4i x = *(const v4i *)(qp + 64 * k);
-                const v4i y = *(const v4i *)(qp + 64 * k + 16);
-                qf[k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        wait_pages_then_barrier(0);
-
-        auto no_valu = [](int) {};
-        // 128-row tiles, paired waves.  Wave w computes the scores, running max/sum and
-        // P of row block w; it owns O for the 64 rows of blocks {2p, 2p+1} (p = w/2) and
-        // the 256 dims [256*hw, +256) (hw = w%2).  Partners (w, w^1) swap their P
-        // fragments and rescale factors through LDS each page, so every V^T fragment
-        // read from LDS feeds two MFMAs (one per row block).
-        const int hw = wave & 1, pair = wave >> 1;
-        const bool o_active = jt * MT + 64 * pair < M;
-        // acc[n]: own row block (2p + hw), acc[8 + n]: the partner's (2p + 1 - hw);
-        // dim tile 8*hw + n in both
-        for (int t = 0; t < size; ++t) {
-            const int after = size - 1 - t;
-            wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
-            if (t + kSlots - 1 < size) {
-                issue_page(page_at(pid_next),
-                           lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
-                pid_next = page_id(t + kSlots);
-            }
-            zero_tail(t);
-            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-            float alpha = 1.f;
-            bool any_grow = false;
-            pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            if (active) {
-                scores(slot, sc, no_valu);
-                const int valid = lim - (first + t) * kPage;   // keys of the page the row sees
-                if (__any(valid < kPage)) {
-#pragma unroll
-                    for (int b = 0; b < 2; ++b)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid)
-                                sc[b][e] = -INFINITY;
-                }
-                float smax = -INFINITY;
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
-                const float mx = half_pair_max(smax) * a.score_scale;
-                const bool grow = mx > m_run + kTau;
-                any_grow = __any(grow);
-                if (any_grow) {
-                    const float m_new = grow ? mx : m_run;
-                    // rows whose max stays keep factor 1 (exp2(m - m) would be NaN for a
-                    // row that has seen no key yet, m = -inf)
-                    alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-                    l_run *= alpha;
-                    lq_run *= alpha;
-                    m_run = m_new;
-                }
-                probs_begin();
-#pragma unroll
-                for (int g = 0; g < 8; ++g) probs_group(sc, g);
-                probs_end();
-            }
-            // swap with the partner: P fragment, per-row rescale factor, rescale flag
-            *(v8i *)&xch_p[wave][lane * 8] = pf;
-            if (half == 0) xch_alpha[wave][l32] = alpha;
-            if (lane == 0) xch_flag[wave] = any_grow ? 1 : 0;
-            lds_barrier();
-            if (!o_active) continue;
-            const v8i pf_other = *(const v8i *)&xch_p[wave ^ 1][lane * 8];
-            const float alpha_other = xch_alpha[wave ^ 1][l32];
-            const bool grow_other = xch_flag[wave ^ 1] != 0;
-            if (any_grow) {
-#pragma unroll
-                for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-            }
-            if (grow_other) {
-#pragma unroll
-                for (int n = 0; n < 8; ++n) acc[8 + n] *= alpha_other;
-            }
-            const uint8_t *vp0 = slot + tr_off[0] + 64 * (4 * hw);
-            const uint8_t *vp1 = slot + tr_off[1] + 64 * (4 * hw);
-            auto vtile = [&](int n) {
-                v8i f;
-                const uint8_t *vp = (n & 1) ? vp1 : vp0;
-#pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
-                    f[2 * w2] = x[0];
-                    f[2 * w2 + 1] = x[1];
-                }
-                return f;
-            };
-            v8i vf = vtile(0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const v8i cur = vf;
-                if (n + 1 < 8) vf = vtile(n + 1);
-                acc[n] = mfma(cur, pf, acc[n]);
-                acc[8 + n] = mfma(cur, pf_other, acc[8 + n]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
-
-        // epilogue: normalise and store this split's FP32 partial and log2 LSE.
-        // l_run is scaled by 2^kPScale like P, so the scale cancels in O / l.
-        const size_t slot_idx = (size_t)off_r + s;
-        const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
-        if (half == 0) xch_alpha[wave][l32] = lq_tot;
-        lds_barrier();
-        const float lq_other = xch_alpha[wave ^ 1][l32];
-        if (active && half == 0 && row0 + l32 < M)
-            lse_out[slot_idx * M + row0 + l32] = m_run + __builtin_amdgcn_logf(l_tot) - kPScale;
-#pragma unroll
-        for (int own = 1; own >= 0; --own) {
-            const int row = jt * MT + 32 * (2 * pair + (own ? hw : 1 - hw)) + l32;
-            if (row < M) {
-                float *po = partial + (slot_idx * M + row) * kVDim;
-                const float lq = own ? lq_tot : lq_other;
-                const float inv = lq > 0.f ? a.out_scale / lq : 0.f;   // no key: O = 0
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int dim = 32 * (8 * hw + n) + 4 * half;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const v16f &t16 = acc[(own ? 0 : 8) + n];
-                        const v4f o = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2],
-                                          t16[4 * q4 + 3]} * inv;
-                        *(v4f *)(po + dim + 8 * q4) = o;
-                    }
-                }
-            }
-        }
-
-        lds_barrier();  // the next unit's prologue overwrites the ring
-    }
-}
-
-
-// 32-row tiles, wave pairs on alternate pages.  Pair p (waves 2p, 2p+1) computes the pages
-// t = p (mod 2) of the split: both waves of the pair compute the page's scores for all 32
-// rows and the same P, and wave 2p+h accumulates O^T for the dims [256h, +256).  Each page's
-// scores are computed twice instead of four times (once per wave of a shared page stream),
-// which halves the MFMA and LDS work per page.  The two pairs' (max, sum, O) are merged
-// through LDS at the end of the unit.  Per iteration: pages 2i and 2i+1 are computed while
-// pages 2i+2 and 2i+3 are fetched into the other two ring slots.
-constexpr int kMergeStride = kVDim / 2 + 4;   // floats per row of a merge region (+16 B pad)
-static_assert(4 * 32 * kMergeStride * 4 <= kSlots * kPageBytes, "merge regions must fit the ring");
-
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode32_kernel(
-    const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
-    const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
-    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
-    float *__restrict__ lse_out, DecodeArgs a)
-{
-    constexpr int MT = 32;
-    constexpr int NT = kVDim / 64;   // 8 output tiles of 32 dims per wave
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
-    __shared__ float xm[2][32], xl[2][32], xq[2][32];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave >> 1, hw = wave & 1;
-    const int l32 = lane & 31, half = lane >> 5;
-    const int R = a.reqs, M = a.rows;
-    const int mt = ceil_div(M, MT);
-    const int W = a.workers;
-
-    // plan summary, item count and the first unit's work pair, loaded together (see
-    // decode_kernel)
-    const int vw = virtual_worker(blockIdx.x, W, mt);
-    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
-    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
-    const int h_reqs = ldc(&header[kHdrReqs]);
-    const int n_items = ldc(&offsets[R]);
-    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
-    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
-                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
-                 "s"(lengths), "s"(counts));
-    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
-        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-        return;
-    }
-    const int units = n_items * mt;
-
-    const DmaOffsets dmao = dma_offsets(wave, lane);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
-
-    // V^T fragment reads of this wave's tile n (dims 256*hw + 32n): vp[n & 1] + 64 * (n >> 1)
-    // (layout as in decode_kernel)
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
-    int tr_off[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1) +
-                      64 * (hw * NT / 2);
-    int k_off[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
-
-    for (int u = vw; u < units; u += W) {
-        const int item = u / mt, jt = u - item * mt;
-        const int r = u == vw ? r_first : ldc(&work[2 * item]);
-        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
-        const int rc = r >= 0 && r < R ? r : 0;
-        const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
-        const int total = a.causal ? ldc(&a.totals[rc]) : L;
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
-        const int pages = ceil_div(L, kPage);
-        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
-        const int first = s * q + (s < rem ? s : rem);
-        const int size = q + (s < rem ? 1 : 0);
-        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
-            off_r + s >= n_items) {
-            if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-            continue;
-        }
-        if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
-            atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
-        const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
-        const int row = jt * MT + l32;
-        const int lim = row_key_limit(a, total, L, row);   // keys this lane's row sees
-
-        bool page_bad = false;
-        auto page_at = [&](int32_t pid) {
-            if (pid < 0 || pid >= a.pool_pages) {
-                page_bad = true;
-                pid = 0;
-            }
-            return kv_in + (int64_t)pid * kPageBytes;
-        };
-        auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
-        auto issue = [&](int t, int32_t pid) {
-            issue_page(page_at(pid), lds_base + (t % kSlots) * kPageBytes, dmao);
-        };
-
-        // Prologue: the unit's Q rows by DMA into the last ring slot, pages 0..2 into the
-        // others; once Q and pages 0, 1 are in, every wave reads its Q^T fragments (lane
-        // (row l32, half) holds dims [64k + 32*half, +32)), and page 3 then takes the slot.
-        int32_t pid0[kSlots];
-#pragma unroll
-        for (int d = 0; d < kSlots; ++d) pid0[d] = page_id(d);
-        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]), "s"(pid0[3]));
-        issue_q<MT>(q_in + ((size_t)r * M + (size_t)jt * MT) * kKDim,
-                    (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + (kSlots - 1) * kPageBytes, M - jt * MT,
-                    wave, lane);
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d)
-            if (d < size) issue(d, pid0[d]);
-        int32_t pid_a = page_id(kSlots), pid_b = page_id(kSlots + 1);
-        wait_pages_then_barrier(size > 2 ? 1 : 0);
-        v8i qf[9];
-        {
-            // the lane index is re-read here rather than kept live across the unit loop
-            int ln;
-            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-            const uint8_t *qs = lds + (kSlots - 1) * kPageBytes + (ln & 31) * kKDim + 32 * (ln >> 5);
-            const bool row_ok = jt * MT + (ln & 31) < M;
-#pragma unroll
-            for (int k = 0; k < 9; ++k) {
-                const v8i x = lds_read2x16(qs + 64 * k, qs + 64 * k + 16);
-                qf[k] = row_ok ? x : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-        lds_barrier();  // every wave has its Q^T: page 3 may overwrite it
-        if (kSlots - 1 < size) issue(kSlots - 1, pid0[kSlots - 1]);
-
-        // l_run: row sum of the FP32 P (for the LSE); lq_run: of the E4M3 P that the MMA
-        // uses (O is normalised by it, so the weights of the output rows sum to one)
-        float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
-        v16f acc[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
-
-        for (int t0 = 0; t0 < size; t0 += 2) {
-            if (t0 > 0) {
-                // pages t0, t0+1 resident (nothing newer in flight); every wave is past
-                // pages t0-2, t0-1, whose slots take pages t0+2, t0+3
-                wait_pages_then_barrier(0);
-                if (t0 + 2 < size) issue(t0 + 2, pid_a);
-                if (t0 + 3 < size) issue(t0 + 3, pid_b);
-                pid_a = page_id(t0 + 4);
-                pid_b = page_id(t0 + 5);
-            }
-            // keys past the request's length (its last page only): zero their rows so that
-            // P V stays finite; their scores are masked by key index below
-            const int last_valid = L - (first + (t0 + 1 < size ? t0 + 1 : t0)) * kPage;
-            if (last_valid < kPage) {
-                const int tz = t0 + 1 < size ? t0 + 1 : t0;
-                uint8_t *zs = lds + (tz % kSlots) * kPageBytes;
-                for (int off = last_valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
-                    *(v4i *)(zs + off) = v4i{0, 0, 0, 0};
-                lds_barrier();
-            }
-            const int t = t0 + pair;
-            if (t >= size) continue;
-            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-            const int valid = lim - (first + t) * kPage;   // keys of the page the row sees
-
-            // S^T[64 keys x 32 rows]: 18 MFMAs, K fragment reads two ahead
-            v16f sc[2];
-            {
-                const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
-                sc[0] = v16f{0};
-                sc[1] = v16f{0};
-                v8i kf0 = lds_read2x16(kp0, kp1);
-                v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < 18; ++j) {
-                    const int b = j / 9, k = j % 9;
-                    const v8i cur = (j & 1) ? kf1 : kf0;
-                    if (j + 2 < 18) {
-                        const int o = 32 * ((j + 2) / 9) * kKDim + 64 * ((j + 2) % 9);
-                        if (j & 1)
-                            kf1 = lds_read2x16(kp0 + o, kp1 + o);
-                        else
-                            kf0 = lds_read2x16(kp0 + o, kp1 + o);
-                    }
-                    sc[b] = mfma(cur, qf[k], sc[b]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            // page max (masked), lazy running max and O rescale
-            if (__any(valid < kPage)) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sc[b][e] = -INFINITY;
-            }
-            float smax = -INFINITY;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
-            const float mx = half_pair_max(smax) * a.score_scale;
-            const bool grow = mx > m_run + kTau;
-            if (__any(grow)) {
-                const float m_new = grow ? mx : m_run;
-                // rows whose max stays keep factor 1 (exp2(m - m) would be NaN for a
-                // row that has seen no key yet, m = -inf)
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-                l_run *= alpha;
-                lq_run *= alpha;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-                m_run = m_new;
-            }
-            // P = 2^(s*scale - m + kPScale): FP32 into the row sum, E4M3 into P^T
-            v8i pf;
-            {
-                const float bias = m_run == -INFINITY ? 0.f : kPScale - m_run;   // no key seen: P = 0
-                float psum = 0.f, qsum = 0.f;
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    const int b = g >> 2, qd = g & 3;
-                    float p4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        p4[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][4 * qd + e], a.score_scale, bias));
-                        psum += p4[e];
-                    }
-                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
-                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
-                    pf[g] = w4;
-                    const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, false);
-                    const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
-                    qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
-                }
-                l_run += psum;
-                lq_run += qsum;
-            }
-            // O^T += V^T P^T over this wave's 8 tiles, transposed V reads one tile ahead
-            {
-                const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
-                auto vtile = [&](int n) {
-                    v8i f;
-                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
-                        f[2 * w2] = x[0];
-                        f[2 * w2 + 1] = x[1];
-                    }
-                    return f;
-                };
-                v8i vf = vtile(0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    const v8i cur = vf;
-                    if (n + 1 < NT) vf = vtile(n + 1);
-                    acc[n] = mfma(cur, pf, acc[n]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-        if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
-
-        // merge the two pairs: m = max_p m_p, l = sum_p l_p 2^(m_p - m) (likewise lq) and
-        // O = sum_p O_p 2^(m_p - m) / lq (the sums carry P's 2^kPScale, which cancels)
-        const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
-        if (hw == 0 && half == 0) {
-            xm[pair][l32] = m_run;
-            xl[pair][l32] = l_tot;
-            xq[pair][l32] = lq_tot;
-        }
-        lds_barrier();  // also: every wave is done with the ring
-        const float m0 = xm[0][l32], m1 = xm[1][l32];
-        const float m_all = fmaxf(m0, m1);
-        const float e0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m_all);
-        const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_all);
-        const float l_all = xl[0][l32] * e0 + xl[1][l32] * e1;
-        const float lq_all = xq[0][l32] * e0 + xq[1][l32] * e1;
-        const float f_own =
-            m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_all) * (a.out_scale / lq_all);
-        const size_t slot_idx = (size_t)off_r + s;
-        if (wave == 0 && half == 0 && row < M)
-            lse_out[slot_idx * M + row] = m_all + __builtin_amdgcn_logf(l_all) - kPScale;
-        // every wave stores its scaled O (32 rows x 256 dims) in region `wave`; then wave w
-        // adds dims [128w, +128) of the two pairs' regions and stores them
-        float *const region = (float *)(void *)lds;
-        {
-            float *mine = region + wave * (32 * kMergeStride) + l32 * kMergeStride + 4 * half;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *(v4f *)(mine + 32 * n + 8 * q4) =
-                        v4f{acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2], acc[n][4 * q4 + 3]} * f_own;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        lds_barrier();
-        {
-            const int hsel = wave >> 1, dbase = 128 * (wave & 1);
-            const float *r0 = region + hsel * (32 * kMergeStride);         // pair 0, half hsel
-            const float *r1 = region + (2 + hsel) * (32 * kMergeStride);   // pair 1, half hsel
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int f = i * 64 + lane, rr = f >> 5, d = dbase + 4 * (f & 31);
-                const v4f sum = *(const v4f *)(r0 + rr * kMergeStride + d) +
-                                *(const v4f *)(r1 + rr * kMergeStride + d);
-                if (jt * MT + rr < M)
-                    *(v4f *)(partial + (slot_idx * M + jt * MT + rr) * kVDim + 256 * hsel + d) = sum;
-            }
-        }
-        lds_barrier();  // the next unit's pages overwrite the regions
-    }
-}
-
-// 64-row tiles, wave pairs on alternate pages.  Pair p (waves 2p, 2p+1) computes the pages
-// t = p (mod 2) of the split for all 64 rows: wave 2p+h computes the scores, running
-// max/sum and P of row block h and accumulates O^T for both row blocks and the dims
-// [256h, +256), so every V^T fragment read from LDS feeds two MFMAs; the partners swap P,
-// the per-row rescale factor and a rescale flag through LDS.  Each page's scores are
-// computed once (with one shared page stream the two waves of each row block would both
-// compute them).  At the end the two pairs' (max, sum, O) are merged through LDS: pair p
-// merges and stores row block p.
-__global__ __launch_bounds__(kDecodeThreads, 1) void decode64_kernel(
-    const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
-    const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
-    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
-    float *__restrict__ lse_out, DecodeArgs a)
-{
-    constexpr int MT = 64;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
-    __shared__ __attribute__((aligned(16))) int32_t xch_p[4][64 * 8];  // per wave: its P fragment
-    __shared__ float xch_alpha[4][32];                                  // per-row rescale factor
-    __shared__ int32_t xch_flag[4];                                     // any row rescaled
-    __shared__ float xm[2][2][32], xl[2][2][32], xq[2][2][32];          // [pair][block][row]
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave >> 1, hw = wave & 1;
-    const int l32 = lane & 31, half = lane >> 5;
-    const int R = a.reqs, M = a.rows;
-    const int mt = ceil_div(M, MT);
-    const int W = a.workers;
-
-    const int vw = virtual_worker(blockIdx.x, W, mt);
-    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
-    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
-    const int h_reqs = ldc(&header[kHdrReqs]);
-    const int n_items = ldc(&offsets[R]);
-    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
-    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
-                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
-                 "s"(lengths), "s"(counts));
-    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
-        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-        return;
-    }
-    const int units = n_items * mt;
-
-    const DmaOffsets dmao = dma_offsets(wave, lane);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
-    const int g16 = lane >> 4, i16 = lane & 15;
-    const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
-    int tr_off[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-        tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1) +
-                      64 * (4 * hw);
-    int k_off[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
-
-    for (int u = vw; u < units; u += W) {
-        const int item = u / mt, jt = u - item * mt;
-        const int r = u == vw ? r_first : ldc(&work[2 * item]);
-        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
-        const int rc = r >= 0 && r < R ? r : 0;
-        const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
-        const int total = a.causal ? ldc(&a.totals[rc]) : L;
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
-        const int pages = ceil_div(L, kPage);
-        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
-        const int first = s * q + (s < rem ? s : rem);
-        const int size = q + (s < rem ? 1 : 0);
-        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
-            off_r + s >= n_items) {
-            if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-            continue;
-        }
-        if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
-            atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
-        const int row0 = jt * MT + 32 * hw;     // this wave's score rows (block hw)
-        const int lim = row_key_limit(a, total, L, row0 + l32);   // keys this lane's row sees
-        const bool active = row0 < M;
-        const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
-
-        bool page_bad = false;
-        auto page_at = [&](int32_t pid) {
-            if (pid < 0 || pid >= a.pool_pages) {
-                page_bad = true;
-                pid = 0;
-            }
-            return kv_in + (int64_t)pid * kPageBytes;
-        };
-        auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
-
-        // the first pages' DMA, then the Q^T fragments of the score rows; wait for all of
-        // it (the compiler tracks the Q loads, not the DMA)
-        int32_t pid0[kSlots - 1];
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
-        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d)
-            if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
-        int32_t pid_a = page_id(kSlots - 1), pid_b = page_id(kSlots);
-        v8i qf[9];
-        if (active && row0 + l32 < M) {
-            const uint8_t *qp = q_in + ((size_t)r * M + row0 + l32) * kKDim + 32 * half;
-#pragma unroll
-            for (int k = 0; k < 9; ++k) {
-                const v4i x = *(const v4i *)(qp + 64 * k);
-                const v4i y = *(const v4i *)(qp + 64 * k + 16);
-                qf[k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 9; ++k) qf[k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        wait_pages_then_barrier(0);
-
-        // l_run: row sum of the FP32 P (for the LSE); lq_run: of the E4M3 P that the MMA
-        // uses (O is normalised by it, so the weights of the output rows sum to one)
-        float m_run = -INFINITY, l_run = 0.f, lq_run = 0.f;
-        v16f acc[16];   // [0, 8): row block hw, [8, 16): block 1 - hw; dim tile 8*hw + n
-#pragma unroll
-        for (int n = 0; n < 16; ++n) acc[n] = v16f{0};
-
-        for (int t0 = 0; t0 < size; t0 += 2) {
-            if (t0 > 0) {
-                // pages t0, t0+1 resident; every wave is past pages t0-2, t0-1, whose slots
-                // take pages t0+2, t0+3 (page 3 goes into slot 3, untouched so far)
-                wait_pages_then_barrier(0);
-                if (t0 + 2 < size) {
-                    issue_page(page_at(pid_a), lds_base + ((t0 + 2) % kSlots) * kPageBytes, dmao);
-                    pid_a = page_id(t0 + 4);
-                }
-                if (t0 + 3 < size) {
-                    issue_page(page_at(pid_b), lds_base + ((t0 + 3) % kSlots) * kPageBytes, dmao);
-                    pid_b = page_id(t0 + 5);
-                }
-            } else if (kSlots - 1 < size) {
-                // page 3 into the free fourth slot
-                issue_page(page_at(pid_a), lds_base + (kSlots - 1) * kPageBytes, dmao);
-                pid_a = page_id(kSlots + 1);
-                // (pid_b already holds page 4's entry, fetched at the next iteration)
-                const int32_t swap = pid_a;
-                pid_a = pid_b;
-                pid_b = swap;
-            }
-            // keys past the request's length (its last page only): zero their rows so that
-            // P V stays finite; their scores are masked by key index below
-            const int tz = t0 + 1 < size ? t0 + 1 : t0;
-            const int last_valid = L - (first + tz) * kPage;
-            if (last_valid < kPage) {
-                uint8_t *zs = lds + (tz % kSlots) * kPageBytes;
-                for (int off = last_valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
-                    *(v4i *)(zs + off) = v4i{0, 0, 0, 0};
-                lds_barrier();
-            }
-            const int t = t0 + pair;
-            const bool has = t < size;
-            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-            float alpha = 1.f;
-            bool any_grow = false;
-            v8i pf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            if (has && active) {
-                // S^T[64 keys x 32 rows]: 18 MFMAs, K fragment reads two ahead
-                v16f sc[2];
-                const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
-                sc[0] = v16f{0};
-                sc[1] = v16f{0};
-                v8i kf0 = lds_read2x16(kp0, kp1);
-                v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < 18; ++j) {
-                    const int b = j / 9, k = j % 9;
-                    const v8i cur = (j & 1) ? kf1 : kf0;
-                    if (j + 2 < 18) {
-                        const int o = 32 * ((j + 2) / 9) * kKDim + 64 * ((j + 2) % 9);
-                        if (j & 1)
-                            kf1 = lds_read2x16(kp0 + o, kp1 + o);
-                        else
-                            kf0 = lds_read2x16(kp0 + o, kp1 + o);
-                    }
-                    sc[b] = mfma(cur, qf[k], sc[b]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                const int valid = lim - (first + t) * kPage;   // keys of the page the row sees
-                if (__any(valid < kPage)) {
-#pragma unroll
-                    for (int b = 0; b < 2; ++b)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e)
-                            if (32 * b + 8 * (e >> 2) + 4 * half + (e & 3) >= valid) sc[b][e] = -INFINITY;
-                }
-                float smax = -INFINITY;
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[b][e]);
-                const float mx = half_pair_max(smax) * a.score_scale;
-                const bool grow = mx > m_run + kTau;
-                any_grow = __any(grow);
-                if (any_grow) {
-                    const float m_new = grow ? mx : m_run;
-                    // rows whose max stays keep factor 1 (exp2(m - m) would be NaN for a
-                    // row that has seen no key yet, m = -inf)
-                    alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-                    l_run *= alpha;
-                    lq_run *= alpha;
-                    m_run = m_new;
-                }
-                const float bias = m_run == -INFINITY ? 0.f : kPScale - m_run;   // no key seen: P = 0
-                float psum = 0.f, qsum = 0.f;
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    const int b = g >> 2, qd = g & 3;
-                    float p4[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        p4[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][4 * qd + e], a.score_scale, bias));
-                        psum += p4[e];
-                    }
-                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
-                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
-                    pf[g] = w4;
-                    const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, false);
-                    const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
-                    qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
-                }
-                l_run += psum;
-                lq_run += qsum;
-            }
-            // swap with the partner: P fragment, per-row rescale factor, rescale flag
-            *(v8i *)&xch_p[wave][lane * 8] = pf;
-            if (half == 0) xch_alpha[wave][l32] = alpha;
-            if (lane == 0) xch_flag[wave] = any_grow ? 1 : 0;
-            lds_barrier();
-            if (has) {
-                const v8i pf_other = *(const v8i *)&xch_p[wave ^ 1][lane * 8];
-                const float alpha_other = xch_alpha[wave ^ 1][l32];
-                const bool grow_other = xch_flag[wave ^ 1] != 0;
-                if (any_grow) {
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) acc[n] *= alpha;
-                }
-                if (grow_other) {
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) acc[8 + n] *= alpha_other;
-                }
-                const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
-                auto vtile = [&](int n) {
-                    v8i f;
-                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
-                        f[2 * w2] = x[0];
-                        f[2 * w2 + 1] = x[1];
-                    }
-                    return f;
-                };
-                v8i vf = vtile(0);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const v8i cur = vf;
-                    if (n + 1 < 8) vf = vtile(n + 1);
-                    acc[n] = mfma(cur, pf, acc[n]);
-                    acc[8 + n] = mfma(cur, pf_other, acc[8 + n]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-        if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
-
-        // merge the pairs.  Block b's state of pair p (m, l over its pages) is in wave
-        // 2p + b; its O for dims half h is in wave 2p + h (slot own if b == h).
-        const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
-        lds_barrier();   // every wave is done with the ring and the exchange
-        if (half == 0) {
-            xm[pair][hw][l32] = m_run;
-            xl[pair][hw][l32] = l_tot;
-            xq[pair][hw][l32] = lq_tot;
-        }
-        lds_barrier();
-        float f_blk[2];          // this pair's factor for block hw (own) and 1 - hw
-        float m_blk[2], l_blk[2];
-#pragma unroll
-        for (int o = 0; o < 2; ++o) {
-            const int b = o == 0 ? hw : 1 - hw;
-            const float m0 = xm[0][b][l32], m1 = xm[1][b][l32];
-            const float mm = fmaxf(m0, m1);
-            const float e0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mm);
-            const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-            const float ll = xl[0][b][l32] * e0 + xl[1][b][l32] * e1;
-            const float lq = xq[0][b][l32] * e0 + xq[1][b][l32] * e1;
-            const float mine = xm[pair][b][l32];
-            f_blk[o] = mine == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mine - mm) * (a.out_scale / lq);
-            m_blk[o] = mm;
-            l_blk[o] = ll;
-        }
-        const size_t slot_idx = (size_t)off_r + s;
-        // LSE of block `pair`, by the wave of this pair that holds it as its own block
-        if (hw == pair && half == 0 && jt * MT + 32 * pair + l32 < M)
-            lse_out[slot_idx * M + jt * MT + 32 * pair + l32] = m_blk[0] + __builtin_amdgcn_logf(l_blk[0]) - kPScale;
-        // every wave stores its scaled O of block 1 - pair (the block the other pair
-        // stores) in region [1 - pair][hw]; then it adds the other pair's O of block `pair`
-        constexpr int kRegion = 32 * kMergeStride;
-        float *const region = (float *)(void *)lds;
-        {
-            const int b = 1 - pair;
-            const int o = b == hw ? 0 : 1;           // acc slot of block b
-            float *mine = region + (b * 2 + hw) * kRegion + l32 * kMergeStride + 4 * half;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const v16f &t16 = acc[8 * o + n];
-                    *(v4f *)(mine + 32 * n + 8 * q4) =
-                        v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]} * f_blk[o];
-                }
-            }
-        }
-        lds_barrier();
-        {
-            const int b = pair;
-            const int o = b == hw ? 0 : 1;
-            const int row = jt * MT + 32 * b + l32;
-            const float *theirs = region + (b * 2 + hw) * kRegion + l32 * kMergeStride + 4 * half;
-            if (row < M) {
-                float *po = partial + (slot_idx * M + row) * kVDim + 256 * hw;
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const v16f &t16 = acc[8 * o + n];
-                        const v4f sum = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2], t16[4 * q4 + 3]} * f_blk[o] +
-                                        *(const v4f *)(theirs + 32 * n + 8 * q4);
-                        *(v4f *)(po + 32 * n + 8 * q4 + 4 * half) = sum;
-                    }
-                }
-            }
-        }
-        lds_barrier();  // the next unit's pages overwrite the regions
     }
 }
 
@@ -2672,13 +1379,18 @@ static int decode_launch(const uint8_t *d_q, const uint8_t *d_kv, int64_t pool_p
     int32_t *hdr = (int32_t *)d_workspace;
     float *part = (float *)((char *)d_workspace + lay.partial_off);
     float *lse = (float *)((char *)d_workspace + lay.lse_off);
-    const dim3 grid(params->workers), block(kDecodeThreads);
+    const dim3 grid(params->workers);
     hipStream_t st = (hipStream_t)stream;
 #define AMLA_DECODE_ARGS d_q, d_kv, d_block_table, d_lengths, d_counts, d_offsets, d_work, hdr, part, lse, a
     switch (params->mtile) {
-    case 32: hipLaunchKernelGGL(decode32_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
-    case 64: hipLaunchKernelGGL(decode64_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
-    default: hipLaunchKernelGGL(decode128_kernel, grid, block, 0, st, AMLA_DECODE_ARGS); break;
+    case 32:
+    case 64:
+        if (launch_decode_stream(params->mtile, grid, st, AMLA_DECODE_ARGS) != hipSuccess)
+            return AMLA_ERR_HIP;
+        break;
+    default:
+        if (launch_decode128(grid, st, AMLA_DECODE_ARGS) != hipSuccess) return AMLA_ERR_HIP;
+        break;
     }
 #undef AMLA_DECODE_ARGS
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;

@@ -1,0 +1,487 @@
+// The 32- and 64-row decode kernels (row tiles of up to 64 folded rows: the shapes whose
+// time is the KV stream from HBM).
+//
+// A workgroup's work units form one stream of ring entries: each unit contributes its query
+// rows (one entry: the tile's rows laid out like a page) and then its pages.  The four LDS
+// ring slots are refilled in stream order across unit boundaries, so the next unit's query
+// rows and first pages arrive while the current unit finishes and a unit costs no
+// pipeline drain.
+//
+// Eight waves, two per SIMD, in two roles one entry apart, so that each SIMD overlaps one
+// role's MFMAs with the other role's softmax, LDS traffic and waits:
+//   score waves (0-3)  wave (rb, kb) computes S^T for key block kb (keys [32kb, +32) of the
+//                      page) and the 32 rows of row block rb, the key block's softmax and
+//                      its half of the E4M3 P^T fragment, published in LDS (double
+//                      buffered); they also issue the ring's DMA.  MT = 32 has one row block:
+//                      waves 2, 3 repeat waves 0, 1, which alone publish.
+//   value waves (4-7)  one entry behind, O^T += V^T P^T for one row block and NT 32-dim
+//                      tiles (MT = 64: 256 dims, MT = 32: 128 dims), and the unit's FP32
+//                      partial and log2 LSE.
+// One barrier per entry (plus one at a unit's first page, where the two key blocks agree on
+// the row reference).
+//
+// Softmax in log2 units against a per-row reference (page "...cutedsl.mla.balanced", module
+// docstring: the row max is kept lazily and P is fed to the MMA in E4M3): m_ref is the row's
+// max over the unit's first page and key block kb's P is 2^(s - m_ref - gap_kb + kPExp)
+// <= 2^8, gap_kb the smallest whole number keeping that block's running max at or below
+// m_ref + gap_kb.  The P V MFMA scales each K block of its B operand by its own E8M0 byte, so
+// key block kb's P is scaled by 2^gap_kb and O and the row sums stay relative to m_ref with
+// no rescaling and no per-page agreement between the two key blocks.
+#include "common.h"
+
+namespace amla {
+namespace {
+
+// DMA of one ring entry: 64 rows of 576 bytes, row i at `base + 576 i`, into the ring slot
+// at `lds_dst` in the swizzled layout.  Rows at or past `valid` (1..64) take a copy of row
+// valid-1, so the slot holds only codes that belong to the entry and nothing past its valid
+// rows is read.
+__device__ __forceinline__ void issue_rows(const uint8_t *base, uint32_t lds_dst, int valid,
+                                           const DmaOffsets &o, int wave, int lane)
+{
+    if (valid >= kPage) {
+        issue_page(base, lds_dst, o);
+        return;
+    }
+    DmaOffsets c;
+#pragma unroll
+    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) c.v[i] = 0;
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+        const int p = (wave * kChunksPerWave + i) * 64 + lane;
+        const int row = p / (kKDim / 16), q = p - row * (kKDim / 16);
+        const int src = row < valid ? row : valid - 1;
+        c.v[i >> 1] |= (uint32_t)(src * kKDim + 16 * (q ^ swz(row))) << (16 * (i & 1));
+    }
+    issue_page(base, lds_dst, c);
+}
+
+// One work unit as the stream sees it.
+struct Unit {
+    int r, s, L, total, off, first, size, jt;
+    bool ok;
+};
+
+template <int MT>
+__global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
+    const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
+    const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ work, int32_t *__restrict__ header, float *__restrict__ partial,
+    float *__restrict__ lse_out, DecodeArgs a)
+{
+    static_assert(MT == 32 || MT == 64, "32- or 64-row tiles");
+    constexpr int NT = MT == 32 ? 4 : 8;   // 32-dim output tiles per value wave
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
+    // P^T fragments of an entry by (buffer, row block, lane): dwords [4kb, +4) come from the
+    // score wave of key block kb (the MFMA takes bytes [16kb, +16) of both lanes of a column
+    // as its K block kb, each K block with its own E8M0 scale)
+    __shared__ __attribute__((aligned(16))) int32_t xch_p[2][2][64][8];
+    // the whole-number gap of each key block's P reference, by (buffer, row block, key
+    // block, row)
+    __shared__ int32_t xch_gap[2][2][2][32];
+    // key-block maxima at a unit's first page; at its last page the row sums of each key
+    // block and the row reference
+    __shared__ float xch_max[2][2][32];
+    __shared__ float xch_l[2][2][32];
+    __shared__ float xch_lq[2][2][32];
+    __shared__ float xch_mref[2][32];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
+    const int R = a.reqs, M = a.rows;
+    const int mt = ceil_div(M, MT);
+    const int W = a.workers;
+
+    const int vw = virtual_worker(blockIdx.x, W, mt);
+    const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
+    const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
+    const int h_reqs = ldc(&header[kHdrReqs]);
+    const int n_items = ldc(&offsets[R]);
+    asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
+                 "s"(n_items));
+    if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
+        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
+        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+        return;
+    }
+    const int units = n_items * mt;
+
+    // The descriptor of unit u: its work pair, then the request's count, length, slot
+    // offset (and global length under DCP); index clamped so the loads stay in bounds.
+    auto load_unit = [&](int u) {
+        Unit d;
+        const int uu = u < units ? u : 0;
+        const int item = uu / mt;
+        d.jt = uu - item * mt;
+        d.r = ldc(&work[2 * item]);
+        d.s = ldc(&work[2 * item + 1]);
+        const int rc = d.r >= 0 && d.r < R ? d.r : 0;
+        const int c = ldc(&counts[rc]);
+        d.L = ldc(&lengths[rc]);
+        d.off = ldc(&offsets[rc]);
+        d.total = a.causal ? ldc(&a.totals[rc]) : d.L;
+        const int pages = ceil_div(d.L, kPage);
+        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
+        d.first = d.s * q + (d.s < rem ? d.s : rem);
+        d.size = q + (d.s < rem ? 1 : 0);
+        d.ok = d.r == rc && d.s >= 0 && d.s < c && d.L > 0 && pages <= a.bt_stride && d.size > 0 &&
+               d.off + d.s < n_items;
+        return d;
+    };
+    // A cursor over the workgroup's entries: the unit (skipping bad work items, which have
+    // no entries) and the entry within it (0: query rows, 1 + t: page t).
+    struct Cursor {
+        int u, e;
+        Unit d, next;
+    };
+    auto cursor_skip = [&](Cursor &c, bool flag) {
+        while (c.u < units && !c.d.ok) {
+            if (flag && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+            c.u += W;
+            c.d = c.next;
+            c.next = load_unit(c.u + W);
+        }
+    };
+    auto cursor_init = [&](Cursor &c, bool flag) {
+        c.u = vw;
+        c.e = 0;
+        c.d = load_unit(c.u);
+        c.next = load_unit(c.u + W);
+        cursor_skip(c, flag);
+    };
+    auto cursor_advance = [&](Cursor &c, bool flag) {
+        if (++c.e > c.d.size) {
+            c.u += W;
+            c.d = c.next;
+            c.next = load_unit(c.u + W);
+            c.e = 0;
+            cursor_skip(c, flag);
+        }
+    };
+
+    if (wave < 4) {
+        // ================================================================ score waves
+        const int srb = MT == 64 ? (wave & 1) : 0;
+        const int skb = MT == 64 ? (wave >> 1) : (wave & 1);
+        const bool writer = MT == 64 || wave < 2;
+
+        // ---- issue side: two entries ahead of this role's entry
+        const DmaOffsets dmao = dma_offsets(wave, lane);
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
+        bool page_bad = false;
+        Cursor ci;
+        cursor_init(ci, false);
+        int issued = 0;
+        int32_t pid_next = 0;
+        auto prefetch_pid = [&]() {
+            const int t = ci.e >= 1 ? ci.e - 1 : 0;   // the page of the next page entry
+            if (ci.u < units)
+                pid_next = ldc(&block_table[(size_t)ci.d.r * a.bt_stride + ci.d.first +
+                                            (t < ci.d.size ? t : ci.d.size - 1)]);
+        };
+        prefetch_pid();
+        auto issue_next = [&]() {
+            if (ci.u >= units) return;
+            const uint32_t dst = lds_base + (uint32_t)(issued % kSlots) * kPageBytes;
+            if (ci.e == 0) {
+                const int rows = M - ci.d.jt * MT;
+                issue_rows(q_in + ((size_t)ci.d.r * M + (size_t)ci.d.jt * MT) * kKDim, dst,
+                           rows < MT ? rows : MT, dmao, wave, lane);
+            } else {
+                const int t = ci.e - 1;
+                int32_t pid = pid_next;
+                if (pid < 0 || pid >= a.pool_pages) {
+                    page_bad = true;
+                    pid = 0;
+                }
+                const int valid = ci.d.L - (ci.d.first + t) * kPage;
+                issue_rows(kv_in + (int64_t)pid * kPageBytes, dst, valid < kPage ? valid : kPage,
+                           dmao, wave, lane);
+            }
+            ++issued;
+            cursor_advance(ci, false);
+            prefetch_pid();
+        };
+
+        // K and Q fragment reads: key 32 skb + l32 / row 32 srb + l32, chunks 4k + 2*half + e
+        // (rows 32 apart share the swizzle)
+        int k_off[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) k_off[e] = l32 * kKDim + 16 * ((2 * half + e) ^ swz(l32));
+        v8i qf[9];
+        // the row's reference (log2 units, the same for both key blocks), this key block's
+        // P-reference gap above it, FP32 and E4M3 P sums of the key block relative to m_ref
+        float m_ref = -INFINITY, l_run = 0.f, lq_run = 0.f;
+        int gap = 0, lim = 0;
+
+        Cursor cs;
+        cursor_init(cs, true);
+        issue_next();
+        issue_next();
+        for (int step = 0;; ++step) {
+            const bool have = cs.u < units;
+            // this role's entry has landed (every score wave waits for its own DMA share)
+            // and every wave is done with the entry two before it, whose slot is refilled
+            if (have) {
+                if (issued - step - 1 >= 1)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kChunksPerWave, 0));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+            }
+            asm volatile("s_barrier" ::: "memory");
+            if (!have) break;
+            issue_next();
+            const uint8_t *slot = lds + (step % kSlots) * kPageBytes;
+            const Unit &u = cs.d;
+            if (cs.e == 0) {
+                // the unit's query rows: Q^T fragments of row block srb (lane (l32, half):
+                // row 32 srb + l32, dims [64k + 32 half, +32))
+                const uint8_t *qs = slot + 32 * srb * kKDim;
+#pragma unroll
+                for (int k = 0; k < 9; ++k)
+                    qf[k] = lds_read2x16(qs + k_off[0] + 64 * k, qs + k_off[1] + 64 * k);
+                m_ref = -INFINITY;
+                l_run = lq_run = 0.f;
+                gap = 0;
+                lim = row_key_limit(a, u.total, u.L, u.jt * MT + 32 * srb + l32);
+                if (a.causal && tid == 0 && shard_count(a, u.total) != u.L)
+                    atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
+            } else {
+                const int t = cs.e - 1;
+                const int buf = step & 1;
+                // a reference more than 2^64 below a key block's running max (practically
+                // never): both key blocks and the value waves move it up by the larger gap
+                // of the previous page
+                if (t > 0) {
+                    const int g0 = xch_gap[buf ^ 1][srb][0][l32], g1 = xch_gap[buf ^ 1][srb][1][l32];
+                    const int gmax = g0 > g1 ? g0 : g1;
+                    if (__any(gmax > kRefGap)) {
+                        const int d = gmax > kRefGap ? gmax : 0;
+                        const float f = __builtin_amdgcn_ldexpf(1.f, -d);
+                        l_run *= f;
+                        lq_run *= f;
+                        if (d > 0) m_ref += (float)d;
+                        gap -= d;
+                    }
+                }
+                // S^T[32 keys of block skb x 32 rows] = K Q^T: 9 MFMAs, K read two ahead
+                v16f sc = v16f{0};
+                {
+                    const uint8_t *kp0 = slot + 32 * skb * kKDim + k_off[0];
+                    const uint8_t *kp1 = slot + 32 * skb * kKDim + k_off[1];
+                    v8i kf0 = lds_read2x16(kp0, kp1);
+                    v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) {
+                        const v8i cur = (k & 1) ? kf1 : kf0;
+                        if (k + 2 < 9) {
+                            if (k & 1)
+                                kf1 = lds_read2x16(kp0 + 64 * (k + 2), kp1 + 64 * (k + 2));
+                            else
+                                kf0 = lds_read2x16(kp0 + 64 * (k + 2), kp1 + 64 * (k + 2));
+                        }
+                        sc = mfma(cur, qf[k], sc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                // keys of the page the row sees, counted from this lane's first key
+                // (32 skb + 4 half): element e holds key 8(e/4) + e%4 past it
+                const int valid = lim - (u.first + t) * kPage - 32 * skb - 4 * half;
+                if (__any(valid < 32)) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (8 * (e >> 2) + (e & 3) >= valid) sc[e] = -INFINITY;
+                }
+                float smax = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) smax = fmaxf(smax, sc[e]);
+                const float mx = half_pair_max(smax) * a.score_scale;   // the key block's max
+                if (t == 0) {
+                    // the unit's first page: the row reference is the page max over both key
+                    // blocks (-inf while the row sees no key: with visible keys a prefix of
+                    // the shard, a row that sees no key of its split's first page sees none)
+                    if (writer && half == 0) xch_max[srb][skb][l32] = mx;
+                    lds_barrier();
+                    m_ref = fmaxf(mx, xch_max[srb][skb ^ 1][l32]);
+                    gap = 0;
+                } else if (mx > m_ref + (float)gap) {
+                    gap = (int)__builtin_ceilf(mx - m_ref);
+                }
+                const float bias = m_ref == -INFINITY ? 0.f : (kPExp - (float)gap) - m_ref;
+                // P = 2^(s*scale - m_ref - gap + kPExp) <= 2^8: FP32 into the row sum, E4M3
+                // into this lane's 16 bytes of key block skb (byte 4g + e: key 32 skb + 8g +
+                // 4 half + e)
+                float psum = 0.f, qsum = 0.f;
+                v4i pw;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float p4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        p4[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g + e], a.score_scale, bias));
+                        psum += p4[e];
+                    }
+                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], 0, false);
+                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], w4, true);
+                    pw[g] = w4;
+                    const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, false);
+                    const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
+                    qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
+                }
+                l_run += __builtin_amdgcn_ldexpf(psum, gap);
+                lq_run += __builtin_amdgcn_ldexpf(qsum, gap);
+                if (writer) {
+                    *(v4i *)&xch_p[buf][srb][lane][4 * skb] = pw;
+                    if (half == 0) xch_gap[buf][srb][skb][l32] = gap;
+                }
+                if (cs.e == u.size) {
+                    // the unit's last page: its row sums (both lane halves: every lane takes
+                    // part in the swap) and reference, for the value waves
+                    const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
+                    if (writer && half == 0) {
+                        xch_l[srb][skb][l32] = l_tot;
+                        xch_lq[srb][skb][l32] = lq_tot;
+                        if (skb == 0) xch_mref[srb][l32] = m_ref;
+                    }
+                }
+            }
+            cursor_advance(cs, true);
+        }
+        if (page_bad && lane == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
+    } else {
+        // ================================================================ value waves
+        const int vwv = wave - 4;
+        const int prb = MT == 64 ? (vwv & 1) : 0;
+        const int tile0 = MT == 64 ? NT * (vwv >> 1) : NT * vwv;
+        const bool lse_writer = MT == 64 ? (vwv >> 1) == 0 : vwv == 0;
+
+        // V^T fragment reads (ds_read_b64_tr_b8): within each 16-lane group, source lane i
+        // supplies key row b = i/2 and dims [8*(i%2), +8) of a 16-dim column block; keys are
+        // tr_key + 16*w2, dims of tile T lie in chunk 2T + (g16&1), swizzled by the key row.
+        // Byte 16b + e of lane half h is then key 32b + 8(e/4) + 4h + e%4, as in P^T.
+        const int g16 = lane >> 4, i16 = lane & 15;
+        const int tr_key = 8 * (i16 >> 3) + 4 * half + ((i16 >> 1) & 3);
+        int tr_off[2];
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) +
+                          8 * (i16 & 1) + 64 * (tile0 >> 1);
+        v16f acc[NT];
+        Cursor cv;
+        cursor_init(cv, false);
+        for (int step = 0;; ++step) {
+            // step s: this role's entry is the one the score waves took at step s - 1
+            if (step > 0 && cv.u >= units) break;
+            asm volatile("s_barrier" ::: "memory");
+            if (step == 0) continue;
+            const Unit &u = cv.d;
+            if (cv.e == 0) {
+                // the query rows: nothing here, but the score waves now agree on the first
+                // page's reference (one more barrier on both sides)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[n] = v16f{0};
+                lds_barrier();
+            } else {
+                const int buf = (step - 1) & 1;
+                const uint8_t *slot = lds + ((step - 1) % kSlots) * kPageBytes;
+                // the row block's P^T fragment and the E8M0 scale of K block `half` (lane
+                // half h supplies the scale of K block h of its column: 2^gap of key block h)
+                const v8i pf = *(const v8i *)&xch_p[buf][prb][lane][0];
+                int g_own = xch_gap[buf][prb][half][l32];
+                {
+                    const int g0 = xch_gap[buf][prb][0][l32], g1 = xch_gap[buf][prb][1][l32];
+                    const int gmax = g0 > g1 ? g0 : g1;
+                    if (__any(gmax > kRefGap)) {
+                        // the score waves move the reference up by the larger gap (see
+                        // there): O follows, before this page is added
+                        const int d = gmax > kRefGap ? gmax : 0;
+                        const float f = __builtin_amdgcn_ldexpf(1.f, -d);
+#pragma unroll
+                        for (int n = 0; n < NT; ++n) acc[n] *= f;
+                        g_own -= d;
+                    }
+                }
+                const int sb = 127 + (g_own < -127 ? -127 : g_own);
+                const uint8_t *vp0 = slot + tr_off[0], *vp1 = slot + tr_off[1];
+                auto vtile = [&](int n) {
+                    v8i f;
+                    const uint8_t *vp = (n & 1) ? vp1 : vp0;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim + 64 * (n >> 1));
+                        f[2 * w2] = x[0];
+                        f[2 * w2 + 1] = x[1];
+                    }
+                    return f;
+                };
+                v8i vf = vtile(0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const v8i cur = vf;
+                    if (n + 1 < NT) vf = vtile(n + 1);
+                    acc[n] = mfma_scaled_b(cur, pf, acc[n], sb);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (cv.e == u.size) {
+                    // the unit's last page: normalise and store the row block's FP32 partial
+                    // (this wave's dims) and the log2 LSE; l and lq carry P's 2^kPExp, which
+                    // cancels in O / lq
+                    float l_tot = xch_l[prb][0][l32] + xch_l[prb][1][l32];
+                    float lq_tot = xch_lq[prb][0][l32] + xch_lq[prb][1][l32];
+                    float mref = xch_mref[prb][l32];
+                    {
+                        const int g0 = xch_gap[buf][prb][0][l32], g1 = xch_gap[buf][prb][1][l32];
+                        const int gmax = g0 > g1 ? g0 : g1;
+                        if (gmax > kRefGap) {   // moved with this page (see above)
+                            const float f = __builtin_amdgcn_ldexpf(1.f, -gmax);
+                            l_tot *= f;
+                            lq_tot *= f;
+                            mref += (float)gmax;
+                        }
+                    }
+                    const size_t slot_idx = (size_t)u.off + u.s;
+                    const int row = u.jt * MT + 32 * prb + l32;
+                    if (row < M) {
+                        if (lse_writer && half == 0)
+                            lse_out[slot_idx * M + row] = mref + __builtin_amdgcn_logf(l_tot) - kPExp;
+                        const float inv = lq_tot > 0.f ? a.out_scale / lq_tot : 0.f;   // no key: O = 0
+                        float *po = partial + (slot_idx * M + row) * kVDim;
+#pragma unroll
+                        for (int n = 0; n < NT; ++n) {
+                            const int dim = 32 * (tile0 + n) + 4 * half;
+#pragma unroll
+                            for (int q4 = 0; q4 < 4; ++q4)
+                                *(v4f *)(po + dim + 8 * q4) =
+                                    v4f{acc[n][4 * q4], acc[n][4 * q4 + 1], acc[n][4 * q4 + 2],
+                                        acc[n][4 * q4 + 3]} * inv;
+                        }
+                    }
+                }
+            }
+            cursor_advance(cv, false);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_stream(int mtile, dim3 grid, hipStream_t stream, const uint8_t *q,
+                                const uint8_t *kv, const int32_t *block_table,
+                                const int32_t *lengths, const int32_t *counts,
+                                const int32_t *offsets, const int32_t *work, int32_t *header,
+                                float *partial, float *lse, const DecodeArgs &a)
+{
+    if (mtile == 32)
+        hipLaunchKernelGGL(decode_stream_kernel<32>, grid, dim3(2 * kDecodeThreads), 0, stream, q,
+                           kv, block_table, lengths, counts, offsets, work, header, partial, lse, a);
+    else
+        hipLaunchKernelGGL(decode_stream_kernel<64>, grid, dim3(2 * kDecodeThreads), 0, stream, q,
+                           kv, block_table, lengths, counts, offsets, work, header, partial, lse, a);
+    return hipGetLastError();
+}
+
+}  // namespace amla
