@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-KERNELS = {32: "decode32_kernel", 64: "decode64_kernel", 128: "decode128_kernel"}
+KERNELS = {32: "decode_stream_kernel<32>", 64: "decode_stream_kernel<64>",
+           128: "decode128_kernel"}
 
 
 def parse():
@@ -74,9 +75,14 @@ def parse():
 
 
 def source_digest():
+    """Digest of every device source (the recorded traffic is valid for this digest only)."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "absorbed_mla_split_amd", "csrc", "amla.hip"), "rb") as f:
-        h.update(f.read())
+    csrc = os.path.join(ROOT, "absorbed_mla_split_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
