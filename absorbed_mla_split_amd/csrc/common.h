@@ -235,6 +235,48 @@ __device__ __forceinline__ void issue_page(const uint8_t *page_base, uint32_t ld
 }
 static_assert(kChunksPerWave == 9, "issue_page is written for 9 DMA instructions per wave");
 
+// issue_page with the lane's offsets taken through opaque copies: the compiler cannot
+// hoist their unpacking out of a page loop (nine live or spilled registers instead of five).
+__device__ __forceinline__ void issue_page_opaque(const uint8_t *page_base, uint32_t lds_dst,
+                                                  const DmaOffsets &o)
+{
+    DmaOffsets c = o;
+#pragma unroll
+    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) asm volatile("" : "+v"(c.v[i]));
+    issue_page(page_base, lds_dst, c);
+}
+
+// DMA of one ring entry: 64 rows of 576 bytes, row i at `base + 576 i`, into the ring slot
+// at `lds_dst` in the swizzled layout (`o`: the lane's offsets from dma_offsets).  Rows at or
+// past `valid` (1..64) take a copy of row valid-1, so the slot holds only codes that belong
+// to the entry and nothing past its valid rows is read.  OPAQUE: the offsets are computed
+// from opaque copies of the lane's values (see issue_page_opaque).
+template <bool OPAQUE = false>
+__device__ __forceinline__ void issue_rows(const uint8_t *base, uint32_t lds_dst, int valid,
+                                           const DmaOffsets &o, int wave, int lane)
+{
+    if (valid >= kPage) {
+        if constexpr (OPAQUE)
+            issue_page_opaque(base, lds_dst, o);
+        else
+            issue_page(base, lds_dst, o);
+        return;
+    }
+    int ln = lane;
+    if constexpr (OPAQUE) asm volatile("" : "+v"(ln));
+    DmaOffsets c;
+#pragma unroll
+    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) c.v[i] = 0;
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+        const int p = (wave * kChunksPerWave + i) * 64 + ln;
+        const int row = p / (kKDim / 16), q = p - row * (kKDim / 16);
+        const int src = row < valid ? row : valid - 1;
+        c.v[i >> 1] |= (uint32_t)(src * kKDim + 16 * (q ^ swz(row))) << (16 * (i & 1));
+    }
+    issue_page(base, lds_dst, c);
+}
+
 __device__ __forceinline__ v8i lds_read2x16(const uint8_t *p0, const uint8_t *p1)
 {
     const v4i a = *(const v4i *)p0;
@@ -345,6 +387,30 @@ __device__ __forceinline__ void scale_acc(v16f &t, float f)
         t[h] = x0; t[h + 1] = x1; t[h + 2] = x2; t[h + 3] = x3;
         t[h + 4] = x4; t[h + 5] = x5; t[h + 6] = x6; t[h + 7] = x7;
     }
+}
+
+// An accumulator tile held in AGPRs, copied to VGPRs eight registers per asm statement.
+// The AGPR operands keep the tile in its AGPRs up to this point (read as plain values, the
+// compiler may move whole tiles into VGPRs at a loop exit).  The caller pads the wait states
+// after the MFMA that last wrote the tile.
+__device__ __forceinline__ v16f acc_read(const v16f &t)
+{
+    v16f o;
+#pragma unroll
+    for (int h = 0; h < 16; h += 8) {
+        float y0, y1, y2, y3, y4, y5, y6, y7;
+        asm volatile(
+            "v_accvgpr_read_b32 %0, %8\n\tv_accvgpr_read_b32 %1, %9\n\t"
+            "v_accvgpr_read_b32 %2, %10\n\tv_accvgpr_read_b32 %3, %11\n\t"
+            "v_accvgpr_read_b32 %4, %12\n\tv_accvgpr_read_b32 %5, %13\n\t"
+            "v_accvgpr_read_b32 %6, %14\n\tv_accvgpr_read_b32 %7, %15"
+            : "=v"(y0), "=v"(y1), "=v"(y2), "=v"(y3), "=v"(y4), "=v"(y5), "=v"(y6), "=v"(y7)
+            : "a"(t[h]), "a"(t[h + 1]), "a"(t[h + 2]), "a"(t[h + 3]), "a"(t[h + 4]),
+              "a"(t[h + 5]), "a"(t[h + 6]), "a"(t[h + 7]));
+        o[h] = y0; o[h + 1] = y1; o[h + 2] = y2; o[h + 3] = y3;
+        o[h + 4] = y4; o[h + 5] = y5; o[h + 6] = y6; o[h + 7] = y7;
+    }
+    return o;
 }
 
 // Launches decode128_kernel (defined in decode128.hip, compiled with MFMA accumulators in

@@ -6,16 +6,50 @@
 namespace amla {
 namespace {
 
-// 128-row tiles, the four waves on every page.  Wave w = 2p + kb computes the scores of key
-// block kb (keys [32kb, +32) of the page) for the 64 rows [64p, +64) of the tile, so each
-// K fragment read from LDS feeds two MFMAs (one per row block); the two waves of a row
-// pair swap their key-block row maxima through LDS, so both take the same lazy max, then
-// each writes its half of the E4M3 P^T fragments of its rows.  Wave w owns O^T for the
-// 128 dims [128w, +128) of all 128 rows: after a second barrier it reads the P^T
-// fragments of the four row blocks and each V^T fragment read from LDS feeds four MFMAs.
-// The DMA of page t+3 goes into the slot page t-1 used.  Read-only inputs are separate
-// __restrict__ arguments; their uniform reads go through the constant address space
-// (scalar loads, which do not wait on the in-flight page DMAs).
+// S^T of both key blocks of a page for one k-step: key block kb's K fragment (A) times the
+// row block's Q^T fragment (B, shared), VGPR results.  The kernel's output accumulators
+// are AGPR-form MFMAs; these are written here so that the score tiles stay in VGPRs.  The
+// compiler does not see them as MFMAs: PAD adds 24 wait states after them, for a result
+// read by VALU code right after (a 16-pass XDL result read by VALU code needs fewer).
+template <bool FIRST, bool PAD>
+__device__ __forceinline__ void score_kpair(v16f &s0, v16f &s1, v8i k0, v8i k1, v8i q)
+{
+    if constexpr (FIRST) {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %2, %4, 0\n\t"
+                     "v_mfma_f32_32x32x64_f8f6f4 %1, %3, %4, 0"
+                     : "=&v"(s0), "=&v"(s1) : "v"(k0), "v"(k1), "v"(q));
+    } else {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %2, %4, %0\n\t"
+                     "v_mfma_f32_32x32x64_f8f6f4 %1, %3, %4, %1"
+                     : "+v"(s0), "+v"(s1) : "v"(k0), "v"(k1), "v"(q));
+    }
+    if constexpr (PAD) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// 128-row tiles, four waves, each owning 32 rows of the tile end to end: wave w computes
+// S^T (the page's 64 keys, two key blocks of 32, x its rows [32w, +32)), the softmax of its
+// rows, and O^T (the 512 value dims, sixteen 32-dim tiles in AGPRs, x its rows).  The lane
+// that holds a row's scores (column l % 32 of S^T) is the lane that supplies that row's
+// column of the P^T operand, so P goes from the exponentials to the P V MFMA in registers:
+// the waves exchange nothing, and meet only once per page, where the page ring advances.
+//
+// Each wave software-pipelines its pages: while the MFMAs of page t+1's scores run, the
+// VALU computes page t's softmax (mask, row max, reference, exponentials, E4M3 P), and
+// while page t's P V MFMAs run, the VALU adds up page t's E4M3 P.  The LDS ring holds
+// four pages: V of page t, K of page t+1 and two pages in flight; the DMA of page t+3 goes
+// into the slot that page t-1 used.  Read-only inputs are separate __restrict__
+// arguments; their uniform reads go through the constant address space (scalar loads,
+// which do not wait on the in-flight page DMAs).
+//
+// Softmax in log2 units against a per-row reference (page "...cutedsl.mla.balanced",
+// module docstring: the row max is kept lazily and P is fed to the MMA in E4M3): m_ref is
+// the row's max over the unit's first page, and on each page key block kb's P is
+// 2^(s - m_ref - g_kb + kPExp) <= 2^8 with g_kb the smallest whole number at or above that
+// block's max over the page minus m_ref (at least -127).  The P V MFMA scales K block kb of
+// its B operand by the E8M0 byte 127 + g_kb, so O and the row sums stay relative to m_ref
+// with no rescaling, while each page's P uses the E4M3 range from its own max down.  A
+// page whose max passes m_ref by more than kRefGap (log2 units; practically never) moves
+// the reference up and rescales the wave's tiles.
 __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
     const uint8_t *__restrict__ q_in, const uint8_t *__restrict__ kv_in,
     const int32_t *__restrict__ block_table, const int32_t *__restrict__ lengths,
@@ -25,18 +59,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 {
     constexpr int MT = 128;          // rows per work unit
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
-    // P^T fragments of the page: [row block][key block][lane][16 B]
-    __shared__ __attribute__((aligned(16))) int32_t xch_p[4][2][64 * 4];
-    // per (key block, row block, row): the key block's max on a unit's first page; at the
-    // end its P sums
-    __shared__ float xch_max[2][4][32];
-    __shared__ float xch_lq[2][4][32];
-    // per (row block, key block, row): the whole-number gap of the key block's P reference
-    __shared__ int32_t xch_gap[4][2][32];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kb = wave & 1, rp = wave >> 1;
     const int l32 = lane & 31, half = lane >> 5;
     const int R = a.reqs, M = a.rows;
     const int mt = ceil_div(M, MT);
@@ -76,11 +101,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 #pragma unroll
     for (int par = 0; par < 2; ++par)
         tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) + 8 * (i16 & 1);
-    // K fragment reads: key 32kb + l32 (same swizzle as key l32), chunks 4k + 2*half + e
-    int k_off[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-        k_off[e] = (32 * kb + l32) * kKDim + 16 * ((2 * half + e) ^ swz(l32));
+    // K fragment reads: key l32 of key block 0 (block 1: 32 rows further, the same swizzle),
+    // chunks 4k + 2*half + e
+    const int k_off0 = l32 * kKDim + 16 * ((2 * half) ^ swz(l32));
+    const int k_off1 = l32 * kKDim + 16 * ((2 * half + 1) ^ swz(l32));
+    constexpr int kBlock1 = 32 * kKDim;
 
     for (int u = vw; u < units; u += W) {
         const int item = u / mt, jt = u - item * mt;
@@ -103,229 +128,84 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         }
         if (a.causal && tid == 0 && shard_count(a, total) != L)   // shard and totals disagree
             atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_LENGTH);
-        const int row0 = jt * MT + 64 * rp;   // this wave's score rows: [row0, +64)
-        int lim[2];   // keys each of this lane's two score rows sees
-#pragma unroll
-        for (int j = 0; j < 2; ++j) lim[j] = row_key_limit(a, total, L, row0 + 32 * j + l32);
+        const int rbase = jt * MT + 32 * wave;   // this wave's rows: [rbase, +32)
+        const int row = rbase + l32;
+        const int lim = row_key_limit(a, total, L, row);   // keys the lane's row sees
         const int32_t *bt = block_table + (size_t)r * a.bt_stride + first;
 
-        v8i qf[2][9];   // Q^T fragments of the two row blocks, loaded below
-
         bool page_bad = false;
-        auto page_at = [&](int32_t pid) {
+        // page t of the split into its ring slot; rows past the request's length (only on
+        // its last page) repeat the last valid row, so that P*V reads no foreign codes
+        auto issue = [&](int t, int32_t pid) {
             if (pid < 0 || pid >= a.pool_pages) {
                 page_bad = true;
                 pid = 0;
             }
-            return kv_in + (int64_t)pid * kPageBytes;
+            const int valid = L - (first + t) * kPage;
+            issue_rows<true>(kv_in + (int64_t)pid * kPageBytes, lds_base + (t % kSlots) * kPageBytes,
+                       valid < kPage ? valid : kPage, dmao, wave, lane);
         };
         // block-table entry of page min(t, size - 1)
         auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
-        // keys past the request's length (only on its last page): zero the rows in LDS so
-        // that P*V stays finite; scores there are masked by key index
-        auto zero_tail = [&](int t) {
-            const int valid = L - (first + t) * kPage;
-            if (valid < kPage) {
-                uint8_t *slot = lds + (t % kSlots) * kPageBytes;
-                for (int off = valid * kKDim + tid * 16; off < kPageBytes; off += kDecodeThreads * 16)
-                    *(v4i *)(slot + off) = v4i{0, 0, 0, 0};
-                lds_barrier();
-            }
-        };
 
-        // per score row block j: the row's reference and the whole-number gap of its P
-        // reference above it (log2 units, shared by the two key-block waves), this key
-        // block's FP32 P sum (for the LSE) and E4M3 P sum (O is normalised by the E4M3 sum
-        // of both key blocks), both relative to m_ref
-        float m_ref[2] = {-INFINITY, -INFINITY};
-        int gap[2] = {0, 0};
-        float l_run[2] = {0.f, 0.f}, lq_run[2] = {0.f, 0.f};
-        v16f acc[4][4];   // O^T of row block rb, dim tile 4*wave + n
+        // The first two pages' block-table entries, loaded together, and the entry of the
+        // next page to fetch; the first pages' DMA, then the Q^T fragments of the wave's rows
+        // from global memory, so that both latencies overlap; then wait for all of it (the
+        // compiler tracks the Q loads, not the DMA).
+        const int32_t pid_a = page_id(0), pid_b = page_id(1);
+        asm volatile("" ::"s"(pid_a), "s"(pid_b));
+        int32_t pid_next = page_id(2);
+        issue(0, pid_a);
+        if (size > 1) issue(1, pid_b);
+        // Q^T fragment of k-step k: row `row`, bytes [64k + 32*half, +32); a row past M (in
+        // a last tile) reads row M-1: its scores are computed and never stored
+        v8i qf[9];
+        {
+            const uint8_t *qp = q_in + ((size_t)r * M + (row < M ? row : M - 1)) * kKDim + 32 * half;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int n = 0; n < 4; ++n) acc[rb][n] = v16f{0};
-
-        // The first pages' block-table entries, loaded together.
-        int32_t pid0[kSlots - 1];
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d) pid0[d] = page_id(d);
-        asm volatile("" ::"s"(pid0[0]), "s"(pid0[1]), "s"(pid0[2]));
-        // the entry of the next page to fetch, read one fetch ahead
-        int32_t pid_next = page_id(kSlots - 1);
-        // The first pages' DMA, then the Q^T fragments from global memory, so that
-        // both latencies overlap; then wait for all of it (the compiler tracks the Q
-        // loads, not the DMA).
-#pragma unroll
-        for (int d = 0; d < kSlots - 1; ++d)
-            if (d < size) issue_page(page_at(pid0[d]), lds_base + d * kPageBytes, dmao);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = row0 + 32 * j + l32;
-            if (row < M) {
-                const uint8_t *qp = q_in + ((size_t)r * M + row) * kKDim + 32 * half;
-#pragma unroll
-                for (int k = 0; k < 9; ++k) {
-                    const v4i x = *(const v4i *)(qp + 64 * k);
-                    const v4i y = *(const v4i *)(qp + 64 * k + 16);
-                    qf[j][k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 9; ++k) qf[j][k] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int k = 0; k < 9; ++k) {
+                const v4i x = *(const v4i *)(qp + 64 * k);
+                const v4i y = *(const v4i *)(qp + 64 * k + 16);
+                qf[k] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
             }
         }
         wait_pages_then_barrier(0);
 
-        for (int t = 0; t < size; ++t) {
-            const int after = size - 1 - t;
-            wait_pages_then_barrier(after < kSlots - 2 ? after : kSlots - 2);
-            if (t + kSlots - 1 < size) {
-                issue_page(page_at(pid_next),
-                           lds_base + ((t + kSlots - 1) % kSlots) * kPageBytes, dmao);
-                pid_next = page_id(t + kSlots);
-            }
-            zero_tail(t);
-            const uint8_t *slot = lds + (t % kSlots) * kPageBytes;
+        // the row's reference and its sums relative to it: FP32 P (for the LSE) and E4M3 P
+        // (O is normalised by the sum of the P it was built from); per lane the keys of
+        // its half, added over the lane pair at the end
+        float m_ref = -INFINITY, l_run = 0.f, lq_run = 0.f;
+        v16f acc[16];   // O^T of dim tile n (dims [32n, +32)) x the wave's rows
+#pragma unroll
+        for (int n = 0; n < 16; ++n) acc[n] = v16f{0};
 
-            // S^T[32 keys of block kb x 32 rows] for the two row blocks: 9 K fragments,
-            // each feeding two MFMAs, read one k-step ahead
-            v16f sc[2];
-            {
-                const uint8_t *kp0 = slot + k_off[0], *kp1 = slot + k_off[1];
-                v8i kf = lds_read2x16(kp0, kp1);
+        // S^T of the page in ring slot `slot` into sc (both key blocks).  The K fragments of
+        // k-step k+1 are read into the registers of k-step k once its MFMAs are issued (an
+        // MFMA reads its A and B operands at issue); `work(k)` runs after them, so that its
+        // VALU work overlaps the MFMAs and the reads.
+        v16f sc[2];
+        auto score = [&](const uint8_t *slot, auto &&work) {
+            v8i kf0 = lds_read2x16(slot + k_off0, slot + k_off1);
+            v8i kf1 = lds_read2x16(slot + kBlock1 + k_off0, slot + kBlock1 + k_off1);
+            static_for<0, 9>([&](auto kk) {
+                constexpr int k = decltype(kk)::value;
+                score_kpair<k == 0, false>(sc[0], sc[1], kf0, kf1, qf[k]);
                 __builtin_amdgcn_sched_barrier(0);
-                static_for<0, 9>([&](auto kk) {
-                    constexpr int k = decltype(kk)::value;
-                    const v8i cur = kf;
-                    if constexpr (k + 1 < 9) kf = lds_read2x16(kp0 + 64 * (k + 1), kp1 + 64 * (k + 1));
-                    score_step<k == 0, k == 8>(sc[0], sc[1], cur, qf[0][k], qf[1][k]);
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-            }
-            // key-block max of each row (masked by the row's key limit)
-            float kmax[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // keys of the page the row sees, counted from this lane's first key
-                // (32kb + 4*half): element e holds key 8(e/4) + e%4 past it
-                const int valid = lim[j] - (first + t) * kPage - (32 * kb + 4 * half);
-                if (__any(valid < 32)) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (8 * (e >> 2) + (e & 3) >= valid) sc[j][e] = -INFINITY;
+                if constexpr (k + 1 < 9) {
+                    kf0 = lds_read2x16(slot + 64 * (k + 1) + k_off0, slot + 64 * (k + 1) + k_off1);
+                    kf1 = lds_read2x16(slot + kBlock1 + 64 * (k + 1) + k_off0,
+                                       slot + kBlock1 + 64 * (k + 1) + k_off1);
                 }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[j][e]);
-                kmax[j] = half_pair_max(mx) * a.score_scale;
-            }
-            // Reference of each row (log2 units, the same in both waves of the row pair):
-            // m_ref is the row's max over the unit's first page (both key blocks, exchanged
-            // once), and key block kb's P is 2^(s - m_ref - gap + kPExp) <= 2^8, gap the
-            // smallest whole number keeping that block's running max at or below m_ref +
-            // gap.  The P V MFMA scales each K block of its B operand by its own E8M0 byte,
-            // so key block kb's P is scaled by 2^gap and O and the row sums stay relative to
-            // m_ref with no rescaling and no agreement between the key blocks on later pages.
-            if (t == 0) {
-                // the row index is recomputed here (an opaque copy): a value kept across the
-                // page loop would be spilled, and its reload waits for the page DMAs
-                int row_l = lane & 31;
-                asm volatile("" : "+v"(row_l));
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (half == 0) xch_max[kb][2 * rp + j][row_l] = kmax[j];
-                lds_barrier();
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    // -inf while the row sees no key: with visible keys a prefix of the
-                    // shard, a row that sees no key of its split's first page sees none
-                    m_ref[j] = fmaxf(kmax[j], xch_max[kb ^ 1][2 * rp + j][row_l]);
-                    gap[j] = 0;
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    if (kmax[j] > m_ref[j] + (float)gap[j]) gap[j] = (int)__builtin_ceilf(kmax[j] - m_ref[j]);
-            }
-            // P = 2^(s*scale - m_ref - gap + kPExp): FP32 into the row sum, E4M3 into this key
-            // block's half of the P^T fragment (lane (l32, half) byte 4g + e, g < 4, holds
-            // key 32kb + 8g + 4*half + e); the sums are kept relative to m_ref
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float bias = m_ref[j] == -INFINITY ? 0.f : (kPExp - (float)gap[j]) - m_ref[j];
-                float psum = 0.f, qsum = 0.f;
-                v4i pw;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float p[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][4 * g + e], a.score_scale, bias));
-                        psum += p[e];
-                    }
-                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w4, true);
-                    pw[g] = w4;
-                    const v2f q0 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, false);
-                    const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
-                    qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
-                }
-                l_run[j] += __builtin_amdgcn_ldexpf(psum, gap[j]);
-                lq_run[j] += __builtin_amdgcn_ldexpf(qsum, gap[j]);
-                *(v4i *)&xch_p[2 * rp + j][kb][lane * 4] = pw;
-                if (half == 0) xch_gap[2 * rp + j][kb][l32] = gap[j];
-            }
-            lds_barrier();
-
-            // The row blocks' P^T fragments and the E8M0 scale of K block `half` (lane half h
-            // supplies the scale of K block h of its column: 2^gap of key block h).  A
-            // reference more than 2^64 below a key block's running max (practically never)
-            // moves up by the larger gap: the row block's tiles in every wave, and its score
-            // state in the two waves that own it.
-            v8i pf[4];
-            int sb[4];
-            bool moved = false;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const v4i lo = *(const v4i *)&xch_p[rb][0][lane * 4];
-                const v4i hi = *(const v4i *)&xch_p[rb][1][lane * 4];
-                pf[rb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const int g0 = xch_gap[rb][0][l32], g1 = xch_gap[rb][1][l32];
-                moved = moved || (g0 > kRefGap || g1 > kRefGap);
-                sb[rb] = 127 + (half ? g1 : g0);
-            }
-            if (__any(moved)) {
-                // an MFMA that has just written a tile, then an MFMA reading a tile written
-                // through v_accvgpr_write: wait states the compiler does not count for the
-                // asm of scale_acc
-                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const int g0 = xch_gap[rb][0][l32], g1 = xch_gap[rb][1][l32];
-                    const int gmax = g0 > g1 ? g0 : g1;
-                    const int d = gmax > kRefGap ? gmax : 0;
-                    const int g = sb[rb] - 127 - d;
-                    sb[rb] = 127 + (g < -127 ? -127 : g);
-                    if (rb >> 1 == rp) {   // this wave's score rows
-                        const int j = rb & 1;
-                        const float f = __builtin_amdgcn_ldexpf(1.f, -d);
-                        l_run[j] *= f;
-                        lq_run[j] *= f;
-                        if (d > 0) m_ref[j] += (float)d;
-                        gap[j] -= d;
-                    }
-                    if (!__any(d != 0)) continue;
-                    const float f = __builtin_amdgcn_ldexpf(1.f, -d);
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) scale_acc(acc[rb][n], f);
-                }
-                asm volatile("s_nop 7" ::: "memory");
-            }
-            // O^T[dims 128w + 32n, rows of block rb] += V^T (P^T, K block h scaled by 2^gap_h)
+                work(kk);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        // O^T[dims 32n.., rows] += V^T (P^T, K block h scaled by 2^(sbv_h - 127)) for the page
+        // in `slot`, the V^T fragments read one tile ahead; `work(n)` runs after the MFMA of
+        // dim tile n is issued.
+        auto pv = [&](const uint8_t *slot, const v8i &pfv, int sbv, auto &&work) {
             auto vtile = [&](int n) {
-                const int T = 4 * wave + n;
-                const uint8_t *vp = slot + tr_off[T & 1] + 64 * (T >> 1);
+                const uint8_t *vp = slot + tr_off[n & 1] + 64 * (n >> 1);
                 v8i f;
 #pragma unroll
                 for (int w2 = 0; w2 < 4; ++w2) {
@@ -336,68 +216,179 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 return f;
             };
             v8i vf = vtile(0);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const v8i cur = vf;
-                if (n + 1 < 4) vf = vtile(n + 1);
-                // all four row blocks, also in a last tile with fewer rows: the accumulators
-                // stay in their registers only when every page updates all of them
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb) acc[rb][n] = mfma_scaled_b(cur, pf[rb], acc[rb][n], sb[rb]);
+            static_for<0, 16>([&](auto nn) {
+                constexpr int n = decltype(nn)::value;
+                v8i cv = vf;
+                if constexpr (n + 1 < 16) vf = vtile(n + 1);
+                // operands in VGPRs (the allocator would otherwise load some into AGPRs,
+                // which the sixteen accumulator tiles fill)
+                asm volatile("" : "+v"(cv));
+                acc[n] = mfma_scaled_b(cv, pfv, acc[n], sbv);
                 __builtin_amdgcn_sched_barrier(0);
+                work(nn);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        // Page t: its scores (with page t-1's E4M3 sum), then page t-1's P V MFMAs with page
+        // t's softmax: mask, row max, reference, exponentials, E4M3 P.
+        v8i pf, pf_prev;          // P^T fragments: bytes [16kb, +16) are key block kb
+        int g0 = 0, g1 = 0;       // page t's whole-number gaps (key blocks 0, 1)
+        int gp0 = 0, gp1 = 0;     // page t-1's
+        auto page = [&](int t, auto has_prev) {
+            constexpr bool PREV = decltype(has_prev)::value;
+            if (t > 0) {
+                wait_pages_then_barrier(t + 1 < size ? 1 : 0);
             }
+            if (t + 2 < size) issue(t + 2, pid_next);
+            {
+                const uint8_t *slot_t = lds + (t % kSlots) * kPageBytes;
+                float qs0 = 0.f, qs1 = 0.f;
+                // page t-1's E4M3 P dwords, added up for lq while the score MFMAs run
+                score(slot_t, [&](auto kk) {
+                    constexpr int k = decltype(kk)::value;
+                    if constexpr (PREV && k < 8) {
+                        const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[k], false);
+                        const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[k], true);
+                        const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
+                        if constexpr (k < 4) qs0 += d4; else qs1 += d4;
+                    }
+                });
+                if constexpr (PREV)
+                    lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
+
+                // keys of the page the lane's row sees, counted from the lane's first key
+                // (4*half): element e of key block kb holds key 32kb + 8(e/4) + e%4 past it
+                const int valid = lim - (first + t) * kPage - 4 * half;
+                float mx0 = -INFINITY, mx1 = -INFINITY;
+                float b0 = 0.f, b1 = 0.f, ps0 = 0.f, ps1 = 0.f;
+                int moved = 0;   // log2 step of the reference on this page
+                auto softmax = [&](auto nn) {
+                    constexpr int n = decltype(nn)::value;
+                    if constexpr (n == 0) {
+                        // the score MFMAs' results, read by VALU code: wait states the
+                        // compiler does not count for their asm
+                        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+                        if (__any(valid < kPage)) {
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                                for (int e = 0; e < 16; ++e)
+                                    if (32 * kb + 8 * (e >> 2) + (e & 3) >= valid) sc[kb][e] = -INFINITY;
+                        }
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) mx0 = fmaxf(mx0, sc[0][e]);
+                    } else if constexpr (n == 1) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) mx1 = fmaxf(mx1, sc[1][e]);
+                        mx0 = half_pair_max(mx0) * a.score_scale;
+                        mx1 = half_pair_max(mx1) * a.score_scale;
+                    } else if constexpr (n == 2) {
+                        // -inf while the row sees no key: with visible keys a prefix of the
+                        // shard, a row that sees no key of its split's first page sees none
+                        if (t == 0) m_ref = fmaxf(mx0, mx1);
+                        const bool none = m_ref == -INFINITY;
+                        g0 = none ? 0 : (int)__builtin_ceilf(fmaxf(mx0 - m_ref, -127.f));
+                        g1 = none ? 0 : (int)__builtin_ceilf(fmaxf(mx1 - m_ref, -127.f));
+                        // a block more than kRefGap above the reference moves it up by the
+                        // larger block's gap (the tiles follow once page t-1's MFMAs are done)
+                        const int gmax = g0 > g1 ? g0 : g1;
+                        moved = gmax > kRefGap ? gmax : 0;
+                        const float f = __builtin_amdgcn_ldexpf(1.f, -moved);
+                        m_ref += (float)moved;
+                        g0 = g0 - moved < -127 ? -127 : g0 - moved;
+                        g1 = g1 - moved < -127 ? -127 : g1 - moved;
+                        l_run *= f;
+                        lq_run *= f;
+                        b0 = none ? 0.f : (kPExp - (float)g0) - m_ref;
+                        b1 = none ? 0.f : (kPExp - (float)g1) - m_ref;
+                    } else if constexpr (n >= 3 && n <= 10) {
+                        // P = 2^(s*scale - m_ref - g + kPExp) for 4 elements: FP32 into the
+                        // block's sum, E4M3 into one dword of the fragment
+                        constexpr int kb = (n - 3) >> 2, e0 = 4 * ((n - 3) & 3);
+                        const float bias = kb ? b1 : b0;
+                        float p[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e0 + i], a.score_scale, bias));
+                        const float sum = (p[0] + p[1]) + (p[2] + p[3]);
+                        if constexpr (kb == 0) ps0 += sum; else ps1 += sum;
+                        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                        w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w4, true);
+                        pf[4 * kb + e0 / 4] = w4;
+                    }
+                };
+                if constexpr (PREV) {
+                    pv(lds + ((t - 1) % kSlots) * kPageBytes, pf_prev, 127 + (half ? gp1 : gp0),
+                       softmax);
+                } else {
+                    static_for<0, 16>([&](auto nn) { softmax(nn); });
+                }
+                l_run += __builtin_amdgcn_ldexpf(ps0, g0) + __builtin_amdgcn_ldexpf(ps1, g1);
+                if (__any(moved != 0)) {
+                    // page t-1's tiles follow the reference.  An MFMA that has just written
+                    // a tile, then an MFMA reading a tile written through v_accvgpr_write:
+                    // wait states the compiler does not count for the asm of scale_acc
+                    const float f = __builtin_amdgcn_ldexpf(1.f, -moved);
+                    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+                    for (int n = 0; n < 16; ++n) scale_acc(acc[n], f);
+                    asm volatile("s_nop 7" ::: "memory");
+                }
+                pf_prev = pf;
+                gp0 = g0;
+                gp1 = g1;
+            }
+            // the block-table entry of the page after the next refill, loaded after the last
+            // LDS read of the page (a scalar load in flight makes every LDS wait a full one)
+            pid_next = page_id(t + 3);
+        };
+        page(0, std::false_type{});
+        for (int t = 1; t < size; ++t) page(t, std::true_type{});
+        {
+            // page size-1's P V MFMAs, with its E4M3 sum
+            float qs0 = 0.f, qs1 = 0.f;
+            pv(lds + ((size - 1) % kSlots) * kPageBytes, pf_prev, 127 + (half ? gp1 : gp0),
+               [&](auto nn) {
+                   constexpr int n = decltype(nn)::value;
+                   if constexpr (n < 8) {
+                       const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[n], false);
+                       const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[n], true);
+                       const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
+                       if constexpr (n < 4) qs0 += d4; else qs1 += d4;
+                   }
+               });
+            lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
         }
 
         if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
 
-        // epilogue: the key-block sums are added over the row pair; each wave normalises
-        // and stores its dims of all rows.  l and lq carry P's 2^kPExp, which cancels
-        // in O / lq.
+        // epilogue: the lane pair's sums; LSE from the FP32 sum, O normalised by the E4M3
+        // sum (both carry P's 2^kPExp, which cancels in O / lq)
         const size_t slot_idx = (size_t)off_r + s;
-        float l_tot[2];
+        const float l = half_pair_sum(l_run), lq = half_pair_sum(lq_run);
+        // (the last P V MFMAs wrote the tiles read below through asm)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        if (row < M) {
+            if (half == 0) lse_out[slot_idx * M + row] = m_ref + __builtin_amdgcn_logf(l) - kPExp;
+            const float inv = lq > 0.f ? a.out_scale / lq : 0.f;   // no key: O = 0
+            float *po = partial + (slot_idx * M + row) * kVDim;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            l_tot[j] = half_pair_sum(l_run[j]);
-            const float lq_tot = half_pair_sum(lq_run[j]);
-            if (half == 0) {
-                xch_max[kb][2 * rp + j][l32] = l_tot[j];
-                xch_lq[kb][2 * rp + j][l32] = lq_tot;
-            }
-        }
-        lds_barrier();
-        if (kb == 0 && half == 0) {
+            for (int n = 0; n < 16; ++n) {
+                const int dim = 32 * n + 4 * half;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int row = row0 + 32 * j + l32;
-                if (row < M) {
-                    const float l = l_tot[j] + xch_max[1][2 * rp + j][l32];
-                    lse_out[slot_idx * M + row] = m_ref[j] + __builtin_amdgcn_logf(l) - kPExp;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const v16f t16 = acc_read(acc[n]);
+                    const v4f o = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2],
+                                      t16[4 * q4 + 3]} * inv;
+                    *(v4f *)(po + dim + 8 * q4) = o;
                 }
-            }
-        }
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int row = jt * MT + 32 * rb + l32;
-            if (row < M) {
-                const float lq = xch_lq[0][rb][l32] + xch_lq[1][rb][l32];
-                const float inv = lq > 0.f ? a.out_scale / lq : 0.f;   // no key: O = 0
-                float *po = partial + (slot_idx * M + row) * kVDim;
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const int dim = 32 * (4 * wave + n) + 4 * half;
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const v16f &t16 = acc[rb][n];
-                        const v4f o = v4f{t16[4 * q4], t16[4 * q4 + 1], t16[4 * q4 + 2],
-                                          t16[4 * q4 + 3]} * inv;
-                        *(v4f *)(po + dim + 8 * q4) = o;
-                    }
-                }
+                // one tile at a time out of the AGPRs (all at once they would not fit)
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        lds_barrier();  // the next unit's prologue overwrites the ring and the exchange
+        lds_barrier();  // the next unit's prologue overwrites the ring
     }
 }
 

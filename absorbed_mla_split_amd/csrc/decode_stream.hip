@@ -32,30 +32,6 @@
 namespace amla {
 namespace {
 
-// DMA of one ring entry: 64 rows of 576 bytes, row i at `base + 576 i`, into the ring slot
-// at `lds_dst` in the swizzled layout.  Rows at or past `valid` (1..64) take a copy of row
-// valid-1, so the slot holds only codes that belong to the entry and nothing past its valid
-// rows is read.
-__device__ __forceinline__ void issue_rows(const uint8_t *base, uint32_t lds_dst, int valid,
-                                           const DmaOffsets &o, int wave, int lane)
-{
-    if (valid >= kPage) {
-        issue_page(base, lds_dst, o);
-        return;
-    }
-    DmaOffsets c;
-#pragma unroll
-    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) c.v[i] = 0;
-#pragma unroll
-    for (int i = 0; i < kChunksPerWave; ++i) {
-        const int p = (wave * kChunksPerWave + i) * 64 + lane;
-        const int row = p / (kKDim / 16), q = p - row * (kKDim / 16);
-        const int src = row < valid ? row : valid - 1;
-        c.v[i >> 1] |= (uint32_t)(src * kKDim + 16 * (q ^ swz(row))) << (16 * (i & 1));
-    }
-    issue_page(base, lds_dst, c);
-}
-
 // One work unit as the stream sees it.
 struct Unit {
     int r, s, L, total, off, first, size, jt;
@@ -86,6 +62,10 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
     __shared__ float xch_l[2][2][32];
     __shared__ float xch_lq[2][2][32];
     __shared__ float xch_mref[2][32];
+    // per (row block, key block, row): the unit's last page's FP32 and E4M3 P sums (relative
+    // to the reference plus that page's gap), added in by the value waves
+    __shared__ float xch_ps[2][2][32];
+    __shared__ float xch_qs[2][2][32];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -215,6 +195,11 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
         // P-reference gap above it, FP32 and E4M3 P sums of the key block relative to m_ref
         float m_ref = -INFINITY, l_run = 0.f, lq_run = 0.f;
         int gap = 0, lim = 0;
+        // the latest page's sums and gap: added to l_run / lq_run at the next page, once the
+        // move of the reference that page may cause is known (ldexp by a gap above kRefGap
+        // could overflow)
+        float pend_ps = 0.f, pend_qs = 0.f;
+        int pend_gap = 0;
 
         Cursor cs;
         cursor_init(cs, true);
@@ -251,20 +236,19 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
             } else {
                 const int t = cs.e - 1;
                 const int buf = step & 1;
-                // a reference more than 2^64 below a key block's running max (practically
-                // never): both key blocks and the value waves move it up by the larger gap
-                // of the previous page
+                // a reference more than 2^kRefGap below a key block's running max (practically
+                // never): both key blocks and the value waves move it up by the larger gap of
+                // the previous page, whose sums are added here relative to the moved reference
                 if (t > 0) {
                     const int g0 = xch_gap[buf ^ 1][srb][0][l32], g1 = xch_gap[buf ^ 1][srb][1][l32];
                     const int gmax = g0 > g1 ? g0 : g1;
-                    if (__any(gmax > kRefGap)) {
-                        const int d = gmax > kRefGap ? gmax : 0;
-                        const float f = __builtin_amdgcn_ldexpf(1.f, -d);
-                        l_run *= f;
-                        lq_run *= f;
-                        if (d > 0) m_ref += (float)d;
-                        gap -= d;
-                    }
+                    const int d = gmax > kRefGap ? gmax : 0;
+                    l_run = __builtin_amdgcn_ldexpf(l_run, -d) +
+                            __builtin_amdgcn_ldexpf(pend_ps, pend_gap - d);
+                    lq_run = __builtin_amdgcn_ldexpf(lq_run, -d) +
+                             __builtin_amdgcn_ldexpf(pend_qs, pend_gap - d);
+                    m_ref += (float)d;
+                    gap -= d;
                 }
                 // S^T[32 keys of block skb x 32 rows] = K Q^T: 9 MFMAs, K read two ahead
                 v16f sc = v16f{0};
@@ -331,19 +315,24 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                     const v2f q1 = __builtin_amdgcn_cvt_pk_f32_fp8(w4, true);
                     qsum += (q0[0] + q0[1]) + (q1[0] + q1[1]);
                 }
-                l_run += __builtin_amdgcn_ldexpf(psum, gap);
-                lq_run += __builtin_amdgcn_ldexpf(qsum, gap);
+                pend_ps = psum;
+                pend_qs = qsum;
+                pend_gap = gap;
                 if (writer) {
                     *(v4i *)&xch_p[buf][srb][lane][4 * skb] = pw;
                     if (half == 0) xch_gap[buf][srb][skb][l32] = gap;
                 }
                 if (cs.e == u.size) {
-                    // the unit's last page: its row sums (both lane halves: every lane takes
-                    // part in the swap) and reference, for the value waves
+                    // the unit's last page: its row sums before that page and that page's
+                    // sums (both lane halves: every lane takes part in the swaps) and the
+                    // reference, for the value waves
                     const float l_tot = half_pair_sum(l_run), lq_tot = half_pair_sum(lq_run);
+                    const float ps_tot = half_pair_sum(pend_ps), qs_tot = half_pair_sum(pend_qs);
                     if (writer && half == 0) {
                         xch_l[srb][skb][l32] = l_tot;
                         xch_lq[srb][skb][l32] = lq_tot;
+                        xch_ps[srb][skb][l32] = ps_tot;
+                        xch_qs[srb][skb][l32] = qs_tot;
                         if (skb == 0) xch_mref[srb][l32] = m_ref;
                     }
                 }
@@ -430,19 +419,20 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                     // the unit's last page: normalise and store the row block's FP32 partial
                     // (this wave's dims) and the log2 LSE; l and lq carry P's 2^kPExp, which
                     // cancels in O / lq
-                    float l_tot = xch_l[prb][0][l32] + xch_l[prb][1][l32];
-                    float lq_tot = xch_lq[prb][0][l32] + xch_lq[prb][1][l32];
-                    float mref = xch_mref[prb][l32];
-                    {
-                        const int g0 = xch_gap[buf][prb][0][l32], g1 = xch_gap[buf][prb][1][l32];
-                        const int gmax = g0 > g1 ? g0 : g1;
-                        if (gmax > kRefGap) {   // moved with this page (see above)
-                            const float f = __builtin_amdgcn_ldexpf(1.f, -gmax);
-                            l_tot *= f;
-                            lq_tot *= f;
-                            mref += (float)gmax;
-                        }
-                    }
+                    // (the sums before the last page, and the last page's relative to the
+                    // reference plus its gaps; a move caused by that page applies to all)
+                    const int g0 = xch_gap[buf][prb][0][l32], g1 = xch_gap[buf][prb][1][l32];
+                    const int gmax = g0 > g1 ? g0 : g1;
+                    const int d = gmax > kRefGap ? gmax : 0;
+                    const float l_tot =
+                        __builtin_amdgcn_ldexpf(xch_l[prb][0][l32] + xch_l[prb][1][l32], -d) +
+                        __builtin_amdgcn_ldexpf(xch_ps[prb][0][l32], g0 - d) +
+                        __builtin_amdgcn_ldexpf(xch_ps[prb][1][l32], g1 - d);
+                    const float lq_tot =
+                        __builtin_amdgcn_ldexpf(xch_lq[prb][0][l32] + xch_lq[prb][1][l32], -d) +
+                        __builtin_amdgcn_ldexpf(xch_qs[prb][0][l32], g0 - d) +
+                        __builtin_amdgcn_ldexpf(xch_qs[prb][1][l32], g1 - d);
+                    const float mref = xch_mref[prb][l32] + (float)d;
                     const size_t slot_idx = (size_t)u.off + u.s;
                     const int row = u.jt * MT + 32 * prb + l32;
                     if (row < M) {

@@ -6,6 +6,8 @@ size in the benchmark's launch configuration and are checked on sampled rows.  I
 carry NaN codes in every cache slot past a request's length and in unused pages, and the
 outputs, LSE and workspace start as NaN.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -13,7 +15,7 @@ import torch
 import oracle
 from absorbed_mla_split_amd import binding
 from absorbed_mla_split_amd import workloads as wl
-from gpu_util import compare, run_gpu, sample_rows, to_dev, ws_partials, vmax, OUT_TOL
+from gpu_util import compare, run_gpu, sample_rows, to_dev, ws_partials, vmax, LSE_TOL, OUT_TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -150,6 +152,34 @@ def test_fold_equals_unfolded_rows():
     assert np.max(np.abs(out_f.reshape(R * k, H, 512) - out_u)) <= OUT_TOL * vm
     assert np.max(np.abs(lse_f.reshape(R * k, H) - lse_u)) <= 1e-3
     compare(wu, out_u, lse_u, tag="unfolded")
+
+
+@pytest.mark.parametrize("k,H", [(4, 8), (7, 8), (4, 64), (3, 43)])
+@pytest.mark.parametrize("peak", [120.0, 200.0])
+def test_score_outliers_move_the_reference(k, H, peak):
+    # Keys far above the rest of their split: the even rows of each request equal its row 0,
+    # and three keys of each request (one on its first page) equal that row, so those rows
+    # score `peak` (log2 units) on them and about peak/24 elsewhere.  A split whose first
+    # page holds no such key sees a later page pass its reference by more than the kernels'
+    # headroom (the reference moves, the output tiles are rescaled); the split holding the
+    # first-page copy sees later pages far below it (down to the -127 clamp of the scale).
+    w = wl.small(2, k, H, [3000, 1500], seed=k * 7 + H)
+    for r in range(w.R):
+        w.q8[r, 2::2, :] = w.q8[r, 0, :]
+        L = int(w.lengths[r])
+        for pos in (0, L // 3, (2 * L) // 3 + 5):
+            w.kv8[w.block_table[r, pos // 64], pos % 64, :] = w.q8[r, 0, :]
+    qv = oracle.e4m3_table()[w.q8[0, 0, :]].astype(np.float64)
+    dot = float((qv * qv).sum()) * w.q_scale * w.k_scale
+    w.sm_scale = peak / (dot * math.log2(math.e))
+    out, lse, dec = run_gpu(w)
+    counts, _, _, _ = dec.plan_host()
+    assert counts.max() >= 3, counts            # several splits per request
+    # The scores come from FP8 MFMAs whose FP32 sums carry an error of order 2^-16 of the
+    # dot product's magnitude: at a score of `peak` log2 units the LSE may be off by that
+    # much more than the usual 1e-3.
+    compare(w, out, lse, tag=f"outlier k{k}H{H}p{peak}", lse_tol=LSE_TOL + peak * 2.0**-15)
+    assert dec.device_status() == 0
 
 
 def test_deterministic_bitwise():
