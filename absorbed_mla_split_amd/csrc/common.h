@@ -277,6 +277,37 @@ __device__ __forceinline__ void issue_rows(const uint8_t *base, uint32_t lds_dst
     issue_page(base, lds_dst, c);
 }
 
+// One of the nine DMA instructions of a wave's share of a ring entry: 1 KiB, lane l's 16
+// bytes from `base` + `off` to `lds_dst` + 16 l (see issue_page), so that a caller can spread
+// a page's DMA between other work instead of stalling on nine issues in a row.
+__device__ __forceinline__ void issue_chunk(const uint8_t *base, uint32_t lds_dst, uint32_t off)
+{
+    base = uniform_ptr(base);
+    lds_dst = __builtin_amdgcn_readfirstlane(lds_dst);
+    asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o], %[b]"
+                 :
+                 : [o] "v"(off), [b] "s"(base), [m] "s"(lds_dst)
+                 : "memory");
+}
+
+// The lane's source offset of chunk i of a ring entry whose rows at or past `valid` repeat row
+// valid-1 (see issue_rows), computed from opaque copies (see issue_page_opaque).
+__device__ __forceinline__ uint32_t chunk_offset(const DmaOffsets &o, int i, int valid, int wave,
+                                                 int lane)
+{
+    if (valid >= kPage) {
+        uint32_t v = o.v[i >> 1];
+        asm volatile("" : "+v"(v));
+        return (i & 1) ? (v >> 16) : (v & 0xFFFFu);
+    }
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int p = (wave * kChunksPerWave + i) * 64 + ln;
+    const int row = p / (kKDim / 16), q = p - row * (kKDim / 16);
+    const int src = row < valid ? row : valid - 1;
+    return (uint32_t)(src * kKDim + 16 * (q ^ swz(row)));
+}
+
 __device__ __forceinline__ v8i lds_read2x16(const uint8_t *p0, const uint8_t *p1)
 {
     const v4i a = *(const v4i *)p0;

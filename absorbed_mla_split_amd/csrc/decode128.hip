@@ -6,24 +6,17 @@
 namespace amla {
 namespace {
 
-// S^T of both key blocks of a page for one k-step: key block kb's K fragment (A) times the
-// row block's Q^T fragment (B, shared), VGPR results.  The kernel's output accumulators
-// are AGPR-form MFMAs; these are written here so that the score tiles stay in VGPRs.  The
-// compiler does not see them as MFMAs: PAD adds 24 wait states after them, for a result
-// read by VALU code right after (a 16-pass XDL result read by VALU code needs fewer).
-template <bool FIRST, bool PAD>
-__device__ __forceinline__ void score_kpair(v16f &s0, v16f &s1, v8i k0, v8i k1, v8i q)
+// S^T of one key block of a page for one k-step: the key block's K fragment (A) times the
+// row block's Q^T fragment (B), VGPR results.  The kernel's output accumulators are
+// AGPR-form MFMAs; this one is written here so that the score tile stays in VGPRs.  The
+// compiler does not see it as an MFMA: its readers pad the wait states.
+template <bool FIRST>
+__device__ __forceinline__ void score_one(v16f &s, v8i k, v8i q)
 {
-    if constexpr (FIRST) {
-        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %2, %4, 0\n\t"
-                     "v_mfma_f32_32x32x64_f8f6f4 %1, %3, %4, 0"
-                     : "=&v"(s0), "=&v"(s1) : "v"(k0), "v"(k1), "v"(q));
-    } else {
-        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %2, %4, %0\n\t"
-                     "v_mfma_f32_32x32x64_f8f6f4 %1, %3, %4, %1"
-                     : "+v"(s0), "+v"(s1) : "v"(k0), "v"(k1), "v"(q));
-    }
-    if constexpr (PAD) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    if constexpr (FIRST)
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
+    else
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
 }
 
 // 128-row tiles, four waves, each owning 32 rows of the tile end to end: wave w computes
@@ -59,6 +52,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 {
     constexpr int MT = 128;          // rows per work unit
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kSlots * kPageBytes];
+    // the unit's block-table entries, 64 pages per half, one copy per wave (each wave reads
+    // the entries it DMA'd itself: a scalar load of an entry in flight would turn every LDS
+    // wait of the page into a full wait)
+    __shared__ int32_t bt_lds[4][2][64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,6 +144,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         };
         // block-table entry of page min(t, size - 1)
         auto page_id = [&](int t) { return ldc(&bt[t < size ? t : size - 1]); };
+        // the entries of pages [64b, +64) (clamped to the unit) into bt_lds[wave][b & 1]:
+        // one DMA instruction, lane l's entry to bt_lds[wave][b & 1][l]
+        const uint32_t bt_lds_base = (uint32_t)(uintptr_t)(LDS_AS int32_t *)&bt_lds[wave][0][0];
+        auto issue_bt = [&](int b) {
+            const int e = 64 * b + lane;
+            const uint32_t off = 4u * (uint32_t)(e < size ? e : size - 1);
+            const uint8_t *base = uniform_ptr((const uint8_t *)bt);
+            const uint32_t m = __builtin_amdgcn_readfirstlane(bt_lds_base + 256u * (uint32_t)(b & 1));
+            asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dword %[o], %[b]"
+                         :
+                         : [o] "v"(off), [b] "s"(base), [m] "s"(m)
+                         : "memory");
+        };
 
         // The first two pages' block-table entries, loaded together, and the entry of the
         // next page to fetch; the first pages' DMA, then the Q^T fragments of the wave's rows
@@ -155,6 +165,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         const int32_t pid_a = page_id(0), pid_b = page_id(1);
         asm volatile("" ::"s"(pid_a), "s"(pid_b));
         int32_t pid_next = page_id(2);
+        issue_bt(0);
         issue(0, pid_a);
         if (size > 1) issue(1, pid_b);
         // Q^T fragment of k-step k: row `row`, bytes [64k + 32*half, +32); a row past M (in
@@ -179,186 +190,279 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 #pragma unroll
         for (int n = 0; n < 16; ++n) acc[n] = v16f{0};
 
-        // S^T of the page in ring slot `slot` into sc (both key blocks).  The K fragments of
-        // k-step k+1 are read into the registers of k-step k once its MFMAs are issued (an
-        // MFMA reads its A and B operands at issue); `work(k)` runs after them, so that its
-        // VALU work overlaps the MFMAs and the reads.
-        v16f sc[2];
-        auto score = [&](const uint8_t *slot, auto &&work) {
-            v8i kf0 = lds_read2x16(slot + k_off0, slot + k_off1);
-            v8i kf1 = lds_read2x16(slot + kBlock1 + k_off0, slot + kBlock1 + k_off1);
-            static_for<0, 9>([&](auto kk) {
-                constexpr int k = decltype(kk)::value;
-                score_kpair<k == 0, false>(sc[0], sc[1], kf0, kf1, qf[k]);
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (k + 1 < 9) {
-                    kf0 = lds_read2x16(slot + 64 * (k + 1) + k_off0, slot + 64 * (k + 1) + k_off1);
-                    kf1 = lds_read2x16(slot + kBlock1 + 64 * (k + 1) + k_off0,
-                                       slot + kBlock1 + 64 * (k + 1) + k_off1);
+        // An MFMA may still read its A and B registers after it is issued, and the data of an
+        // LDS load is written to its registers when it returns, with no interlock between the
+        // two.  So no load may target the operand registers of the MFMA issued last: each
+        // MFMA's operands are kept live (an empty asm using them) until the next MFMA is
+        // issued, and fragments are read into registers freed that way.
+        //
+        // A wave issues in order, and an MFMA waits at issue until the one before it is done,
+        // so VALU work overlaps an MFMA only when it stands between two MFMAs.  A page is
+        // therefore 34 slots of one MFMA followed by at most about one MFMA's worth of VALU
+        // work: 18 score slots (page t's S^T, key block 0 then key block 1, k-steps 0-8)
+        // carrying page t-1's key-block-1 exponentials, its E4M3 sum and the ring refill, then
+        // 16 P V slots (page t-1's O^T update, dim tiles 0-15) carrying page t's mask, row max,
+        // reference and key-block-0 exponentials.
+
+        v16f sc[2];   // S^T of the page in flight: key blocks 0, 1
+        // K fragment of score slot i (key block i / 9, k-step i % 9) of the page in `slot`
+        auto kfrag = [&](const uint8_t *slot, int i) {
+            const uint8_t *kp = slot + (i / 9) * kBlock1 + 64 * (i % 9);
+            return lds_read2x16(kp + k_off0, kp + k_off1);
+        };
+        // V^T fragment of dim tile n (dims [32n, +32)) of the page in `slot`
+        auto vtile = [&](const uint8_t *slot, int n) {
+            const uint8_t *vp = slot + tr_off[n & 1] + 64 * (n >> 1);
+            v8i f;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim);
+                f[2 * w2] = x[0];
+                f[2 * w2 + 1] = x[1];
+            }
+            return f;
+        };
+
+        // Score slots of the page in `slot` (SCORE) with `work(i)` after slot i's MFMA.  The
+        // K fragments go round a ring of three, read two slots ahead into the registers of
+        // slot i-1 once slot i's MFMA is issued.
+        v8i kf[3];
+        auto score_slots = [&](auto score, const uint8_t *slot, auto &&work) {
+            constexpr bool SCORE = decltype(score)::value;
+            if constexpr (SCORE) {
+                kf[0] = kfrag(slot, 0);
+                kf[1] = kfrag(slot, 1);
+            }
+            static_for<0, 18>([&](auto ii) {
+                constexpr int i = decltype(ii)::value;
+                if constexpr (SCORE) {
+                    score_one<i % 9 == 0>(sc[i / 9], kf[i % 3], qf[i % 9]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (i >= 1) asm volatile("" ::"v"(kf[(i - 1) % 3]));
+                    if constexpr (i + 2 < 18) kf[(i + 2) % 3] = kfrag(slot, i + 2);
                 }
-                work(kk);
+                work(ii);
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        // O^T[dims 32n.., rows] += V^T (P^T, K block h scaled by 2^(sbv_h - 127)) for the page
-        // in `slot`, the V^T fragments read one tile ahead; `work(n)` runs after the MFMA of
-        // dim tile n is issued.
-        auto pv = [&](const uint8_t *slot, const v8i &pfv, int sbv, auto &&work) {
-            auto vtile = [&](int n) {
-                const uint8_t *vp = slot + tr_off[n & 1] + 64 * (n >> 1);
-                v8i f;
-#pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const v2i x = lds_read_tr8(vp + 16 * w2 * kKDim);
-                    f[2 * w2] = x[0];
-                    f[2 * w2 + 1] = x[1];
-                }
-                return f;
-            };
-            v8i vf = vtile(0);
+        // P V slots of the page in `slot` (PV; fragment pfv, E8M0 scales sbv) with `work(n)`
+        // after dim tile n's MFMA.  The V^T fragments go round a ring of three (tile n in
+        // vr[n % 3]; the caller reads tiles 0 and 1), two tiles ahead into the registers of
+        // tile n-1 once tile n's MFMA is issued.  The last MFMA's operands are kept live for
+        // 64 cycles after it.
+        v8i vr[3];
+        auto pv_slots = [&](auto pvb, const uint8_t *slot, const v8i &pfv, int sbv, auto &&work) {
+            constexpr bool PV = decltype(pvb)::value;
             static_for<0, 16>([&](auto nn) {
                 constexpr int n = decltype(nn)::value;
-                v8i cv = vf;
-                if constexpr (n + 1 < 16) vf = vtile(n + 1);
-                // operands in VGPRs (the allocator would otherwise load some into AGPRs,
-                // which the sixteen accumulator tiles fill)
-                asm volatile("" : "+v"(cv));
-                acc[n] = mfma_scaled_b(cv, pfv, acc[n], sbv);
-                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (PV) {
+                    // operands in VGPRs (the allocator would otherwise load some into AGPRs,
+                    // which the sixteen accumulator tiles fill)
+                    asm volatile("" : "+v"(vr[n % 3]));
+                    acc[n] = mfma_scaled_b(vr[n % 3], pfv, acc[n], sbv);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (n >= 1) asm volatile("" ::"v"(vr[(n - 1) % 3]));
+                    if constexpr (n + 2 < 16) vr[(n + 2) % 3] = vtile(slot, n + 2);
+                }
                 work(nn);
                 __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (PV)
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                             "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::"v"(vr[15 % 3]), "v"(pfv));
         };
 
-        // Page t: its scores (with page t-1's E4M3 sum), then page t-1's P V MFMAs with page
-        // t's softmax: mask, row max, reference, exponentials, E4M3 P.
-        v8i pf, pf_prev;          // P^T fragments: bytes [16kb, +16) are key block kb
-        int g0 = 0, g1 = 0;       // page t's whole-number gaps (key blocks 0, 1)
-        int gp0 = 0, gp1 = 0;     // page t-1's
-        auto page = [&](int t, auto has_prev) {
-            constexpr bool PREV = decltype(has_prev)::value;
-            if (t > 0) {
-                wait_pages_then_barrier(t + 1 < size ? 1 : 0);
-            }
-            if (t + 2 < size) issue(t + 2, pid_next);
-            {
-                const uint8_t *slot_t = lds + (t % kSlots) * kPageBytes;
-                float qs0 = 0.f, qs1 = 0.f;
-                // page t-1's E4M3 P dwords, added up for lq while the score MFMAs run
-                score(slot_t, [&](auto kk) {
-                    constexpr int k = decltype(kk)::value;
-                    if constexpr (PREV && k < 8) {
-                        const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[k], false);
-                        const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[k], true);
-                        const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
-                        if constexpr (k < 4) qs0 += d4; else qs1 += d4;
-                    }
-                });
-                if constexpr (PREV)
-                    lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
+        // Softmax state.  Page t's key block kb has whole-number gap g_kb and bias b_kb (P =
+        // 2^(s*scale + b_kb)); the previous page's (gp, bp1) are kept for its key-block-1
+        // exponentials, its sums and its P V MFMAs.  pf: the P^T fragment being built (bytes
+        // [16kb, +16) are key block kb; key block 0 is written with the page's softmax, key
+        // block 1 one page later); pfa: the previous page's, complete once its key-block-1
+        // exponentials are done.
+        v8i pf, pfa;
+        int g0 = 0, g1 = 0, gp0 = 0, gp1 = 0;
+        float b0 = 0.f, b1 = 0.f, bp1 = 0.f;
 
-                // keys of the page the lane's row sees, counted from the lane's first key
-                // (4*half): element e of key block kb holds key 32kb + 8(e/4) + e%4 past it
-                const int valid = lim - (first + t) * kPage - 4 * half;
-                float mx0 = -INFINITY, mx1 = -INFINITY;
-                float b0 = 0.f, b1 = 0.f, ps0 = 0.f, ps1 = 0.f;
-                int moved = 0;   // log2 step of the reference on this page
-                auto softmax = [&](auto nn) {
-                    constexpr int n = decltype(nn)::value;
-                    if constexpr (n == 0) {
-                        // the score MFMAs' results, read by VALU code: wait states the
-                        // compiler does not count for their asm
-                        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-                        if (__any(valid < kPage)) {
+        // Score-slot work for the previous page (PREV): its key-block-1 exponentials (two per
+        // slot, slots 0-7), their FP32 sum into l (slot 8), its E4M3 sum over the whole
+        // fragment (one dword per slot, slots 9-16, into lq at slot 16); the ring refill (REFILL:
+        // one DMA instruction per slot, slots 9-17) and the first V^T fragments of the previous
+        // page (slots 16, 17).
+        float ps1 = 0.f, qs0 = 0.f, qs1 = 0.f;
+        float pt[4];
+        bool bt_next = false;
+        int bt_block = 0;
+        auto prev_work = [&](auto ii, bool refill, const uint8_t *src, uint32_t dst, int rvalid,
+                             const uint8_t *slot_p, auto prev) {
+            constexpr int i = decltype(ii)::value;
+            constexpr bool PREV = decltype(prev)::value;
+            if constexpr (PREV && i < 8) {
 #pragma unroll
-                            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                                for (int e = 0; e < 16; ++e)
-                                    if (32 * kb + 8 * (e >> 2) + (e & 3) >= valid) sc[kb][e] = -INFINITY;
-                        }
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) mx0 = fmaxf(mx0, sc[0][e]);
-                    } else if constexpr (n == 1) {
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) mx1 = fmaxf(mx1, sc[1][e]);
-                        mx0 = half_pair_max(mx0) * a.score_scale;
-                        mx1 = half_pair_max(mx1) * a.score_scale;
-                    } else if constexpr (n == 2) {
-                        // -inf while the row sees no key: with visible keys a prefix of the
-                        // shard, a row that sees no key of its split's first page sees none
-                        if (t == 0) m_ref = fmaxf(mx0, mx1);
-                        const bool none = m_ref == -INFINITY;
-                        g0 = none ? 0 : (int)__builtin_ceilf(fmaxf(mx0 - m_ref, -127.f));
-                        g1 = none ? 0 : (int)__builtin_ceilf(fmaxf(mx1 - m_ref, -127.f));
-                        // a block more than kRefGap above the reference moves it up by the
-                        // larger block's gap (the tiles follow once page t-1's MFMAs are done)
-                        const int gmax = g0 > g1 ? g0 : g1;
-                        moved = gmax > kRefGap ? gmax : 0;
-                        const float f = __builtin_amdgcn_ldexpf(1.f, -moved);
-                        m_ref += (float)moved;
-                        g0 = g0 - moved < -127 ? -127 : g0 - moved;
-                        g1 = g1 - moved < -127 ? -127 : g1 - moved;
-                        l_run *= f;
-                        lq_run *= f;
-                        b0 = none ? 0.f : (kPExp - (float)g0) - m_ref;
-                        b1 = none ? 0.f : (kPExp - (float)g1) - m_ref;
-                    } else if constexpr (n >= 3 && n <= 10) {
-                        // P = 2^(s*scale - m_ref - g + kPExp) for 4 elements: FP32 into the
-                        // block's sum, E4M3 into one dword of the fragment
-                        constexpr int kb = (n - 3) >> 2, e0 = 4 * ((n - 3) & 3);
-                        const float bias = kb ? b1 : b0;
-                        float p[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e0 + i], a.score_scale, bias));
-                        const float sum = (p[0] + p[1]) + (p[2] + p[3]);
-                        if constexpr (kb == 0) ps0 += sum; else ps1 += sum;
-                        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                        w4 = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w4, true);
-                        pf[4 * kb + e0 / 4] = w4;
-                    }
-                };
-                if constexpr (PREV) {
-                    pv(lds + ((t - 1) % kSlots) * kPageBytes, pf_prev, 127 + (half ? gp1 : gp0),
-                       softmax);
-                } else {
-                    static_for<0, 16>([&](auto nn) { softmax(nn); });
+                for (int e = 0; e < 2; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][2 * i + e], a.score_scale, bp1));
+                    pt[2 * (i & 1) + e] = p;
+                    ps1 += p;
                 }
-                l_run += __builtin_amdgcn_ldexpf(ps0, g0) + __builtin_amdgcn_ldexpf(ps1, g1);
-                if (__any(moved != 0)) {
-                    // page t-1's tiles follow the reference.  An MFMA that has just written
-                    // a tile, then an MFMA reading a tile written through v_accvgpr_write:
-                    // wait states the compiler does not count for the asm of scale_acc
-                    const float f = __builtin_amdgcn_ldexpf(1.f, -moved);
-                    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-#pragma unroll
-                    for (int n = 0; n < 16; ++n) scale_acc(acc[n], f);
-                    asm volatile("s_nop 7" ::: "memory");
+                if constexpr (i & 1) {
+                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], 0, false);
+                    w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[2], pt[3], w4, true);
+                    pfa[4 + (i >> 1)] = w4;
                 }
-                pf_prev = pf;
-                gp0 = g0;
-                gp1 = g1;
             }
-            // the block-table entry of the page after the next refill, loaded after the last
-            // LDS read of the page (a scalar load in flight makes every LDS wait a full one)
-            pid_next = page_id(t + 3);
+            if constexpr (PREV && i == 8) l_run += __builtin_amdgcn_ldexpf(ps1, gp1);
+            if constexpr (PREV && i >= 9 && i <= 16) {
+                const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pfa[i - 9], false);
+                const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pfa[i - 9], true);
+                const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
+                if constexpr (i < 13) qs0 += d4; else qs1 += d4;
+                if constexpr (i == 16)
+                    lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
+            }
+            if constexpr (i >= 9) {
+                if (refill) issue_chunk(src, dst + 1024 * (i - 9), chunk_offset(dmao, i - 9, rvalid, wave, lane));
+            }
+            if constexpr (i == 0) {
+                // the next 64 block-table entries, well before they are read (and before
+                // this page's refill, so that the barrier's vmcnt wait still counts the
+                // refill as the newest nine)
+                if (bt_next) issue_bt(bt_block);
+            }
+            if constexpr (PREV && i >= 16) vr[i - 16] = vtile(slot_p, i - 16);
+        };
+
+        // P-V-slot work for page t (SOFTMAX): mask and key-block-0 max (slot 0), key-block-1
+        // max (1), gaps and the reference move (2), biases (3), key-block-0 exponentials (two
+        // per slot, 4-11), their FP32 sum into l (12).
+        float mx0 = -INFINITY, mx1 = -INFINITY, ps0 = 0.f;
+        int32_t bt_v = 0;
+        int moved = 0;   // log2 step of the reference on this page
+        auto cur_work = [&](auto nn, int t, int valid, auto softmax) {
+            constexpr int n = decltype(nn)::value;
+            if constexpr (decltype(softmax)::value) {
+                if constexpr (n == 0) {
+                    // the score MFMAs' results, read by VALU code: wait states the compiler
+                    // does not count for their asm
+                    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+                    if (__any(valid < kPage)) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int e = 0; e < 16; ++e)
+                                if (32 * kb + 8 * (e >> 2) + (e & 3) >= valid) sc[kb][e] = -INFINITY;
+                    }
+                    mx0 = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx0 = fmaxf(mx0, sc[0][e]);
+                } else if constexpr (n == 1) {
+                    mx1 = -INFINITY;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx1 = fmaxf(mx1, sc[1][e]);
+                    mx0 = half_pair_max(mx0) * a.score_scale;
+                    mx1 = half_pair_max(mx1) * a.score_scale;
+                } else if constexpr (n == 2) {
+                    // -inf while the row sees no key: with visible keys a prefix of the
+                    // shard, a row that sees no key of its split's first page sees none
+                    if (t == 0) m_ref = fmaxf(mx0, mx1);
+                    const bool none = m_ref == -INFINITY;
+                    g0 = none ? 0 : (int)__builtin_ceilf(fmaxf(mx0 - m_ref, -127.f));
+                    g1 = none ? 0 : (int)__builtin_ceilf(fmaxf(mx1 - m_ref, -127.f));
+                    // a block more than kRefGap above the reference moves it up by the
+                    // larger block's gap (the tiles follow once page t-1's MFMAs are done)
+                    const int gmax = g0 > g1 ? g0 : g1;
+                    moved = gmax > kRefGap ? gmax : 0;
+                } else if constexpr (n == 3) {
+                    const float f = __builtin_amdgcn_ldexpf(1.f, -moved);
+                    m_ref += (float)moved;
+                    g0 = g0 - moved < -127 ? -127 : g0 - moved;
+                    g1 = g1 - moved < -127 ? -127 : g1 - moved;
+                    l_run *= f;
+                    lq_run *= f;
+                    const bool none = m_ref == -INFINITY;
+                    b0 = none ? 0.f : (kPExp - (float)g0) - m_ref;
+                    b1 = none ? 0.f : (kPExp - (float)g1) - m_ref;
+                    ps0 = 0.f;
+                } else if constexpr (n >= 4 && n <= 11) {
+                    constexpr int i = n - 4;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][2 * i + e], a.score_scale, b0));
+                        pt[2 * (i & 1) + e] = p;
+                        ps0 += p;
+                    }
+                    if constexpr (i & 1) {
+                        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], 0, false);
+                        w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[2], pt[3], w4, true);
+                        pf[i >> 1] = w4;
+                    }
+                } else if constexpr (n == 12) {
+                    l_run += __builtin_amdgcn_ldexpf(ps0, g0);
+                }
+            }
+            if constexpr (n == 13) {
+                // the block-table entry of the page after the next refill
+                const int tt = t + 3 < size ? t + 3 : size - 1;
+                bt_v = bt_lds[wave][(tt >> 6) & 1][tt & 63];
+            }
+        };
+
+        // Page t: wait for it and refill the ring, its score slots, the previous page's P V
+        // slots, then (rarely) the tiles follow a reference move, and the page's state becomes
+        // the previous page's.
+        auto page = [&](int t, auto prev) {
+            constexpr bool PREV = decltype(prev)::value;
+            if (t > 0) wait_pages_then_barrier(t + 1 < size ? 1 : 0);
+            const uint8_t *slot_t = lds + (t % kSlots) * kPageBytes;
+            const uint8_t *slot_p = lds + ((t + kSlots - 1) % kSlots) * kPageBytes;
+            // the ring refill: page t+2
+            const bool refill = t + 2 < size;
+            int32_t pid = pid_next;
+            if (refill && (pid < 0 || pid >= a.pool_pages)) {
+                page_bad = true;
+                pid = 0;
+            }
+            const uint8_t *src = kv_in + (int64_t)pid * kPageBytes;
+            const uint32_t dst = lds_base + ((t + 2) % kSlots) * kPageBytes;
+            const int rvalid = L - (first + t + 2) * kPage;
+            bt_block = (t >> 6) + 1;
+            bt_next = (t & 63) == 8 && 64 * bt_block < size;
+            ps1 = qs0 = qs1 = 0.f;
+            score_slots(std::true_type{}, slot_t, [&](auto ii) {
+                prev_work(ii, refill, src, dst, rvalid, slot_p, prev);
+            });
+            // keys of the page the lane's row sees, counted from the lane's first key
+            // (4*half): element e of key block kb holds key 32kb + 8(e/4) + e%4 past it
+            const int valid = lim - (first + t) * kPage - 4 * half;
+            pv_slots(prev, slot_p, pfa, 127 + (half ? gp1 : gp0), [&](auto nn) {
+                cur_work(nn, t, valid, std::true_type{});
+            });
+            if (__any(moved != 0)) {
+                // the previous page's tiles follow the reference.  An MFMA that has just
+                // written a tile, then an MFMA reading a tile written through
+                // v_accvgpr_write: wait states the compiler does not count for scale_acc
+                const float f = __builtin_amdgcn_ldexpf(1.f, -moved);
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+                for (int n = 0; n < 16; ++n) scale_acc(acc[n], f);
+                asm volatile("s_nop 7" ::: "memory");
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pfa[w] = pf[w];
+            gp0 = g0;
+            gp1 = g1;
+            bp1 = b1;
+            pid_next = __builtin_amdgcn_readfirstlane(bt_v);
         };
         page(0, std::false_type{});
         for (int t = 1; t < size; ++t) page(t, std::true_type{});
         {
-            // page size-1's P V MFMAs, with its E4M3 sum
-            float qs0 = 0.f, qs1 = 0.f;
-            pv(lds + ((size - 1) % kSlots) * kPageBytes, pf_prev, 127 + (half ? gp1 : gp0),
-               [&](auto nn) {
-                   constexpr int n = decltype(nn)::value;
-                   if constexpr (n < 8) {
-                       const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[n], false);
-                       const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pf_prev[n], true);
-                       const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
-                       if constexpr (n < 4) qs0 += d4; else qs1 += d4;
-                   }
-               });
-            lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
+            // the last page's key-block-1 exponentials and E4M3 sum, then its P V MFMAs
+            const uint8_t *slot_l = lds + ((size - 1) % kSlots) * kPageBytes;
+            ps1 = qs0 = qs1 = 0.f;
+            score_slots(std::false_type{}, slot_l, [&](auto ii) {
+                prev_work(ii, false, slot_l, 0u, 0, slot_l, std::true_type{});
+            });
+            pv_slots(std::true_type{}, slot_l, pfa, 127 + (half ? gp1 : gp0), [&](auto nn) {
+                cur_work(nn, 0, 0, std::false_type{});
+            });
         }
 
         if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
