@@ -250,26 +250,28 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                     m_ref += (float)d;
                     gap -= d;
                 }
-                // S^T[32 keys of block skb x 32 rows] = K Q^T: 9 MFMAs, K read two ahead
+                // S^T[32 keys of block skb x 32 rows] = K Q^T: 9 MFMAs.  An MFMA may still read
+                // its operands after it is issued and a returning LDS load is not held back,
+                // so the K fragments go round a ring of three, read two ahead into the
+                // registers of the k-step before once k-step k's MFMA is issued (kept live
+                // until then).
                 v16f sc = v16f{0};
                 {
                     const uint8_t *kp0 = slot + 32 * skb * kKDim + k_off[0];
                     const uint8_t *kp1 = slot + 32 * skb * kKDim + k_off[1];
-                    v8i kf0 = lds_read2x16(kp0, kp1);
-                    v8i kf1 = lds_read2x16(kp0 + 64, kp1 + 64);
+                    v8i kf[3];
+                    kf[0] = lds_read2x16(kp0, kp1);
+                    kf[1] = lds_read2x16(kp0 + 64, kp1 + 64);
                     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int k = 0; k < 9; ++k) {
-                        const v8i cur = (k & 1) ? kf1 : kf0;
-                        if (k + 2 < 9) {
-                            if (k & 1)
-                                kf1 = lds_read2x16(kp0 + 64 * (k + 2), kp1 + 64 * (k + 2));
-                            else
-                                kf0 = lds_read2x16(kp0 + 64 * (k + 2), kp1 + 64 * (k + 2));
-                        }
-                        sc = mfma(cur, qf[k], sc);
+                    static_for<0, 9>([&](auto kk) {
+                        constexpr int k = decltype(kk)::value;
+                        sc = mfma(kf[k % 3], qf[k], sc);
                         __builtin_amdgcn_sched_barrier(0);
-                    }
+                        if constexpr (k >= 1) asm volatile("" ::"v"(kf[(k - 1) % 3]));
+                        if constexpr (k + 2 < 9)
+                            kf[(k + 2) % 3] = lds_read2x16(kp0 + 64 * (k + 2), kp1 + 64 * (k + 2));
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
                 }
                 // keys of the page the row sees, counted from this lane's first key
                 // (32 skb + 4 half): element e holds key 8(e/4) + e%4 past it
@@ -406,15 +408,22 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                     }
                     return f;
                 };
-                v8i vf = vtile(0);
+                // (V^T fragments round a ring of three as the K fragments above; the last
+                // MFMA's operands stay live for 64 cycles after it)
+                v8i vr[3];
+                vr[0] = vtile(0);
+                vr[1] = vtile(1);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    const v8i cur = vf;
-                    if (n + 1 < NT) vf = vtile(n + 1);
-                    acc[n] = mfma_scaled_b(cur, pf, acc[n], sb);
+                static_for<0, NT>([&](auto nn) {
+                    constexpr int n = decltype(nn)::value;
+                    acc[n] = mfma_scaled_b(vr[n % 3], pf, acc[n], sb);
                     __builtin_amdgcn_sched_barrier(0);
-                }
+                    if constexpr (n >= 1) asm volatile("" ::"v"(vr[(n - 1) % 3]));
+                    if constexpr (n + 2 < NT) vr[(n + 2) % 3] = vtile(n + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                             "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::"v"(vr[(NT - 1) % 3]), "v"(pf));
                 if (cv.e == u.size) {
                     // the unit's last page: normalise and store the row block's FP32 partial
                     // (this wave's dims) and the log2 LSE; l and lq carry P's 2^kPExp, which
