@@ -12,11 +12,12 @@
 //   score waves (0-3)  wave (rb, kb) computes S^T for key block kb (keys [32kb, +32) of the
 //                      page) and the 32 rows of row block rb, the key block's softmax and
 //                      its half of the E4M3 P^T fragment, published in LDS (double
-//                      buffered); they also issue the ring's DMA.  MT = 32 has one row block:
-//                      waves 2, 3 repeat waves 0, 1, which alone publish.
+//                      buffered).  MT = 32 has one row block: waves 2, 3 repeat waves 0, 1,
+//                      which alone publish.
 //   value waves (4-7)  one entry behind, O^T += V^T P^T for one row block and NT 32-dim
 //                      tiles (MT = 64: 256 dims, MT = 32: 128 dims), and the unit's FP32
-//                      partial and log2 LSE.
+//                      partial and log2 LSE; they also issue the ring's DMA (a wave stalls
+//                      on DMA issue, and the value waves have the slack).
 // One barrier per entry (plus one at a unit's first page, where the two key blocks agree on
 // the row reference).
 //
@@ -147,44 +148,6 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
         const int skb = MT == 64 ? (wave >> 1) : (wave & 1);
         const bool writer = MT == 64 || wave < 2;
 
-        // ---- issue side: two entries ahead of this role's entry
-        const DmaOffsets dmao = dma_offsets(wave, lane);
-        const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
-        bool page_bad = false;
-        Cursor ci;
-        cursor_init(ci, false);
-        int issued = 0;
-        int32_t pid_next = 0;
-        auto prefetch_pid = [&]() {
-            const int t = ci.e >= 1 ? ci.e - 1 : 0;   // the page of the next page entry
-            if (ci.u < units)
-                pid_next = ldc(&block_table[(size_t)ci.d.r * a.bt_stride + ci.d.first +
-                                            (t < ci.d.size ? t : ci.d.size - 1)]);
-        };
-        prefetch_pid();
-        auto issue_next = [&]() {
-            if (ci.u >= units) return;
-            const uint32_t dst = lds_base + (uint32_t)(issued % kSlots) * kPageBytes;
-            if (ci.e == 0) {
-                const int rows = M - ci.d.jt * MT;
-                issue_rows(q_in + ((size_t)ci.d.r * M + (size_t)ci.d.jt * MT) * kKDim, dst,
-                           rows < MT ? rows : MT, dmao, wave, lane);
-            } else {
-                const int t = ci.e - 1;
-                int32_t pid = pid_next;
-                if (pid < 0 || pid >= a.pool_pages) {
-                    page_bad = true;
-                    pid = 0;
-                }
-                const int valid = ci.d.L - (ci.d.first + t) * kPage;
-                issue_rows(kv_in + (int64_t)pid * kPageBytes, dst, valid < kPage ? valid : kPage,
-                           dmao, wave, lane);
-            }
-            ++issued;
-            cursor_advance(ci, false);
-            prefetch_pid();
-        };
-
         // K and Q fragment reads: key 32 skb + l32 / row 32 srb + l32, chunks 4k + 2*half + e
         // (rows 32 apart share the swizzle)
         int k_off[2];
@@ -203,21 +166,12 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
 
         Cursor cs;
         cursor_init(cs, true);
-        issue_next();
-        issue_next();
         for (int step = 0;; ++step) {
             const bool have = cs.u < units;
-            // this role's entry has landed (every score wave waits for its own DMA share)
-            // and every wave is done with the entry two before it, whose slot is refilled
-            if (have) {
-                if (issued - step - 1 >= 1)
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kChunksPerWave, 0));
-                else
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-            }
+            // the value waves wait for this step's entry; this wave's LDS traffic is done
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
             asm volatile("s_barrier" ::: "memory");
             if (!have) break;
-            issue_next();
             const uint8_t *slot = lds + (step % kSlots) * kPageBytes;
             const Unit &u = cs.d;
             if (cs.e == 0) {
@@ -341,7 +295,6 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
             }
             cursor_advance(cs, true);
         }
-        if (page_bad && lane == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
     } else {
         // ================================================================ value waves
         const int vwv = wave - 4;
@@ -360,13 +313,80 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
         for (int par = 0; par < 2; ++par)
             tr_off[par] = tr_key * kKDim + 16 * ((2 * par + (g16 & 1)) ^ swz(tr_key)) +
                           8 * (i16 & 1) + 64 * (tile0 >> 1);
+        // ---- the ring's DMA, two entries ahead of the score waves' entry (the value waves
+        // have the slack: their P V MFMAs are half of a step's)
+        const DmaOffsets dmao = dma_offsets(vwv, lane);
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + vwv * (kChunksPerWave * 1024);
+        bool page_bad = false;
+        Cursor ci;
+        cursor_init(ci, false);
+        int issued = 0;
+        int32_t pid_next = 0;
+        auto prefetch_pid = [&]() {
+            const int t = ci.e >= 1 ? ci.e - 1 : 0;   // the page of the next page entry
+            if (ci.u < units)
+                pid_next = ldc(&block_table[(size_t)ci.d.r * a.bt_stride + ci.d.first +
+                                            (t < ci.d.size ? t : ci.d.size - 1)]);
+        };
+        prefetch_pid();
+        // The next entry's DMA, right after the barrier that frees its slot (the sooner it is
+        // issued, the more of the HBM latency it hides): prepare_next issues its scalar loads
+        // (the cursor's next unit, the block-table entry after it) first, then dma_all its nine
+        // DMA instructions, which stall the wave a while, so that the scalar loads are back by
+        // the next LDS wait (every LDS wait is a full one while a scalar load is in flight).
+        // Each is called from one place in the loop: every inlined copy of the cursor code
+        // adds registers next to the output tiles.
+        bool dma_on = false;
+        const uint8_t *dma_base = kv_in;
+        uint32_t dma_dst = 0;
+        int dma_valid = kPage;
+        auto prepare_next = [&]() {
+            dma_on = ci.u < units;
+            if (!dma_on) return;
+            dma_dst = lds_base + (uint32_t)(issued % kSlots) * kPageBytes;
+            if (ci.e == 0) {
+                const int rows = M - ci.d.jt * MT;
+                dma_base = q_in + ((size_t)ci.d.r * M + (size_t)ci.d.jt * MT) * kKDim;
+                dma_valid = rows < MT ? rows : MT;
+            } else {
+                const int t = ci.e - 1;
+                int32_t pid = pid_next;
+                if (pid < 0 || pid >= a.pool_pages) {
+                    page_bad = true;
+                    pid = 0;
+                }
+                const int v = ci.d.L - (ci.d.first + t) * kPage;
+                dma_base = kv_in + (int64_t)pid * kPageBytes;
+                dma_valid = v < kPage ? v : kPage;
+            }
+            ++issued;
+            cursor_advance(ci, false);
+            prefetch_pid();
+        };
+        auto dma_all = [&]() {
+            if (dma_on) issue_rows(dma_base, dma_dst, dma_valid, dmao, vwv, lane);
+        };
         v16f acc[NT];
         Cursor cv;
         cursor_init(cv, false);
+        prepare_next();
+        dma_all();
+        prepare_next();
+        dma_all();
         for (int step = 0;; ++step) {
             // step s: this role's entry is the one the score waves took at step s - 1
             if (step > 0 && cv.u >= units) break;
+            // the score waves' entry of this step has landed (every value wave waits for its
+            // own DMA share) and every wave is done with the entry two before it, whose slot
+            // is refilled after the barrier
+            if (issued > step && issued - step - 1 >= 1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(kChunksPerWave, 0));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
             asm volatile("s_barrier" ::: "memory");
+            // the ring refill, before the step's first LDS wait
+            prepare_next();
+            dma_all();
             if (step == 0) continue;
             const Unit &u = cv.d;
             if (cv.e == 0) {
@@ -382,9 +402,9 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                 // half h supplies the scale of K block h of its column: 2^gap of key block h)
                 const v8i pf = *(const v8i *)&xch_p[buf][prb][lane][0];
                 int g_own = xch_gap[buf][prb][half][l32];
+                const int gl0 = xch_gap[buf][prb][0][l32], gl1 = xch_gap[buf][prb][1][l32];
                 {
-                    const int g0 = xch_gap[buf][prb][0][l32], g1 = xch_gap[buf][prb][1][l32];
-                    const int gmax = g0 > g1 ? g0 : g1;
+                    const int gmax = gl0 > gl1 ? gl0 : gl1;
                     if (__any(gmax > kRefGap)) {
                         // the score waves move the reference up by the larger gap (see
                         // there): O follows, before this page is added
@@ -430,18 +450,22 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                     // cancels in O / lq
                     // (the sums before the last page, and the last page's relative to the
                     // reference plus its gaps; a move caused by that page applies to all)
-                    const int g0 = xch_gap[buf][prb][0][l32], g1 = xch_gap[buf][prb][1][l32];
+                    // (the row index is an opaque copy here: addresses kept across the page
+                    // loop would be spilled, and a reload waits for the DMA in flight)
+                    int rl = l32;
+                    asm volatile("" : "+v"(rl));
+                    const int g0 = xch_gap[buf][prb][0][rl], g1 = xch_gap[buf][prb][1][rl];
                     const int gmax = g0 > g1 ? g0 : g1;
                     const int d = gmax > kRefGap ? gmax : 0;
                     const float l_tot =
-                        __builtin_amdgcn_ldexpf(xch_l[prb][0][l32] + xch_l[prb][1][l32], -d) +
-                        __builtin_amdgcn_ldexpf(xch_ps[prb][0][l32], g0 - d) +
-                        __builtin_amdgcn_ldexpf(xch_ps[prb][1][l32], g1 - d);
+                        __builtin_amdgcn_ldexpf(xch_l[prb][0][rl] + xch_l[prb][1][rl], -d) +
+                        __builtin_amdgcn_ldexpf(xch_ps[prb][0][rl], g0 - d) +
+                        __builtin_amdgcn_ldexpf(xch_ps[prb][1][rl], g1 - d);
                     const float lq_tot =
-                        __builtin_amdgcn_ldexpf(xch_lq[prb][0][l32] + xch_lq[prb][1][l32], -d) +
-                        __builtin_amdgcn_ldexpf(xch_qs[prb][0][l32], g0 - d) +
-                        __builtin_amdgcn_ldexpf(xch_qs[prb][1][l32], g1 - d);
-                    const float mref = xch_mref[prb][l32] + (float)d;
+                        __builtin_amdgcn_ldexpf(xch_lq[prb][0][rl] + xch_lq[prb][1][rl], -d) +
+                        __builtin_amdgcn_ldexpf(xch_qs[prb][0][rl], g0 - d) +
+                        __builtin_amdgcn_ldexpf(xch_qs[prb][1][rl], g1 - d);
+                    const float mref = xch_mref[prb][rl] + (float)d;
                     const size_t slot_idx = (size_t)u.off + u.s;
                     const int row = u.jt * MT + 32 * prb + l32;
                     if (row < M) {
@@ -463,6 +487,7 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
             }
             cursor_advance(cv, false);
         }
+        if (page_bad && lane == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
     }
 }
 
