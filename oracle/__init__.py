@@ -58,9 +58,9 @@ def _load():
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p,
                                     ctypes.c_int32]
-        lib.oracle_split_range.restype = ctypes.c_int
-        lib.oracle_split_range.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                           i32p, i32p]
+        lib.oracle_item_range.restype = ctypes.c_int
+        lib.oracle_item_range.argtypes = [i32p, ctypes.c_int32, i32p, ctypes.c_int32,
+                                          ctypes.c_int32, i32p, i32p, i32p]
         _lib = lib
     return _lib
 
@@ -155,7 +155,10 @@ def merge(o, lse):
 
 def plan(lengths, bt_cols, M, MT, W, min_split_tokens=256, max_splits=256, mode=BALANCED,
          list_len=None):
-    """Split plan: (counts int32 [R], offsets int32 [R+1], work int32 [list_len], items)."""
+    """Split plan: (counts int32 [R], offsets int32 [R+1], work int32 [list_len], items).
+
+    work: items in request order as (request, first page) pairs, then the first item of each
+    of the G = max(1, W // ceil(M / MT)) worker groups (G + 1 entries) at 2 * (R + W)."""
     lengths = np.ascontiguousarray(lengths, dtype=np.int32)
     R = lengths.shape[0]
     if list_len is None:
@@ -173,14 +176,24 @@ def plan(lengths, bt_cols, M, MT, W, min_split_tokens=256, max_splits=256, mode=
     return counts, offsets, work[:list_len], n
 
 
-def split_range(length, count, s):
-    """Token range [a, b) of split s of a request of ``length`` keys cut in ``count``."""
-    a = ctypes.c_int32()
-    b = ctypes.c_int32()
-    if _load().oracle_split_range(int(length), int(count), int(s), ctypes.byref(a),
-                                  ctypes.byref(b)) != 0:
-        raise ValueError("oracle_split_range: bad split")
-    return a.value, b.value
+def item_range(work, n, lengths, i):
+    """(request, first token, end token) of item i of a plan's work list of n items."""
+    work = np.ascontiguousarray(work, dtype=np.int32)
+    lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+    r, a, b = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    if _load().oracle_item_range(_ptr(work, ctypes.c_int32), int(n), _ptr(lengths, ctypes.c_int32),
+                                 lengths.shape[0], int(i), ctypes.byref(r), ctypes.byref(a),
+                                 ctypes.byref(b)) != 0:
+        raise ValueError("oracle_item_range: bad item")
+    return r.value, a.value, b.value
+
+
+def group_starts(work, R, W, M, MT):
+    """The first item of each worker group (G + 1 entries) from a plan's work list."""
+    mt = -(-M // MT)
+    G = max(1, W // mt)
+    base = 2 * (R + W)
+    return np.asarray(work[base:base + G + 1], dtype=np.int64)
 
 
 # ------------------------------------------------------------------- fold (host rules)

@@ -204,109 +204,135 @@ void oracle_merge(const double *o, const double *lse, int32_t n, double *out, do
 
 /* ------------------------------------------------------------------- plan */
 
-typedef struct {
-    int32_t size, r, s;
-} oracle_item;
-
-static int oracle_item_order(const void *x, const void *y)
-{
-    const oracle_item *p = (const oracle_item *)x, *q = (const oracle_item *)y;
-    if (p->size != q->size)
-        return p->size > q->size ? -1 : 1; /* longest first */
-    if (p->r != q->r)
-        return p->r < q->r ? -1 : 1; /* ties: the lower request first */
-    return p->s < q->s ? -1 : (p->s > q->s);
-}
-
 /*
- * The split plan (this project's reading; the pages leave the formula open).
+ * The split plan (this project's reading; the pages leave the formula open: per-request
+ * split counts planned from the KV lengths on the device, one wave of persistent workers
+ * walking a work list, fixed equal splits per batch shape as the comparator).
  *
- *   pages_r = ceil(L_r / 64); mt = ceil(M / MT) row tiles per split.
- *   BALANCED: chunk(B) = the smallest c >= 1 with mt * sum_r ceil(pages_r / c) <= B
- *             (c = max pages if none), raised to at least ceil(min_split_tokens / 64);
- *             count_r = min(max_splits, ceil(pages_r / chunk)), with chunk = chunk(W);
- *             but when the longest split, max_r ceil(pages_r / count_r), exceeds 5/4 of the
- *             mean work per worker, mt * sum_r pages_r / W (that is, 4 * longest * W >
- *             5 * mt * total), chunk = chunk(2 W): finer splits, about two per worker,
- *             so that a batch of very different lengths does not wait on its longest
- *             split.
- *   FIXED:    count_r = min(pages_r, clamp(floor(W / (R * mt)), 1, max_splits)).
- *   count_r = 0 when pages_r = 0.
- *   offsets = exclusive prefix sum of counts (workspace slot of (r, s) = offsets[r] + s).
- *   Split s of r covers pages [s*q + min(s, rem), +q + (s < rem)) with q = pages_r / count_r,
- *   rem = pages_r % count_r.
- *   work = (r, s) pairs sorted by split size, longest first, ties by r then s
- *   (the tie rule of the host tiering: page "drafter.attention", _plan_kernel),
- *   then -1 up to list_len.
+ *   pages_r = ceil(L_r / 64); P = sum_r pages_r; mt = ceil(M / MT) row tiles per split; the
+ *   mt row tiles of a split go to the mt workers of one group, G = max(1, floor(W / mt))
+ *   groups; minp = max(1, ceil(min_split_tokens / 64)).
+ *   BALANCED: the requests' pages are laid end to end (request r from off_r, the pages of
+ *     the requests before it) and cut into Gp = min(G, max_splits, max(1, floor(P / minp)))
+ *     ranges at c_g = floor(g * P / Gp), g = 0..Gp.  A cut inside request r (off_r < c_g <
+ *     off_r + pages_r) less than minp pages from the request's start moves to its start,
+ *     less than minp pages from its end moves to its end.  Group g takes the pages between
+ *     its two moved cuts, so every group has P / Gp pages give or take minp; a request's
+ *     splits are its pieces between the moved cuts inside it, each at least minp pages long
+ *     or the whole request.
+ *   FIXED: count_r = min(pages_r, clamp(floor(W / (R * mt)), 1, max_splits)) equal splits,
+ *     split s covering pages [s*q + min(s, rem), +q + (s < rem)), q = pages_r / count_r,
+ *     rem = pages_r % count_r; group g takes items [floor(g * N / G), floor((g+1) * N / G)).
+ *   count_r = 0 when pages_r = 0.  offsets = exclusive prefix sum of counts.  Items are in
+ *   request order, item offsets[r] + s being split s of request r (and its workspace slot):
+ *   work[2i] = r, work[2i+1] = its first page (i < N), then -1 up to 2 * (R + W); then
+ *   work[2 * (R + W) + g] = the first item of group g, g = 0..G (group g takes items
+ *   [that, the next group's)); the rest of the list is -1.  Item i covers pages
+ *   [first_i, first_{i+1}) when item i+1 is of the same request, else [first_i, pages_r).
  *
- * Returns the number of items, -1 on invalid arguments (negative length,
- * pages_r > bt_cols, bad sizes), -2 if list_len < 2 * items.
+ * Returns N, the number of items, -1 on invalid arguments (negative length, pages_r >
+ * bt_cols, bad sizes), -2 if list_len < 2 * (R + 2 * W).
  */
-/* The smallest chunk c >= 1 with mt * sum_r ceil(pages_r / c) <= budget (the longest
-   request's pages if none), raised to min_pages; by trying every c in turn. */
-static int32_t oracle_chunk(const int32_t *lengths, int32_t R, int32_t mt, int64_t pmax,
-                            int64_t budget, int32_t min_pages)
-{
-    int32_t chunk = (int32_t)(pmax > 0 ? pmax : 1);
-    for (int64_t c = 1; c <= pmax; ++c) {
-        int64_t units = 0;
-        for (int32_t r = 0; r < R; ++r) {
-            int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-            units += mt * ((pages + c - 1) / c);
-        }
-        if (units <= budget) {
-            chunk = (int32_t)c;
-            break;
-        }
-    }
-    return chunk < min_pages ? min_pages : chunk;
-}
-
 int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, int32_t MT,
                 int32_t W, int32_t min_split_tokens, int32_t max_splits, int32_t mode,
                 int32_t *counts, int32_t *offsets, int32_t *work, int32_t list_len)
 {
-    int64_t pmax = 0, n = 0;
-    int32_t mt, min_pages, chunk;
-    oracle_item *items;
+    int64_t P = 0, n = 0, G, minp, mt;
+    int64_t *pages, *off, *cut = NULL;
+    int32_t *gstart;
 
     if (R < 0 || M < 1 || MT < 1 || W < 1 || max_splits < 1 || min_split_tokens < 0 ||
         (mode != 0 && mode != 1))
         return -1;
+    for (int32_t r = 0; r < R; ++r)
+        if (lengths[r] < 0 || ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE > bt_cols)
+            return -1;
+    if ((int64_t)list_len < 2 * ((int64_t)R + 2 * (int64_t)W))
+        return -2;
     mt = (M + MT - 1) / MT;
-    min_pages = (min_split_tokens + ORACLE_PAGE - 1) / ORACLE_PAGE;
-    for (int32_t r = 0; r < R; ++r) {
-        int64_t pages;
-        if (lengths[r] < 0)
-            return -1;
-        pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-        if (pages > bt_cols)
-            return -1;
-        if (pages > pmax)
-            pmax = pages;
+    G = W / mt < 1 ? 1 : W / mt;
+    minp = ((int64_t)min_split_tokens + ORACLE_PAGE - 1) / ORACLE_PAGE;
+    if (minp < 1)
+        minp = 1;
+
+    pages = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R + 1));
+    off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R + 1));
+    if (!pages || !off) {
+        free(pages);
+        free(off);
+        return -1;
     }
+    for (int32_t r = 0; r < R; ++r) {
+        pages[r] = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
+        off[r] = P;
+        P += pages[r];
+    }
+    off[R] = P;
+    for (int32_t k = 0; k < list_len; ++k)
+        work[k] = -1;
+    gstart = work + 2 * ((int64_t)R + W);
 
     if (mode == 0) {
-        int64_t total = 0, longest = 0;
-        chunk = oracle_chunk(lengths, R, mt, pmax, (int64_t)W, min_pages);
-        for (int32_t r = 0; r < R; ++r) {
-            int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-            int64_t c = (pages + chunk - 1) / chunk, size;
-            total += pages;
-            if (pages == 0)
-                continue;
-            if (c > max_splits)
-                c = max_splits;
-            size = (pages + c - 1) / c;
-            if (size > longest)
-                longest = size;
+        int64_t Gp = P / minp;
+        if (Gp < 1)
+            Gp = 1;
+        if (Gp > G)
+            Gp = G;
+        if (Gp > max_splits)
+            Gp = max_splits;
+        /* the moved cuts C_0..C_Gp */
+        cut = (int64_t *)malloc(sizeof(int64_t) * (size_t)(Gp + 1));
+        if (!cut) {
+            free(pages);
+            free(off);
+            return -1;
         }
-        if (4 * longest * (int64_t)W > 5 * (int64_t)mt * total)
-            chunk = oracle_chunk(lengths, R, mt, pmax, 2 * (int64_t)W, min_pages);
+        for (int64_t g = 0; g <= Gp; ++g) {
+            int64_t c = g * P / Gp;
+            cut[g] = c;
+            for (int32_t r = 0; r < R; ++r) {
+                if (off[r] < c && c < off[r] + pages[r]) {       /* inside request r */
+                    if (c - off[r] < minp)
+                        cut[g] = off[r];
+                    else if (off[r] + pages[r] - c < minp)
+                        cut[g] = off[r] + pages[r];
+                    break;
+                }
+            }
+        }
+        /* each request's splits: its pieces between the distinct moved cuts inside it */
         for (int32_t r = 0; r < R; ++r) {
-            int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-            int64_t c = pages == 0 ? 0 : (pages + chunk - 1) / chunk;
-            counts[r] = (int32_t)(c < max_splits ? c : max_splits);
+            int64_t last = -1;
+            offsets[r] = (int32_t)n;
+            counts[r] = 0;
+            if (pages[r] == 0)
+                continue;
+            work[2 * n] = r;
+            work[2 * n + 1] = 0;
+            ++n;
+            counts[r] = 1;
+            for (int64_t g = 0; g <= Gp; ++g) {
+                if (off[r] < cut[g] && cut[g] < off[r] + pages[r] && cut[g] != last) {
+                    work[2 * n] = r;
+                    work[2 * n + 1] = (int32_t)(cut[g] - off[r]);
+                    ++n;
+                    ++counts[r];
+                    last = cut[g];
+                }
+            }
+        }
+        /* group g takes the items starting in [C_g, C_{g+1}) */
+        for (int64_t g = 0; g <= G; ++g) {
+            int64_t first = n;
+            if (g <= Gp) {
+                for (int64_t i = 0; i < n; ++i) {
+                    if (off[work[2 * i]] + work[2 * i + 1] >= cut[g]) {
+                        first = i;
+                        break;
+                    }
+                }
+            }
+            gstart[g] = (int32_t)first;
         }
     } else {
         int64_t fixed = R > 0 ? (int64_t)W / ((int64_t)R * mt) : 1;
@@ -315,57 +341,39 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
         if (fixed > max_splits)
             fixed = max_splits;
         for (int32_t r = 0; r < R; ++r) {
-            int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-            counts[r] = (int32_t)(pages < fixed ? pages : fixed);
+            int64_t c = pages[r] < fixed ? pages[r] : fixed;
+            offsets[r] = (int32_t)n;
+            counts[r] = (int32_t)c;
+            for (int64_t s = 0; s < c; ++s) {
+                int64_t q = pages[r] / c, rem = pages[r] % c;
+                work[2 * n] = r;
+                work[2 * n + 1] = (int32_t)(s * q + (s < rem ? s : rem));
+                ++n;
+            }
         }
-    }
-
-    for (int32_t r = 0; r < R; ++r) {
-        offsets[r] = (int32_t)n;
-        n += counts[r];
+        for (int64_t g = 0; g <= G; ++g)
+            gstart[g] = (int32_t)(g * n / G);
     }
     offsets[R] = (int32_t)n;
-    if (2 * n > list_len)
-        return -2;
-
-    items = (oracle_item *)malloc(sizeof(oracle_item) * (size_t)(n > 0 ? n : 1));
-    if (!items)
-        return -1;
-    n = 0;
-    for (int32_t r = 0; r < R; ++r) {
-        int64_t pages = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-        for (int32_t s = 0; s < counts[r]; ++s) {
-            int64_t q = pages / counts[r], rem = pages % counts[r];
-            items[n].size = (int32_t)(q + (s < rem));
-            items[n].r = r;
-            items[n].s = s;
-            ++n;
-        }
-    }
-    qsort(items, (size_t)n, sizeof(oracle_item), oracle_item_order);
-    for (int32_t k = 0; k < list_len; ++k)
-        work[k] = -1;
-    for (int64_t k = 0; k < n; ++k) {
-        work[2 * k] = items[k].r;
-        work[2 * k + 1] = items[k].s;
-    }
-    free(items);
+    free(cut);
+    free(pages);
+    free(off);
     return (int32_t)n;
 }
 
-/* The token range [*a, *b) of split s of request r under a plan (counts). */
-int oracle_split_range(int32_t length, int32_t count, int32_t s, int32_t *a, int32_t *b)
+/* The request and token range [*a, *b) of item i of a plan (work list of N items). */
+int oracle_item_range(const int32_t *work, int32_t N, const int32_t *lengths, int32_t R,
+                      int32_t i, int32_t *r, int32_t *a, int32_t *b)
 {
-    int64_t pages = ((int64_t)length + ORACLE_PAGE - 1) / ORACLE_PAGE;
-    int64_t q, rem, first, size, end;
-    if (count < 1 || s < 0 || s >= count || length < 0)
+    int64_t pages, end;
+    if (i < 0 || i >= N || work[2 * i] < 0 || work[2 * i] >= R)
         return -1;
-    q = pages / count;
-    rem = pages % count;
-    first = s * q + (s < rem ? s : rem);
-    size = q + (s < rem);
-    end = (first + size) * ORACLE_PAGE;
-    *a = (int32_t)(first * ORACLE_PAGE);
-    *b = (int32_t)(end < length ? end : length);
+    *r = work[2 * i];
+    pages = ((int64_t)lengths[*r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
+    end = (i + 1 < N && work[2 * i + 2] == *r) ? work[2 * i + 3] : pages;
+    if (work[2 * i + 1] < 0 || work[2 * i + 1] >= end || end > pages)
+        return -1;
+    *a = work[2 * i + 1] * ORACLE_PAGE;
+    *b = (int32_t)(end * ORACLE_PAGE < lengths[*r] ? end * ORACLE_PAGE : lengths[*r]);
     return 0;
 }

@@ -32,13 +32,16 @@ MUTANTS = {
     "exponent bias": ("exponent - 7);", "exponent - 8);"),
     "sign dropped": ("return sign ? -magnitude : magnitude;", "return magnitude;"),
     "merge weight base": ("double w = exp2(lse[s] - *lse_out);", "double w = exp(lse[s] - *lse_out);"),
-    "plan ties by request descending": ("return p->r < q->r ? -1 : 1;", "return p->r > q->r ? -1 : 1;"),
-    "plan shortest first": ("return p->size > q->size ? -1 : 1;", "return p->size < q->size ? -1 : 1;"),
-    "plan ignores min split": ("return chunk < min_pages ? min_pages : chunk;", "return chunk;"),
-    "plan never rebalances": ("if (4 * longest * (int64_t)W > 5 * (int64_t)mt * total)",
-                              "if (0)"),
-    "split remainder to the end": ("items[n].size = (int32_t)(q + (s < rem));",
-                                   "items[n].size = (int32_t)(q + (s >= count_r_dummy));"),
+    "plan cut not moved to the request start": ("cut[g] = off[r];", "cut[g] = c;"),
+    "plan cut not moved to the request end": ("cut[g] = off[r] + pages[r];", "cut[g] = c;"),
+    "plan ignores min split": ("int64_t Gp = P / minp;", "int64_t Gp = P;"),
+    "plan ignores max splits": ("if (Gp > max_splits)\n            Gp = max_splits;", ""),
+    "plan cuts rounded up": ("int64_t c = g * P / Gp;", "int64_t c = (g * P + Gp - 1) / Gp;"),
+    "plan group start off by one": ("work[2 * i + 1] >= cut[g])", "work[2 * i + 1] > cut[g])"),
+    "fixed groups rounded up": ("gstart[g] = (int32_t)(g * n / G);",
+                                "gstart[g] = (int32_t)((g * n + G - 1) / G);"),
+    "fixed remainder to the end": ("(int32_t)(s * q + (s < rem ? s : rem));", "(int32_t)(s * q);"),
+    "item range ends a page early": ("work[2 * i + 3] : pages;", "work[2 * i + 3] : pages - 1;"),
 }
 
 PIN_TESTS = [
@@ -51,9 +54,12 @@ PIN_TESTS = [
     lambda: pins.test_split_merge_equals_no_split(0),
     pins.test_merge_two_equal_halves,
     plan_pins.test_plan_worked_example_two_requests,
+    plan_pins.test_plan_worked_example_cuts_inside_a_request,
+    plan_pins.test_plan_worked_example_moved_cuts,
+    plan_pins.test_plan_worked_example_row_tiles_and_max_splits,
+    plan_pins.test_plan_fixed_mode,
     lambda: plan_pins.test_plan_properties_random(3),
     plan_pins.test_plan_exhaustive_small,
-    plan_pins.test_plan_rebalances_a_skewed_batch,
 ]
 
 
@@ -61,10 +67,6 @@ def build_mutant(tmp_path, old, new):
     src = open(SRC).read()
     assert old in src, old
     src = src.replace(old, new, 1)
-    if "count_r_dummy" in new:
-        src = src.replace("int64_t q = pages / counts[r], rem = pages % counts[r];",
-                          "int64_t q = pages / counts[r], rem = pages % counts[r];"
-                          " int64_t count_r_dummy = counts[r] - rem;", 1)
     c = tmp_path / "mutant.c"
     so = tmp_path / "libmutant.so"
     c.write_text(src)
@@ -80,7 +82,7 @@ def test_pins_catch_mutant(name, tmp_path, monkeypatch):
     real = oracle._load()
     mutant = ctypes.CDLL(path)
     for fn in ("oracle_e4m3_value", "oracle_e4m3_table", "oracle_attend", "oracle_merge",
-               "oracle_plan", "oracle_split_range"):
+               "oracle_plan", "oracle_item_range"):
         f = getattr(mutant, fn)
         f.restype = getattr(real, fn).restype
         f.argtypes = getattr(real, fn).argtypes

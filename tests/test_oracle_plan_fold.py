@@ -1,11 +1,13 @@
 """Pins of the oracle's split plan and of the host fold rules.
 
 The fold rules are pinned by the worked examples the pages print (tests/golden).  The
-split plan is this project's reading of a rule the pages leave open; it is pinned by a
-hand-worked example and by the properties that define it: the splits tile each
-request's pages, split sizes of a request differ by at most one, the work list is
-ordered longest first with the pages' tie rule, and no uniform chunk size could have met
-the worker budget with shorter splits (checked by exhaustive search).
+split plan is this project's reading of a rule the pages leave open (the lengths laid end
+to end and cut into equal page ranges, one per worker group, each cut moved to the nearer
+request boundary when it would leave a piece shorter than the minimum split); it is pinned
+by hand-worked examples and by the properties that define it, checked exhaustively on
+small batches: the items tile every request in request order, every piece is at least the
+minimum split or a whole request, the group boundaries are the cuts at g * P / Gp or the
+request boundary within a minimum split of one, and a cut only moves when it must.
 """
 import itertools
 import os
@@ -58,82 +60,155 @@ def pages_of(lengths):
     return [(int(L) + 63) // 64 for L in lengths]
 
 
+def groups_of(W, M, MT):
+    return max(1, W // -(-M // MT))
+
+
+def pieces(work, n, lengths):
+    """Items as (request, first page, end page) from the work pairs: an item ends where the
+    next item of its request starts, the last one at the request's end."""
+    pages = pages_of(lengths)
+    out = []
+    for i in range(n):
+        r, f = int(work[2 * i]), int(work[2 * i + 1])
+        nxt = int(work[2 * i + 3]) if i + 1 < n and int(work[2 * i + 2]) == r else pages[r]
+        out.append((r, f, nxt))
+    return out
+
+
 def check_plan(lengths, M, MT, W, min_tokens=256, max_splits=256, mode=oracle.BALANCED):
+    """Every property of a plan that holds in both modes, plus the group rule of each mode;
+    returns (counts, offsets, work, n, items, gstart)."""
+    lengths = list(lengths)
     R = len(lengths)
     counts, offsets, work, n = oracle.plan(lengths, max(pages_of(lengths) + [1]), M, MT, W,
                                            min_tokens, max_splits, mode)
     pages = pages_of(lengths)
-    mt = -(-M // MT)
+    P = sum(pages)
+    G = groups_of(W, M, MT)
+    minp = max(1, -(-min_tokens // 64))
     assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts) and offsets[R] == n
-    assert n <= R + 2 * W
-    sizes = {}
+    assert n <= R + W
+    assert np.all(work[2 * n:2 * (R + W)] == -1) and np.all(work[2 * (R + W) + G + 1:] == -1)
+    items = pieces(work, n, lengths)
+    # request order; every request with keys covered by its items, end to end
     for r in range(R):
+        mine = items[offsets[r]:offsets[r + 1]]
+        assert all(it[0] == r for it in mine)
         if pages[r] == 0:
             assert counts[r] == 0
             continue
         assert 1 <= counts[r] <= min(max_splits, pages[r])
-        covered = []
-        for s in range(counts[r]):
-            a, b = oracle.split_range(lengths[r], counts[r], s)
-            assert a % 64 == 0 and a < b <= lengths[r]
-            covered.append((a, b))
-            sizes[(r, s)] = (-(-b // 64)) - a // 64
-        assert covered[0][0] == 0 and covered[-1][1] == lengths[r]
-        assert all(x[1] == y[0] for x, y in zip(covered, covered[1:]))
-        szs = [sizes[(r, s)] for s in range(counts[r])]
-        assert sum(szs) == pages[r] and max(szs) - min(szs) <= 1
-    pairs = [(int(work[2 * i]), int(work[2 * i + 1])) for i in range(n)]
-    assert sorted(pairs) == sorted(sizes)
-    keys = [(-sizes[p], p[0], p[1]) for p in pairs]
-    assert keys == sorted(keys)
-    assert np.all(work[2 * n:] == -1)
-    return counts, offsets, work, n, sizes, mt
+        assert mine[0][1] == 0 and mine[-1][2] == pages[r]
+        assert all(x[2] == y[1] and x[1] < x[2] for x, y in zip(mine, mine[1:] + [(r, pages[r], 0)]))
+        for k, (_, f, e) in enumerate(mine):
+            assert oracle.item_range(work, n, lengths, offsets[r] + k) == \
+                (r, 64 * f, min(64 * e, lengths[r]))
+    gstart = oracle.group_starts(work, R, W, M, MT).tolist()
+    assert len(gstart) == G + 1 and gstart[0] == 0 and gstart[-1] == n
+    assert all(x <= y for x, y in zip(gstart, gstart[1:]))
+    if mode == oracle.FIXED:
+        # equal splits: sizes of a request differ by at most one, the longer ones first
+        for r in range(R):
+            sz = [e - f for _, f, e in items[offsets[r]:offsets[r + 1]]]
+            assert sz == sorted(sz, reverse=True) and (not sz or sz[0] - sz[-1] <= 1)
+        assert gstart == [g * n // G for g in range(G + 1)]
+        return counts, offsets, work, n, items, gstart
+    # BALANCED: pieces at least the minimum split unless whole requests
+    assert all(e - f >= minp or (f == 0 and e == pages[r]) for r, f, e in items)
+    Gp = max(1, min(G, max_splits, P // minp))
+    assert all(g == n for g in gstart[Gp:])
+    # group g takes the pages [B_g, B_{g+1}): B_g is the start of its first item (P if none)
+    starts = [sum(pages[:r]) + f for r, f, _ in items]
+    bounds = [starts[i] if i < n else P for i in gstart[:Gp + 1]]
+    off = [sum(pages[:r]) for r in range(R)] + [P]
+    for g, B in enumerate(bounds):
+        c = g * P // Gp
+        inside = [r for r in range(R) if off[r] < c < off[r] + pages[r]]
+        if not inside:
+            assert B == c
+        else:
+            r = inside[0]
+            if c - off[r] < minp:
+                assert B == off[r]
+            elif off[r] + pages[r] - c < minp:
+                assert B == off[r] + pages[r]
+            else:
+                assert B == c
+    # a request's splits start exactly at the group boundaries strictly inside it
+    for r in range(R):
+        if pages[r]:
+            cuts = sorted({B - off[r] for B in bounds if off[r] < B < off[r] + pages[r]})
+            assert [f for _, f, _ in items[offsets[r]:offsets[r + 1]]] == [0] + cuts
+    return counts, offsets, work, n, items, gstart
 
 
 def test_plan_worked_example_two_requests():
-    # pages [4, 5]; one row tile; the 4-page minimum sets the chunk: counts [1, 2]
+    # pages [4, 5] (P = 9), minimum split 4 pages: Gp = min(256, 9 // 4) = 2 groups, cut at
+    # 9 // 2 = 4, the boundary between the requests: one item each
     counts, offsets, work, n = oracle.plan([200, 317], 5, M=32, MT=32, W=256)
-    assert counts.tolist() == [1, 2] and offsets.tolist() == [0, 1, 3] and n == 3
-    assert oracle.split_range(200, 1, 0) == (0, 200)
-    assert oracle.split_range(317, 2, 0) == (0, 192)
-    assert oracle.split_range(317, 2, 1) == (192, 317)
-    assert work[:6].tolist() == [0, 0, 1, 0, 1, 1] and np.all(work[6:] == -1)
+    assert counts.tolist() == [1, 1] and offsets.tolist() == [0, 1, 2] and n == 2
+    assert work[:4].tolist() == [0, 0, 1, 0] and np.all(work[4:2 * (2 + 256)] == -1)
+    g = oracle.group_starts(work, 2, 256, 32, 32)
+    assert g[:3].tolist() == [0, 1, 2] and np.all(g[3:] == 2) and len(g) == 257
+    assert oracle.item_range(work, n, [200, 317], 1) == (1, 0, 317)
+
+
+def test_plan_worked_example_cuts_inside_a_request():
+    # pages [7, 1], 4 groups, minimum 1 page: cuts at 0, 2, 4, 6, 8, three of them inside
+    # request 0; group 3 takes the last page of request 0 and request 1
+    counts, offsets, work, n = oracle.plan([7 * 64, 64], 8, M=32, MT=32, W=4, min_split_tokens=0)
+    assert counts.tolist() == [4, 1] and offsets.tolist() == [0, 4, 5] and n == 5
+    assert work[:10].tolist() == [0, 0, 0, 2, 0, 4, 0, 6, 1, 0]
+    assert np.all(work[10:12] == -1)
+    assert work[12:17].tolist() == [0, 1, 2, 3, 5] and np.all(work[17:] == -1)
+    assert oracle.item_range(work, n, [7 * 64, 64], 3) == (0, 384, 448)
+
+
+def test_plan_worked_example_moved_cuts():
+    # pages [5, 3], 4 groups, minimum 2 pages: cuts 2, 4, 6; cut 4 leaves 1 page at the end
+    # of request 0 and moves to its end (5); cut 6 leaves 1 page at the start of request 1
+    # and moves to its start (5): group 2 is empty
+    counts, offsets, work, n = oracle.plan([5 * 64, 3 * 64 - 10], 5, M=32, MT=32, W=4,
+                                           min_split_tokens=128)
+    assert counts.tolist() == [2, 1] and n == 3
+    assert work[:6].tolist() == [0, 0, 0, 2, 1, 0]
+    assert oracle.group_starts(work, 2, 4, 32, 32).tolist() == [0, 1, 2, 2, 3]
+    assert oracle.item_range(work, n, [320, 182], 2) == (1, 0, 182)
+
+
+def test_plan_worked_example_row_tiles_and_max_splits():
+    # 448 rows in 128-row tiles: 4 workers per group, 8 workers -> 2 groups; one request of
+    # 10 pages: one cut at 5
+    counts, _, work, n = oracle.plan([640], 10, M=448, MT=128, W=8, min_split_tokens=0)
+    assert counts.tolist() == [2] and work[:4].tolist() == [0, 0, 0, 5]
+    assert oracle.group_starts(work, 1, 8, 448, 128).tolist() == [0, 1, 2]
+    # at most 3 splits: Gp = 3, cuts at 3 and 6
+    counts, _, work, n = oracle.plan([640], 10, M=32, MT=32, W=8, min_split_tokens=0,
+                                     max_splits=3)
+    assert counts.tolist() == [3] and work[:6].tolist() == [0, 0, 0, 3, 0, 6]
+    assert oracle.group_starts(work, 1, 8, 32, 32).tolist() == [0, 1, 2, 3, 3, 3, 3, 3, 3]
 
 
 def test_plan_uniform_batch_fills_workers():
-    # 64 requests x 128 pages, 256 workers: 4 splits of 32 pages each
-    counts, offsets, work, n = oracle.plan([8192] * 64, 128, M=32, MT=32, W=256)
-    assert np.all(counts == 4) and n == 256
+    # 64 requests x 128 pages, 256 groups of 32 pages: 4 equal splits per request
+    counts, offsets, work, n, items, gstart = check_plan([8192] * 64, M=32, MT=32, W=256)
+    assert np.all(counts == 4) and n == 256 and gstart == list(range(257))
+    assert all(e - f == 32 for _, f, e in items)
 
 
 def test_plan_fixed_mode():
     rng = np.random.default_rng(0)
     lengths = np.floor(np.exp(rng.uniform(np.log(512), np.log(65536), 128))).astype(np.int32)
-    counts, *_ = oracle.plan(lengths, 1024, M=56, MT=64, W=256, mode=oracle.FIXED)
+    counts, *_ = check_plan(lengths, M=56, MT=64, W=256, mode=oracle.FIXED)
     assert np.all(counts == 2)                  # floor(256 / 128) splits, every request
-    counts, *_ = oracle.plan([64, 10000], 200, M=32, MT=32, W=256, mode=oracle.FIXED)
+    counts, *_ = check_plan([64, 10000], M=32, MT=32, W=256, mode=oracle.FIXED)
     assert counts.tolist() == [1, 128]          # never more splits than pages
-
-
-def best_uniform_chunk(pages, mt, W, min_pages, max_splits):
-    """Exhaustive: the shortest longest-split over every uniform chunk that fits W."""
-    best = None
-    for c in range(1, max(pages + [1]) + 1):
-        cc = max(c, min_pages)
-        cnt = [0 if p == 0 else min(max_splits, -(-p // cc)) for p in pages]
-        if mt * sum(cnt) <= W:
-            longest = max([-(-p // k) for p, k in zip(pages, cnt) if k] + [0])
-            best = longest if best is None else min(best, longest)
-    return best
-
-
-def expected_longest(pages, mt, W, min_pages, max_splits):
-    """The plan's longest split by exhaustive search: the best uniform chunk within W
-    workers, or within 2W when that longest split exceeds 5/4 of the mean per worker."""
-    best = best_uniform_chunk(pages, mt, W, min_pages, max_splits)
-    if best is not None and 4 * best * W > 5 * mt * sum(pages):
-        best = best_uniform_chunk(pages, mt, 2 * W, min_pages, max_splits)
-    return best
+    # pages [5, 2, 0], 8 workers: 2 splits each (3 + 2 pages, 1 + 1), groups floor(g * 4 / 8)
+    counts, offsets, work, n = oracle.plan([300, 128, 0], 5, M=32, MT=32, W=8, mode=oracle.FIXED)
+    assert counts.tolist() == [2, 2, 0] and offsets.tolist() == [0, 2, 4, 4]
+    assert work[:8].tolist() == [0, 0, 0, 3, 1, 0, 1, 1]
+    assert oracle.group_starts(work, 3, 8, 32, 32).tolist() == [0, 0, 1, 1, 2, 2, 3, 3, 4]
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -146,12 +221,24 @@ def test_plan_properties_random(seed):
     MT = 32 if M <= 32 else (64 if M <= 64 else 128)
     W = int(rng.choice([8, 64, 256]))
     min_tokens = int(rng.choice([0, 64, 256, 1000]))
-    counts, offsets, work, n, sizes, mt = check_plan(lengths, M, MT, W, min_tokens)
-    pages = pages_of(lengths)
-    best = expected_longest(pages, mt, W, -(-min_tokens // 64), 256)
-    longest = max(sizes.values()) if sizes else 0
-    if best is not None:
-        assert longest == best
+    max_splits = int(rng.choice([2, 16, 256]))
+    for mode in (oracle.BALANCED, oracle.FIXED):
+        check_plan(lengths, M, MT, W, min_tokens, max_splits, mode)
+
+
+def test_plan_balance_bound():
+    # every group's pages lie within two minimum splits of P / Gp
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        R = int(rng.integers(1, 200))
+        lengths = np.floor(np.exp(rng.uniform(np.log(64), np.log(65536), R))).astype(np.int64)
+        minp = 4
+        counts, offsets, work, n, items, gstart = check_plan(lengths, 56, 64, 256, 64 * minp)
+        P = sum(pages_of(lengths))
+        Gp = min(256, P // minp)
+        for g in range(Gp):
+            got = sum(e - f for _, f, e in items[gstart[g]:gstart[g + 1]])
+            assert abs(got - P / Gp) < 2 * minp
 
 
 def test_plan_exhaustive_small():
@@ -160,11 +247,8 @@ def test_plan_exhaustive_small():
     for R in (1, 2, 3):
         for lengths in itertools.product(choices, repeat=R):
             for W in (1, 3, 8):
-                counts, offsets, work, n, sizes, mt = check_plan(list(lengths), 32, 32, W, 0)
-                pages = pages_of(lengths)
-                best = expected_longest(pages, 1, W, 0, 256)
-                if best is not None and sizes:
-                    assert max(sizes.values()) == best
+                for min_tokens in (0, 128, 256):
+                    check_plan(list(lengths), 32, 32, W, min_tokens)
                 check_plan(list(lengths), 32, 32, W, 0, mode=oracle.FIXED)
 
 
@@ -174,20 +258,6 @@ def test_plan_rejects_bad_input():
     with pytest.raises(ValueError):
         oracle.plan([64 * 5], 4, 32, 32, 256)          # more pages than table columns
     with pytest.raises(ValueError):
-        oracle.plan([64] * 4, 4, 32, 32, 256, list_len=3)
-
-
-def test_plan_rebalances_a_skewed_batch():
-    # pages [7, 1], 4 workers: chunk(4) = 3 gives splits 3, 2, 2 and 1 page, the longest (3)
-    # above 5/4 of the mean per worker (8 / 4 = 2), so the plan takes chunk(8) = 1: eight
-    # one-page splits, two per worker
-    counts, offsets, work, n = oracle.plan(np.array([7 * 64, 64], np.int32), 8, 32, 32, 4,
-                                           min_split_tokens=0)
-    assert counts.tolist() == [7, 1] and offsets.tolist() == [0, 7, 8] and n == 8
-    assert work[:16].tolist() == [0, 0, 0, 1, 0, 2, 0, 3, 0, 4, 0, 5, 0, 6, 1, 0]
-    assert np.all(work[16:] == -1)
-    # pages [10, 1, 1, 1], 8 workers: chunk(8) = 2, longest 2 against a mean of 13/8 (not
-    # above 5/4 of it): no rebalancing
-    counts, _, _, n = oracle.plan(np.array([640, 64, 64, 64], np.int32), 16, 32, 32, 8,
-                                  min_split_tokens=0)
-    assert counts.tolist() == [5, 1, 1, 1] and n == 8
+        oracle.plan([64] * 4, 4, 32, 32, 256, list_len=2 * (4 + 2 * 256) - 1)
+    with pytest.raises(ValueError):
+        oracle.item_range(np.array([0, 0, 0, 2], np.int32), 2, [64], 0)   # first beyond end
