@@ -20,6 +20,8 @@ UVDIM = 128
 MAX_ROWS = 1024
 MAX_REQS = 4096
 MAX_SPLITS = 256
+MAX_SPLIT_COST = 4096
+SPLIT_COST_DEFAULT = 4   # pages a split costs its worker beyond its own (query rows, partials)
 
 OK = 0
 ERR_INVALID = -1
@@ -54,12 +56,14 @@ class PlanParams(ctypes.Structure):
         ("min_split_tokens", ctypes.c_int32),
         ("max_splits", ctypes.c_int32),
         ("mode", ctypes.c_int32),
+        ("split_cost_pages", ctypes.c_int32),
     ]
 
     def __repr__(self):
         return ("PlanParams(rows_per_req=%d, mtile=%d, workers=%d, min_split_tokens=%d, "
-                "max_splits=%d, mode=%d)" % (self.rows_per_req, self.mtile, self.workers,
-                                             self.min_split_tokens, self.max_splits, self.mode))
+                "max_splits=%d, mode=%d, split_cost_pages=%d)"
+                % (self.rows_per_req, self.mtile, self.workers, self.min_split_tokens,
+                   self.max_splits, self.mode, self.split_cost_pages))
 
 
 class DcpParams(ctypes.Structure):
@@ -171,8 +175,9 @@ def workspace_bytes(num_reqs, rows_per_req, workers):
 
 
 def make_params(rows_per_req, mtile, workers, min_split_tokens=256, max_splits=MAX_SPLITS,
-                mode=PLAN_BALANCED) -> PlanParams:
-    return PlanParams(rows_per_req, mtile, workers, min_split_tokens, max_splits, mode)
+                mode=PLAN_BALANCED, split_cost_pages=SPLIT_COST_DEFAULT) -> PlanParams:
+    return PlanParams(rows_per_req, mtile, workers, min_split_tokens, max_splits, mode,
+                      split_cost_pages)
 
 
 # ----------------------------------------------------------------------- device calls
@@ -274,7 +279,8 @@ class FoldedDecoder:
     BalancedMla)."""
 
     def __init__(self, max_reqs, rows_per_req, device=None, mode=PLAN_BALANCED,
-                 min_split_tokens=256, max_splits=MAX_SPLITS, workers=None, mtile=None):
+                 min_split_tokens=256, max_splits=MAX_SPLITS, workers=None, mtile=None,
+                 split_cost_pages=SPLIT_COST_DEFAULT):
         import torch
 
         load()
@@ -283,7 +289,7 @@ class FoldedDecoder:
         self.compute_units = props.multi_processor_count
         w, mt = decode_config(self.compute_units, rows_per_req)
         self.params = make_params(rows_per_req, mtile or mt, workers or w, min_split_tokens,
-                                  max_splits, mode)
+                                  max_splits, mode, split_cost_pages)
         self.max_reqs = max_reqs
         i32 = dict(dtype=torch.int32, device=self.device)
         self.counts = torch.zeros(max(max_reqs, 1), **i32)

@@ -144,517 +144,191 @@ struct PlanArgs {
     int32_t *work;
     int32_t *header;
     int32_t reqs, bt_cols, rows, mtile, workers, min_pages, max_splits, mode, list_len;
+    int32_t split_cost;
 };
 
 __device__ inline int64_t pages_of(int32_t len) { return ((int64_t)len + kPage - 1) / kPage; }
 
-// Sort key of a run of equal-size splits of request r: size descending, then r ascending.
-__device__ inline uint64_t run_key(int64_t size, int32_t r)
-{
-    return ((uint64_t)(0x7FFFFFFFll - size) << 32) | (uint32_t)r;
-}
-
-// Reduces four values over the workgroup at once (max, max, sum, sum).
-__device__ void block_reduce4(int64_t &mx0, int64_t &mx1, int64_t &sm0, int64_t &sm1,
-                              int64_t (*scratch)[4])
+// Exclusive scan of one int64 per thread (thread order) over the workgroup; the grand
+// total goes to *total.
+__device__ int64_t block_exclusive_scan64(int64_t v, int64_t *scratch, int64_t *total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    mx0 = wave_all64<true>(mx0);
-    mx1 = wave_all64<true>(mx1);
-    sm0 = wave_all64<false>(sm0);
-    sm1 = wave_all64<false>(sm1);
-    if (lane == 0) {
-        scratch[wave][0] = mx0;
-        scratch[wave][1] = mx1;
-        scratch[wave][2] = sm0;
-        scratch[wave][3] = sm1;
+    int64_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
     }
     __syncthreads();
-    mx0 = mx1 = sm0 = sm1 = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
-        mx0 = scratch[w][0] > mx0 ? scratch[w][0] : mx0;
-        mx1 = scratch[w][1] > mx1 ? scratch[w][1] : mx1;
-        sm0 += scratch[w][2];
-        sm1 += scratch[w][3];
+    if (lane == 63) scratch[wave] = incl;
+    __syncthreads();
+    int64_t before = 0, all = 0;
+    for (int i = 0; i < kPlanThreads / 64; ++i) {
+        if (i < wave) before += scratch[i];
+        all += scratch[i];
     }
+    *total = all;
+    return before + incl - v;
 }
 
-constexpr int kRankSortRuns = kPlanThreads;   // rank sort up to this many runs, else bitonic
+// ceil(x / y) for x >= 0, y > 0
+__device__ inline int64_t cdiv64(int64_t x, int64_t y) { return x == 0 ? 0 : (x - 1) / y + 1; }
 
+// The split plan, one workgroup; thread t owns the requests [t * per, (t + 1) * per).
+// BALANCED (page "...cutedsl.mla.balanced", module docstring: split counts planned on the
+// device from the KV lengths, one wave of persistent workers walking a work list; the rule
+// is this library's reading): every non-empty request is laid out as a head of a =
+// split_cost pages (what a split costs beyond its pages) and its pages, end to end, V in
+// all, and V is cut into Gp = min(W / mt, max_splits, V / minp) equal ranges, one per group
+// of mt = ceil(M / MT) workers (one per row tile), at c_g = floor(g V / Gp).  A cut inside
+// request r less than minp pages into its pages (or in its head) moves to its start, less
+// than minp from its end to its end; the others cut it, so the splits of r start at 0 and
+// at the cuts with voff_r + a + minp <= c_g <= voff_r + a + pages_r - minp, which are
+// g = g0(r) .. g1(r) in closed form (the cuts are at least minp apart since V / Gp >= minp).
+// Group g takes the items starting in [C_g, C_{g+1}) of the moved cuts.
+// FIXED: min(pages_r, W / (R mt)) equal splits per request, group g taking items
+// [g N / G, (g + 1) N / G).
+// Work list: (request, first page) per item in request order (item offsets[r] + s is split
+// s of request r and its workspace slot), -1 up to 2 (R + W), the G + 1 group starts, -1.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
 {
-    __shared__ int32_t pg[AMLA_MAX_REQS];            // pages per request
-    __shared__ int32_t cnt[AMLA_MAX_REQS];           // splits per request
-    __shared__ uint64_t keys[kMaxRuns];              // run keys (sorted in place: bitonic)
-    __shared__ uint64_t ranked[kRankSortRuns];       // run keys in order (rank sort)
-    __shared__ int64_t red4[kPlanThreads / 64][4];
+    __shared__ int64_t voff[AMLA_MAX_REQS + 1];    // virtual pages before request r
+    __shared__ int32_t ioff[AMLA_MAX_REQS + 1];    // items before request r
+    __shared__ int64_t red64[kPlanThreads / 64];
     __shared__ int32_t red32[kPlanThreads / 64];
-    __shared__ int32_t ok[2][16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int R = a.reqs;
+    const int per = ceil_div(R > 0 ? R : 1, kPlanThreads);
+    const int r0 = tid * per < R ? tid * per : R, r1 = r0 + per < R ? r0 + per : R;
     const int64_t mt = ceil_div(a.rows, a.mtile);
-    const int64_t budget = (int64_t)a.workers / mt;  // most splits the workers take at once
-    const int64_t budget2 = (int64_t)kPlanSlack * a.workers / mt;
+    const int64_t G = a.workers / mt > 0 ? a.workers / mt : 1;
+    const int64_t minp = a.min_pages > 0 ? a.min_pages : 1;
+    const int64_t head = a.split_cost;
 
-    // 1. pages per request, validity, longest request, total pages, non-empty requests
-    int64_t bad = 0, pmax = 0, total = 0, nz = 0;
-    for (int r = tid; r < R; r += kPlanThreads) {
+    // 1. pages, validity, virtual offsets
+    int64_t mine = 0;
+    int bad_l = 0;
+    for (int r = r0; r < r1; ++r) {
         const int32_t L = a.lengths[r];
         const int64_t p = pages_of(L);
-        const bool b = L < 0 || p > a.bt_cols;
-        bad |= b;
-        pg[r] = b ? 0 : (int32_t)p;
-        pmax = p > pmax ? p : pmax;
-        total += b ? 0 : p;
-        nz += (!b && p > 0);
+        bad_l |= L < 0 || p > a.bt_cols;
+        mine += L <= 0 ? 0 : head + p;
     }
-    block_reduce4(bad, pmax, total, nz, red4);
-
-    // 2. BALANCED: the smallest chunk c with sum_r ceil(pages_r / c) <= budget.  Since
-    //    total/c <= sum <= total/c + nz, it lies in [ceil(total/budget),
-    //    ceil(total/(budget - nz))]; a 16-way search (one candidate per wave) narrows that.
-    // the smallest chunk with sum_r ceil(pages_r / c) <= b, at least the minimum split
-    auto search = [&](int64_t b) {
-        int64_t chunk;
-        __syncthreads();   // the candidate flags of an earlier search are read by now
-        if (b < nz) {
-            chunk = pmax;                         // no chunk fits: one split per request
-        } else {
-            int64_t lo = (total + b - 1) / b, hi = pmax;
-            if (b > nz) {
-                const int64_t h = (total + (b - nz) - 1) / (b - nz);
-                hi = h < hi ? h : hi;
-            }
-            lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
-            constexpr int kCand = 16, kPerWave = kCand / (kPlanThreads / 64);
-            int round = 0;
-            while (lo < hi) {
-                const int64_t span = hi - lo;
-#pragma unroll
-                for (int k = 0; k < kPerWave; ++k) {
-                    const int cand = wave * kPerWave + k;
-                    const uint32_t c = (uint32_t)(lo + span * cand / kCand);
-                    int64_t u = 0;
-                    for (int r = lane; r < R; r += 64) u += ((uint32_t)pg[r] + c - 1u) / c;
-                    u = wave_all64<false>(u);
-                    if (lane == 0) ok[round & 1][cand] = u <= b;
-                }
-                __syncthreads();
-                int first = -1;
-                for (int w = kCand - 1; w >= 0; --w)
-                    if (ok[round & 1][w]) first = w;
-                if (first >= 0) {
-                    const int64_t cf = lo + span * first / kCand;
-                    const int64_t cp = first > 0 ? lo + span * (first - 1) / kCand + 1 : lo;
-                    hi = cf;
-                    lo = cp < cf ? cp : cf;
-                } else {
-                    lo = lo + span * (kCand - 1) / kCand + 1;
-                }
-                ++round;
-            }
-            chunk = hi;
-        }
-        return chunk > a.min_pages ? chunk : (int64_t)a.min_pages;
+    const bool bad = __syncthreads_or(bad_l) != 0;
+    // virtual length of request r (0 for an empty one or a bad batch)
+    auto vlen = [&](int r) -> int64_t {
+        const int32_t L = a.lengths[r];
+        return bad || L <= 0 ? 0 : head + pages_of(L);
     };
-    int64_t chunk = 1, fixed = 1;
-    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
-        chunk = search(budget);
-        // rebalance (see plan_small_kernel): the longest split against the mean per worker
-        int64_t longest = 0;
-        for (int r = tid; r < R; r += kPlanThreads) {
-            const uint32_t p = (uint32_t)pg[r];
-            if (p == 0) continue;
-            uint32_t cc = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
-            cc = cc < (uint32_t)a.max_splits ? cc : (uint32_t)a.max_splits;
-            const int64_t sz = (p + cc - 1u) / cc;
-            longest = sz > longest ? sz : longest;
-        }
-        longest = wave_all64<true>(longest);
-        if (lane == 0) red32[wave] = (int32_t)longest;
-        __syncthreads();
-        longest = 0;
-        for (int w = 0; w < kPlanThreads / 64; ++w) longest = red32[w] > longest ? red32[w] : longest;
-        __syncthreads();   // red32 is reused below
-        if (4 * longest * (int64_t)a.workers > 5 * mt * total) chunk = search(budget2);
-    } else if (!bad && a.mode == AMLA_PLAN_FIXED) {
-        fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
-        fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
+    int64_t V = 0;
+    int64_t run = block_exclusive_scan64(bad ? 0 : mine, red64, &V);
+    for (int r = r0; r < r1; ++r) {
+        voff[r] = run;
+        run += vlen(r);
     }
+    if (tid == 0) voff[R] = V;
 
-    // 3. counts and their exclusive scan: thread t owns requests [t*per, (t+1)*per)
-    const int per = ceil_div(R > 0 ? R : 1, kPlanThreads);
-    int32_t mine = 0;
-    for (int i = 0; i < per; ++i) {
-        const int r = tid * per + i;
-        if (r >= R) break;
-        const uint32_t p = (uint32_t)pg[r];
+    // 2. counts and item offsets
+    int64_t Gp = V / minp;
+    Gp = Gp < 1 ? 1 : Gp;
+    Gp = Gp < G ? Gp : G;
+    Gp = Gp < a.max_splits ? Gp : a.max_splits;
+    int64_t fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
+    fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
+    const bool balanced = a.mode == AMLA_PLAN_BALANCED;
+    // the first and last cut inside the pages of a request whose pages start at virtual
+    // position s (g1 < g0: none)
+    auto cut_range = [&](int64_t s, int64_t p, int64_t &g0, int64_t &g1) {
+        g0 = cdiv64((s + minp) * Gp, V);
+        g1 = cdiv64((s + p - minp + 1) * Gp, V) - 1;
+    };
+    int32_t icount = 0;
+    for (int r = r0; r < r1; ++r) {
+        const int64_t p = bad ? 0 : pages_of(a.lengths[r]);
         int64_t c = 0;
-        if (!bad && p > 0) {
-            if (a.mode == AMLA_PLAN_BALANCED) {
-                c = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
-                c = c < a.max_splits ? c : a.max_splits;
+        if (p > 0) {
+            if (balanced) {
+                int64_t g0, g1;
+                cut_range(voff[r] + head, p, g0, g1);
+                c = 1 + (g1 >= g0 ? g1 - g0 + 1 : 0);
             } else {
-                c = (int64_t)p < fixed ? (int64_t)p : fixed;
+                c = p < fixed ? p : fixed;
             }
         }
-        cnt[r] = (int32_t)c;
         a.counts[r] = (int32_t)c;
-        mine += (int32_t)c;
+        icount += (int32_t)c;
     }
-    int32_t n_items = 0;
-    int32_t run = block_exclusive_scan(mine, red32, &n_items);
-    for (int i = 0; i < per; ++i) {
-        const int r = tid * per + i;
-        if (r >= R) break;
-        a.offsets[r] = run;
-        run += cnt[r];
-    }
-    if (tid == 0) a.offsets[R] = n_items;
+    int32_t N = 0;
+    int32_t irun = block_exclusive_scan(icount, red32, &N);
 
-    // 4. runs of equal-size splits, (q+1) x rem from s = 0 then q x (c-rem) from s = rem,
-    //    keyed (size descending, request ascending), sorted ascending
-    const int runs = 2 * R;
-    const uint64_t *sorted;
-    auto key_of = [&](int x) -> uint64_t {
-        const int r = x >> 1;
-        const int c = cnt[r];
-        if (c == 0) return ~0ull;
-        const int q = pg[r] / c, rem = pg[r] % c;
-        if ((x & 1) == 0) return rem > 0 ? run_key(q + 1, r) : ~0ull;
-        return run_key(q, r);
-    };
-    if (runs <= kRankSortRuns) {
-        const uint64_t mykey = tid < runs ? key_of(tid) : ~0ull;
-        if (tid < runs) keys[tid] = mykey;
-        __syncthreads();
-        if (tid < runs && mykey != ~0ull) {
-            int rank = 0;
-            for (int y = 0; y < runs; ++y) rank += keys[y] < mykey;
-            ranked[rank] = mykey;
-        }
-        // empty runs sort last: fill the tail so the positions below see count 0
-        int nonempty = 0;
-        {
-            int64_t z0 = 0, z1 = 0, e0 = (tid < runs && mykey != ~0ull), e1 = 0;
-            block_reduce4(z0, z1, e0, e1, red4);
-            nonempty = (int)e0;
-        }
-        for (int i = nonempty + tid; i < kRankSortRuns; i += kPlanThreads) ranked[i] = ~0ull;
-        __syncthreads();
-        sorted = ranked;
-    } else {
-        int n = 2;
-        while (n < runs) n <<= 1;
-        for (int x = tid; x < n; x += kPlanThreads) keys[x] = x < runs ? key_of(x) : ~0ull;
-        __syncthreads();
-        for (int k = 2; k <= n; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = tid; i < n; i += kPlanThreads) {
-                    const int ixj = i ^ j;
-                    if (ixj > i) {
-                        const uint64_t x = keys[i], y = keys[ixj];
-                        const bool up = (i & k) == 0;
-                        if ((x > y) == up) {
-                            keys[i] = y;
-                            keys[ixj] = x;
-                        }
-                    }
-                }
-                __syncthreads();
+    // 3. the items of each request
+    for (int r = r0; r < r1; ++r) {
+        const int64_t p = bad ? 0 : pages_of(a.lengths[r]);
+        ioff[r] = irun;
+        a.offsets[r] = irun;
+        if (p == 0) continue;
+        int32_t *w = a.work + 2 * (int64_t)irun;
+        if (balanced) {
+            const int64_t s = voff[r] + head;
+            int64_t g0, g1;
+            cut_range(s, p, g0, g1);
+            w[0] = r;
+            w[1] = 0;
+            for (int64_t g = g0; g <= g1; ++g) {
+                w[2 * (g - g0 + 1)] = r;
+                w[2 * (g - g0 + 1) + 1] = (int32_t)(g * V / Gp - s);
             }
-        }
-        sorted = keys;
-    }
-
-    // 5. positions of the runs in sorted order, then the (r, s) pairs
-    int n_sorted = 2;
-    while (n_sorted < runs) n_sorted <<= 1;
-    if (runs <= kRankSortRuns) n_sorted = kRankSortRuns;
-    const int per_run = n_sorted / kPlanThreads > 0 ? n_sorted / kPlanThreads : 1;
-    constexpr int kMaxPerRun = kMaxRuns / kPlanThreads;
-    int32_t cnt_local[kMaxPerRun], s0_local[kMaxPerRun], r_local[kMaxPerRun];
-    int32_t my_items = 0;
-    for (int i = 0; i < per_run; ++i) {
-        const int idx = tid * per_run + i;
-        cnt_local[i] = 0;
-        s0_local[i] = 0;
-        r_local[i] = 0;
-        if (idx >= n_sorted) continue;
-        const uint64_t key = sorted[idx];
-        if (key == ~0ull) continue;
-        const int64_t size = 0x7FFFFFFFll - (int64_t)(key >> 32);
-        const int32_t r = (int32_t)(key & 0xFFFFFFFFu);
-        const int32_t c = cnt[r];
-        const int32_t q = pg[r] / c, rem = pg[r] % c;
-        if (rem > 0 && size == q + 1) {
-            cnt_local[i] = rem;
-            s0_local[i] = 0;
+            irun += (int32_t)(1 + (g1 >= g0 ? g1 - g0 + 1 : 0));
         } else {
-            cnt_local[i] = c - rem;
-            s0_local[i] = rem;
+            const int64_t c = p < fixed ? p : fixed, q = p / c, rem = p % c;
+            for (int64_t k = 0; k < c; ++k) {
+                w[2 * k] = r;
+                w[2 * k + 1] = (int32_t)(k * q + (k < rem ? k : rem));
+            }
+            irun += (int32_t)c;
         }
-        r_local[i] = r;
-        my_items += cnt_local[i];
     }
-    int32_t total_items = 0;
-    int32_t pos = block_exclusive_scan(my_items, red32, &total_items);
-    for (int i = 0; i < per_run && 2 * total_items <= a.list_len; ++i) {
-        for (int32_t e = 0; e < cnt_local[i]; ++e) {
-            a.work[2 * (pos + e)] = r_local[i];
-            a.work[2 * (pos + e) + 1] = s0_local[i] + e;
-        }
-        pos += cnt_local[i];
-    }
-    for (int i = 2 * total_items + tid; i < a.list_len; i += kPlanThreads) a.work[i] = -1;
-
     if (tid == 0) {
-        a.header[kHdrStatus] = bad ? AMLA_DEV_BAD_LENGTH : 0;
-        a.header[kHdrItems] = n_items;
-        a.header[kHdrRows] = a.rows;
-        a.header[kHdrMtile] = a.mtile;
-        a.header[kHdrWorkers] = a.workers;
-        a.header[kHdrMode] = a.mode;
-        a.header[kHdrReqs] = R;
-        a.header[kHdrPlanned] = kPlannedMagic;
+        ioff[R] = N;
+        a.offsets[R] = N;
     }
-}
+    const int64_t gbase = 2 * ((int64_t)R + a.workers);
+    for (int64_t i = 2 * (int64_t)N + tid; i < gbase; i += kPlanThreads) a.work[i] = -1;
+    for (int64_t i = gbase + G + 1 + tid; i < a.list_len; i += kPlanThreads) a.work[i] = -1;
+    __syncthreads();   // voff and ioff complete
 
-// Inclusive scan over the 64 lanes of a wave: DPP row shifts within rows of 16 lanes,
-// then the row broadcasts of lanes 15 and 31 into the rows above them.
-__device__ __forceinline__ int32_t wave_incl_scan(int32_t v)
-{
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-    return v;
-}
-
-__device__ __forceinline__ int32_t wave_total(int32_t incl)
-{
-    return __builtin_amdgcn_readlane(incl, 63);
-}
-
-// Plan of up to kSmallReqs requests.  Every wave derives the whole plan summary by itself
-// (lane l holds requests l, l+64, l+128, l+192), so the chunk search and the scans need
-// no barrier; one barrier publishes the runs, whose list positions the 256 threads then
-// compute one run each.  Same result as plan_kernel.
-constexpr int kSmallReqs = 256;
-constexpr int kSmallPer = kSmallReqs / 64;
-
-__global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(PlanArgs a)
-{
-    // runs in request order, packed (0x7FFFFFFF - size) << 32 | r << 18 | s0 << 9 | length
-    // (s0 = its first split): the order of the packed words is the list order (size
-    // descending, then r; a request has one run per size)
-    __shared__ uint64_t runs[2 * kSmallReqs];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int R = a.reqs;
-    const int64_t mt = ceil_div(a.rows, a.mtile);
-    const int64_t budget = (int64_t)a.workers / mt;          // splits W workers take at once
-    const int64_t budget2 = (int64_t)kPlanSlack * a.workers / mt;
-
-    // 1. pages per request (every wave reads all lengths); kn = request groups in use
-    const int kn = (R + 63) >> 6;
-    int32_t pg[kSmallPer];
-    int32_t len[kSmallPer];
-#pragma unroll
-    for (int k = 0; k < kSmallPer; ++k) {
-        const int r = lane + 64 * k;
-        len[k] = k < kn && r < R ? a.lengths[r] : 0;
-    }
-    bool bad_l = false;
-    int32_t pmax_l = 0, nz_l = 0;
-    int64_t total_l = 0;
-#pragma unroll
-    for (int k = 0; k < kSmallPer; ++k) {
-        const int32_t L = len[k];
-        const int32_t p = (L >> 6) + ((L & 63) != 0);   // ceil(L / 64) without overflow
-        const bool b = L < 0 || p > a.bt_cols;
-        bad_l |= b;
-        pg[k] = b ? 0 : p;
-        pmax_l = pg[k] > pmax_l ? pg[k] : pmax_l;
-        total_l += pg[k];
-        nz_l += pg[k] > 0;
-    }
-    const bool bad = __any(bad_l);
-    const int64_t pmax = wave_all64<true>(pmax_l);
-    const int64_t total = wave_all64<false>(total_l);
-    const int64_t nz = wave_all64<false>(nz_l);
-    if (bad) {
-#pragma unroll
-        for (int k = 0; k < kSmallPer; ++k) pg[k] = 0;
-    }
-
-    // 2. chunk (BALANCED) or fixed count.  units(c) = sum_r ceil(pages_r / c) falls with c
-    //    and total/c <= units(c) <= total/c + nz, so the smallest c with units(c) <= budget
-    //    lies in [ceil(total/budget), ceil(total/(budget - nz))]: binary search, trying the
-    //    lower bound first (the answer for near-uniform lengths)
-    auto units = [&](int64_t c) {
-        int64_t u = 0;
-#pragma unroll
-        for (int k = 0; k < kSmallPer; ++k)
-            if (k < kn) u += ((uint32_t)pg[k] + (uint32_t)c - 1u) / (uint32_t)c;
-        return wave_all64<false>(u);
-    };
-    // ceil(x / y) for x >= 0, y > 0, in 32 bits when both fit
-    auto cdiv = [](int64_t x, int64_t y) -> int64_t {
-        if (x == 0) return 0;
-        if ((uint64_t)x <= 0xFFFFFFFFull && (uint64_t)y <= 0xFFFFFFFFull)
-            return (int64_t)((uint32_t)(x - 1) / (uint32_t)y) + 1;
-        return (x - 1) / y + 1;
-    };
-    // the smallest chunk with units(c) <= b, at least the minimum split
-    auto search = [&](int64_t b) {
-        int64_t c;
-        if (b < nz) {
-            c = pmax;
-        } else {
-            int64_t lo = cdiv(total, b), hi = pmax;
-            if (b > nz) {
-                const int64_t h = cdiv(total, b - nz);
-                hi = h < hi ? h : hi;
-            }
-            lo = lo < 1 ? 1 : (lo > hi ? hi : lo);
-            if (lo < hi && units(lo) <= b) hi = lo;
-            else if (lo < hi) ++lo;
+    // 4. the first item of each group
+    for (int64_t g = tid; g <= G; g += kPlanThreads) {
+        int32_t first = N;
+        if (!balanced) {
+            first = (int32_t)(g * N / G);
+        } else if (g < Gp && V > 0) {
+            const int64_t c = g * V / Gp;
+            int lo = 1, hi = R;                 // the first request with voff > c ...
             while (lo < hi) {
-                const int64_t mid = lo + (hi - lo) / 2;
-                if (units(mid) <= b) hi = mid;
+                const int mid = (lo + hi) >> 1;
+                if (voff[mid] > c) hi = mid;
                 else lo = mid + 1;
             }
-            c = hi;
-        }
-        return c > a.min_pages ? c : (int64_t)a.min_pages;
-    };
-    int64_t chunk = 1, fixed = 1;
-    if (!bad && a.mode == AMLA_PLAN_BALANCED && pmax > 0) {
-        chunk = search(budget);
-        // rebalance: when the longest split exceeds the mean work per worker by more than a
-        // quarter, plan for twice the workers (about two units per worker)
-        int64_t longest = 0;
-#pragma unroll
-        for (int k = 0; k < kSmallPer; ++k) {
-            if (k >= kn || pg[k] == 0) continue;
-            const uint32_t p = (uint32_t)pg[k];
-            uint32_t cc = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
-            cc = cc < (uint32_t)a.max_splits ? cc : (uint32_t)a.max_splits;
-            const int64_t sz = (p + cc - 1u) / cc;
-            longest = sz > longest ? sz : longest;
-        }
-        longest = wave_all64<true>(longest);
-        if (4 * longest * (int64_t)a.workers > 5 * mt * total) chunk = search(budget2);
-    } else if (!bad && a.mode == AMLA_PLAN_FIXED) {
-        fixed = R > 0 ? (int64_t)a.workers / ((int64_t)R * mt) : 1;
-        fixed = fixed < 1 ? 1 : (fixed > a.max_splits ? a.max_splits : fixed);
-    }
-
-    // 3. counts, offsets (request order = k-major lane order) and the runs of each request:
-    //    (q+1) x rem from s = 0, then q x (c - rem) from s = rem
-    int32_t cnt[kSmallPer], off[kSmallPer], rbase[kSmallPer];
-    int32_t carry = 0, rcarry = 0;
-#pragma unroll
-    for (int k = 0; k < kSmallPer; ++k) {
-        cnt[k] = off[k] = rbase[k] = 0;
-        if (k >= kn) continue;
-        const uint32_t p = (uint32_t)pg[k];
-        int32_t c = 0;
-        if (p > 0) {
-            if (a.mode == AMLA_PLAN_BALANCED) {
-                const uint32_t cc = (p + (uint32_t)chunk - 1u) / (uint32_t)chunk;
-                c = (int32_t)(cc < (uint32_t)a.max_splits ? cc : (uint32_t)a.max_splits);
+            const int r = lo - 1;               // ... less one holds position c
+            const int64_t x = c - voff[r] - head, p = voff[r + 1] - voff[r] - head;
+            if (x < minp) {
+                first = ioff[r];
+            } else if (p - x < minp) {
+                first = ioff[r + 1];
             } else {
-                c = (int32_t)((int64_t)p < fixed ? (int64_t)p : fixed);
+                int64_t g0, g1;
+                cut_range(voff[r] + head, p, g0, g1);
+                first = ioff[r] + 1 + (int32_t)(g - g0);
             }
         }
-        cnt[k] = c;
-        const int32_t rem = c > 0 ? (int32_t)(p % (uint32_t)c) : 0;
-        const int32_t nruns = (rem > 0) + (c - rem > 0);
-        const int32_t ci = wave_incl_scan(c), ri = wave_incl_scan(nruns);
-        off[k] = carry + ci - c;
-        rbase[k] = rcarry + ri - nruns;
-        carry += wave_total(ci);
-        rcarry += wave_total(ri);
+        a.work[gbase + g] = first;
     }
-    const int32_t n_items = carry, n_runs = rcarry;
-    if (wave == 0) {
-#pragma unroll
-        for (int k = 0; k < kSmallPer; ++k) {
-            const int r = lane + 64 * k;
-            if (r < R) {
-                a.counts[r] = cnt[k];
-                a.offsets[r] = off[k];
-                const int32_t c = cnt[k];
-                if (c > 0) {
-                    const uint32_t p = (uint32_t)pg[k];
-                    const int32_t q = (int32_t)(p / (uint32_t)c), rem = (int32_t)(p % (uint32_t)c);
-                    int idx = rbase[k];
-                    if (rem > 0)
-                        runs[idx++] = ((uint64_t)(0x7FFFFFFF - (q + 1)) << 32) | ((uint32_t)r << 18) |
-                                      (uint32_t)rem;
-                    if (c - rem > 0)
-                        runs[idx] = ((uint64_t)(0x7FFFFFFF - q) << 32) | ((uint32_t)r << 18) |
-                                    ((uint32_t)rem << 9) | (uint32_t)(c - rem);
-                }
-            }
-        }
-        if (lane == 0) a.offsets[R] = n_items;
-    }
-    __syncthreads();
-
-    // 4. list position of each run: the lengths of the runs that sort before it; then its
-    //    (r, s) pairs.  Up to 64 runs, the four threads of a quad count over every fourth
-    //    run and sum in the quad (all 256 threads busy); more, one thread per run.
-    auto place = [&](uint64_t key, int32_t pos, int e0, int de) {
-        const int32_t r = (int32_t)((key >> 18) & 0xFF), s0 = (int32_t)((key >> 9) & 0x1FF);
-        const int32_t n = (int32_t)(key & 0x1FF);
-        for (int e = e0; e < n && 2 * n_items <= a.list_len; e += de) {
-            a.work[2 * (pos + e)] = r;
-            a.work[2 * (pos + e) + 1] = s0 + e;
-        }
-    };
-    if (n_runs <= kPlanThreads / 4) {
-        const int part = tid & 3, x = tid >> 2;
-        const uint64_t key = x < n_runs ? runs[x] : ~0ull;
-        int32_t pos = 0;
-        for (int y0 = 0; y0 < n_runs; y0 += 16) {   // uniform trip count, four reads in flight
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int y = y0 + 4 * j + part;
-                const uint64_t o = runs[y < n_runs ? y : 0];
-                pos += y < n_runs && o < key ? (int32_t)(o & 0x1FF) : 0;
-            }
-        }
-        pos += __builtin_amdgcn_mov_dpp(pos, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
-        pos += __builtin_amdgcn_mov_dpp(pos, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
-        if (x < n_runs) place(key, pos, part, 4);
-    } else {
-        for (int x = tid; x < n_runs; x += kPlanThreads) {
-            const uint64_t key = runs[x];
-            int32_t pos = 0;
-            int y = 0;
-            for (; y + 4 <= n_runs; y += 4) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint64_t o = runs[y + j];
-                    pos += o < key ? (int32_t)(o & 0x1FF) : 0;
-                }
-            }
-            for (; y < n_runs; ++y) {
-                const uint64_t o = runs[y];
-                pos += o < key ? (int32_t)(o & 0x1FF) : 0;
-            }
-            place(key, pos, 0, 1);
-        }
-    }
-    for (int i = 2 * n_items + tid; i < a.list_len; i += kPlanThreads) a.work[i] = -1;
 
     if (tid == 0) {
         a.header[kHdrStatus] = bad ? AMLA_DEV_BAD_LENGTH : 0;
-        a.header[kHdrItems] = n_items;
+        a.header[kHdrItems] = N;
         a.header[kHdrRows] = a.rows;
         a.header[kHdrMtile] = a.mtile;
         a.header[kHdrWorkers] = a.workers;
@@ -1177,7 +851,8 @@ bool params_ok(const amla_plan_params *p)
            (p->mtile == 32 || p->mtile == 64 || p->mtile == 128) && p->workers >= 1 &&
            p->workers <= 65536 && p->min_split_tokens >= 0 && p->max_splits >= 1 &&
            p->max_splits <= AMLA_MAX_SPLITS &&
-           (p->mode == AMLA_PLAN_BALANCED || p->mode == AMLA_PLAN_FIXED);
+           (p->mode == AMLA_PLAN_BALANCED || p->mode == AMLA_PLAN_FIXED) &&
+           p->split_cost_pages >= 0 && p->split_cost_pages <= AMLA_MAX_SPLIT_COST;
 }
 
 // ------------------------------------------------- allocation-free entry: static scratch
@@ -1328,10 +1003,8 @@ int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols
     a.max_splits = params->max_splits;
     a.mode = params->mode;
     a.list_len = list_len;
-    if (num_reqs <= kSmallReqs)
-        hipLaunchKernelGGL(plan_small_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a);
-    else
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a);
+    a.split_cost = params->split_cost_pages;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 

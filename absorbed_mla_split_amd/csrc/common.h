@@ -22,10 +22,11 @@ constexpr int kDecodeThreads = 256;            // 4 waves
 constexpr int kChunksPerWave = kPageBytes / (4 * 1024);  // 9 x 1 KiB DMA per wave per page
 constexpr int kHeaderBytes = 256;
 constexpr int kPlanThreads = 256;
-// A plan may use up to kPlanSlack * W units (see the rebalancing rule in the plan kernels):
-// the work list and the workspace hold num_reqs + kPlanSlack * workers splits.
+// The work list and the workspace are sized for num_reqs + kPlanSlack * workers splits; a
+// plan uses at most num_reqs + workers - 1 (one per request and one per cut between worker
+// groups), and the list holds the group starts after its first 2 (num_reqs + workers)
+// entries.
 constexpr int kPlanSlack = 2;
-constexpr int kMaxRuns = 2 * AMLA_MAX_REQS;    // two split-size runs per request
 constexpr float kLog2e = 1.4426950408889634f;
 // Lazy max: the running row max is only raised when a page's max exceeds it by more
 // than 2^kTau, so p = 2^(t - m) <= 2^kTau; P is scaled by 2^kPScale before the E4M3
@@ -335,15 +336,37 @@ __device__ __forceinline__ v2i lds_read_tr8(const uint8_t *p)
 }
 
 // blockIdx -> virtual worker: hardware hands workgroups to the 8 XCDs round-robin, so
-// virtual workers v and v+1 (the row tiles of one split) are put on the same XCD and
-// share its L2.
+// consecutive virtual workers (the row tiles of one worker group, which read the same
+// pages) are put on the same XCD and share its L2.
 __device__ __forceinline__ int virtual_worker(int b, int W, int mt)
 {
-    // with one row tile per split there is nothing to share: workgroups take the list in
-    // order, so those that start first (and those started as CUs free up) take the
-    // longest items
+    // with one row tile per split there is nothing to share
     if (mt == 1 || W % 8 != 0) return b;
     return (b % 8) * (W / 8) + b / 8;
+}
+
+// The worker groups of a plan (plan kernel): G = max(1, W / mt) groups of min(W, mt)
+// workers; group g takes the items [work[2 (R + W) + g], work[2 (R + W) + g + 1]) of the
+// work list, each with its mt row tiles, as units (item-major, tile-minor) that its workers
+// take in turn.  Workers beyond the groups (W % mt of them) are idle.
+struct WorkerGroup {
+    int groups;      // G
+    int list_at;     // 2 (R + W) + g: where the group's first item is listed
+    int first_tile;  // the worker's first unit within an item's tiles
+    int step;        // units between the worker's units
+    bool active;
+};
+
+__device__ __forceinline__ WorkerGroup worker_group(int vw, int W, int mt, int R)
+{
+    WorkerGroup w;
+    w.groups = W / mt > 0 ? W / mt : 1;
+    w.step = W < mt ? W : mt;
+    const int g = vw / w.step;
+    w.active = g < w.groups;
+    w.first_tile = vw - g * w.step;
+    w.list_at = 2 * (R + W) + (w.active ? g : 0);
+    return w;
 }
 
 __device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c)

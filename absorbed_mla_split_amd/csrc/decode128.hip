@@ -64,26 +64,30 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
     const int mt = ceil_div(M, MT);
     const int W = a.workers;
 
-    // The plan summary, the item count and the first unit's work pair do not depend on
-    // each other, so they are loaded together and their latencies overlap.  The pair is
-    // inside the list: its item is below W and list_len >= 2 * (reqs + 2 * workers).
+    // The plan summary, the item count and the group's item range do not depend on each
+    // other, so they are loaded together and their latencies overlap (the range is inside
+    // the list, which holds at least 2 (R + 2 W) entries).
     const int vw = virtual_worker(blockIdx.x, W, mt);
+    const WorkerGroup wg = worker_group(vw, W, mt, R);
     const int h_planned = ldc(&header[kHdrPlanned]), h_rows = ldc(&header[kHdrRows]);
     const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
     const int h_reqs = ldc(&header[kHdrReqs]);
     const int n_items = ldc(&offsets[R]);
-    int r_first = ldc(&work[2 * (vw / mt)]), s_first = ldc(&work[2 * (vw / mt) + 1]);
+    const int g_begin = ldc(&work[wg.list_at]), g_end = ldc(&work[wg.list_at + 1]);
     // consume every value here so that the compiler cannot sink a load past the checks
     // below (it would otherwise chain them one behind the other)
     asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
-                 "s"(n_items), "s"(r_first), "s"(s_first), "s"(q_in), "s"(kv_in), "s"(block_table),
+                 "s"(n_items), "s"(g_begin), "s"(g_end), "s"(q_in), "s"(kv_in), "s"(block_table),
                  "s"(lengths), "s"(counts));
     if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
-        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+        h_reqs != R || n_items < 0 || n_items > R + W || 2 * (R + W) + wg.groups >= a.list_len ||
+        g_begin < 0 || g_begin > g_end || g_end > n_items) {
+        if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
         return;
     }
-    const int units = n_items * mt;
+    if (!wg.active) return;
+    const int units = g_end * mt;   // the group's units, item-major; this worker's: every
+                                    // wg.step-th from its own tile
 
     const DmaOffsets dmao = dma_offsets(wave, lane);
     const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
@@ -104,22 +108,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
     const int k_off1 = l32 * kKDim + 16 * ((2 * half + 1) ^ swz(l32));
     constexpr int kBlock1 = 32 * kKDim;
 
-    for (int u = vw; u < units; u += W) {
+    for (int u = g_begin * mt + wg.first_tile; u < units; u += wg.step) {
         const int item = u / mt, jt = u - item * mt;
-        const int r = u == vw ? r_first : ldc(&work[2 * item]);
-        const int s = u == vw ? s_first : ldc(&work[2 * item + 1]);
-        // the request's count, length and slot offset, loaded together (index clamped so
-        // that the loads stay in bounds before r is checked)
+        // the work pair, the next one (where the item ends), the request's count, length and
+        // item offset, loaded together (index clamped so that the loads stay in bounds
+        // before r is checked)
+        const int r = ldc(&work[2 * item]), first = ldc(&work[2 * item + 1]);
+        const int r_next = ldc(&work[2 * item + 2]), f_next = ldc(&work[2 * item + 3]);
         const int rc = r >= 0 && r < R ? r : 0;
         const int c = ldc(&counts[rc]), L = ldc(&lengths[rc]), off_r = ldc(&offsets[rc]);
         const int total = a.causal ? ldc(&a.totals[rc]) : L;
-        asm volatile("" ::"s"(c), "s"(L), "s"(off_r), "s"(total));
+        asm volatile("" ::"s"(r), "s"(first), "s"(r_next), "s"(f_next), "s"(c), "s"(L),
+                     "s"(off_r), "s"(total));
         const int pages = ceil_div(L, kPage);
-        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
-        const int first = s * q + (s < rem ? s : rem);
-        const int size = q + (s < rem ? 1 : 0);
-        if (r != rc || s < 0 || s >= c || L <= 0 || pages > a.bt_stride || size <= 0 ||
-            off_r + s >= n_items) {
+        const int end = item + 1 < n_items && r_next == r ? f_next : pages;
+        const int size = end - first;
+        if (r != rc || L <= 0 || pages > a.bt_stride || first < 0 || size <= 0 || end > pages ||
+            item < off_r || item >= off_r + c) {
             if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
             continue;
         }
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 
         // epilogue: the lane pair's sums; LSE from the FP32 sum, O normalised by the E4M3
         // sum (both carry P's 2^kPExp, which cancels in O / lq)
-        const size_t slot_idx = (size_t)off_r + s;
+        const size_t slot_idx = (size_t)item;
         const float l = half_pair_sum(l_run), lq = half_pair_sum(lq_run);
         // (the last P V MFMAs wrote the tiles read below through asm)
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");

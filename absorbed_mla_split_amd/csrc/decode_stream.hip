@@ -35,7 +35,7 @@ namespace {
 
 // One work unit as the stream sees it.
 struct Unit {
-    int r, s, L, total, off, first, size, jt;
+    int r, L, total, slot, first, size, jt;
     bool ok;
 };
 
@@ -80,35 +80,44 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
     const int h_mtile = ldc(&header[kHdrMtile]), h_workers = ldc(&header[kHdrWorkers]);
     const int h_reqs = ldc(&header[kHdrReqs]);
     const int n_items = ldc(&offsets[R]);
+    // this worker's group and the group's item range (inside the list, which holds at least
+    // 2 (R + 2 W) entries)
+    const WorkerGroup wg = worker_group(vw, W, mt, R);
+    const int g_begin = ldc(&work[wg.list_at]), g_end = ldc(&work[wg.list_at + 1]);
     asm volatile("" ::"s"(h_planned), "s"(h_rows), "s"(h_mtile), "s"(h_workers), "s"(h_reqs),
-                 "s"(n_items));
+                 "s"(n_items), "s"(g_begin), "s"(g_end));
     if (h_planned != kPlannedMagic || h_rows != M || h_mtile != MT || h_workers != W ||
-        h_reqs != R || n_items < 0 || 2 * n_items > a.list_len || n_items > R + kPlanSlack * W) {
-        if (tid == 0 && blockIdx.x == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
+        h_reqs != R || n_items < 0 || n_items > R + W || 2 * (R + W) + wg.groups >= a.list_len ||
+        g_begin < 0 || g_begin > g_end || g_end > n_items) {
+        if (tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
         return;
     }
-    const int units = n_items * mt;
+    if (!wg.active) return;
+    // the group's units, item-major: this worker takes every wg.step-th from its own tile
+    const int units = g_end * mt, ustep = wg.step;
 
-    // The descriptor of unit u: its work pair, then the request's count, length, slot
-    // offset (and global length under DCP); index clamped so the loads stay in bounds.
+    // The descriptor of unit u: its work pair and the next one (where the item ends), then
+    // the request's count, length, item offset (and global length under DCP); index clamped
+    // so the loads stay in bounds.
     auto load_unit = [&](int u) {
         Unit d;
         const int uu = u < units ? u : 0;
         const int item = uu / mt;
         d.jt = uu - item * mt;
         d.r = ldc(&work[2 * item]);
-        d.s = ldc(&work[2 * item + 1]);
+        d.first = ldc(&work[2 * item + 1]);
+        const int r_next = ldc(&work[2 * item + 2]), f_next = ldc(&work[2 * item + 3]);
         const int rc = d.r >= 0 && d.r < R ? d.r : 0;
         const int c = ldc(&counts[rc]);
         d.L = ldc(&lengths[rc]);
-        d.off = ldc(&offsets[rc]);
+        const int off = ldc(&offsets[rc]);
         d.total = a.causal ? ldc(&a.totals[rc]) : d.L;
         const int pages = ceil_div(d.L, kPage);
-        const int q = c > 0 ? pages / c : 0, rem = c > 0 ? pages % c : 0;
-        d.first = d.s * q + (d.s < rem ? d.s : rem);
-        d.size = q + (d.s < rem ? 1 : 0);
-        d.ok = d.r == rc && d.s >= 0 && d.s < c && d.L > 0 && pages <= a.bt_stride && d.size > 0 &&
-               d.off + d.s < n_items;
+        const int end = item + 1 < n_items && r_next == d.r ? f_next : pages;
+        d.size = end - d.first;
+        d.slot = item;
+        d.ok = d.r == rc && d.L > 0 && pages <= a.bt_stride && d.first >= 0 && d.size > 0 &&
+               end <= pages && item >= off && item < off + c;
         return d;
     };
     // A cursor over the workgroup's entries: the unit (skipping bad work items, which have
@@ -120,23 +129,23 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
     auto cursor_skip = [&](Cursor &c, bool flag) {
         while (c.u < units && !c.d.ok) {
             if (flag && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_ITEM);
-            c.u += W;
+            c.u += ustep;
             c.d = c.next;
-            c.next = load_unit(c.u + W);
+            c.next = load_unit(c.u + ustep);
         }
     };
     auto cursor_init = [&](Cursor &c, bool flag) {
-        c.u = vw;
+        c.u = g_begin * mt + wg.first_tile;
         c.e = 0;
         c.d = load_unit(c.u);
-        c.next = load_unit(c.u + W);
+        c.next = load_unit(c.u + ustep);
         cursor_skip(c, flag);
     };
     auto cursor_advance = [&](Cursor &c, bool flag) {
         if (++c.e > c.d.size) {
-            c.u += W;
+            c.u += ustep;
             c.d = c.next;
-            c.next = load_unit(c.u + W);
+            c.next = load_unit(c.u + ustep);
             c.e = 0;
             cursor_skip(c, flag);
         }
@@ -466,7 +475,7 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
                         __builtin_amdgcn_ldexpf(xch_qs[prb][0][rl], g0 - d) +
                         __builtin_amdgcn_ldexpf(xch_qs[prb][1][rl], g1 - d);
                     const float mref = xch_mref[prb][rl] + (float)d;
-                    const size_t slot_idx = (size_t)u.off + u.s;
+                    const size_t slot_idx = (size_t)u.slot;
                     const int row = u.jt * MT + 32 * prb + l32;
                     if (row < M) {
                         if (lse_writer && half == 0)

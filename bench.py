@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--pools", type=int, default=3, help="KV pool copies rotated over steps")
     ap.add_argument("--mtile", type=int, default=None, choices=[32, 64, 128],
                     help="rows per decode work unit (default: the library's choice)")
+    ap.add_argument("--split-cost", type=int, default=None,
+                    help="plan's split cost in pages (default: the library's)")
     ap.add_argument("--workers", type=int, default=None,
                     help="persistent decode workgroups and plan budget (default: one per CU)")
     ap.add_argument("--graph-steps", type=int, default=12,
@@ -176,7 +178,8 @@ def cpu_baseline(w, target_s, single_thread):
 class Runner:
     """Device copies of one workload plus the decoder, and the three ways of timing it."""
 
-    def __init__(self, w, dev, mode, mtile=None, workers=None, pools=3, uv=False, dcp=0):
+    def __init__(self, w, dev, mode, mtile=None, workers=None, pools=3, uv=False, dcp=0,
+                 split_cost=None):
         import torch
 
         from absorbed_mla_split_amd import binding
@@ -190,8 +193,9 @@ class Runner:
         self.lengths = torch.from_numpy(w.lengths).to(dev)
         kv0 = torch.from_numpy(w.kv8).to(dev)
         self.pools = [kv0] + [kv0.clone() for _ in range(max(0, pools - 1))]
-        self.dec = binding.FoldedDecoder(R, M, device=dev, mode=mode, mtile=mtile,
-                                         workers=workers)
+        self.dec = binding.FoldedDecoder(
+            R, M, device=dev, mode=mode, mtile=mtile, workers=workers,
+            split_cost_pages=binding.SPLIT_COST_DEFAULT if split_cost is None else split_cost)
         self.bmm1, self.bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
         self.out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((R, M), dtype=torch.float32, device=dev)
@@ -401,7 +405,8 @@ def measure(w, dev, args, mode_name, config, unfolded=False, layers=0, uv=False,
     from absorbed_mla_split_amd import binding
 
     mode = binding.PLAN_FIXED if mode_name == "fixed" else binding.PLAN_BALANCED
-    run = Runner(w, dev, mode, mtile=args.mtile, workers=args.workers, pools=args.pools,
+    run = Runner(w, dev, mode, mtile=args.mtile, workers=args.workers, split_cost=args.split_cost,
+                 pools=args.pools,
                  uv=uv, dcp=dcp)
     run.warm(args.warmup)
     eager = run.eager_pass(args.steps)
@@ -421,6 +426,7 @@ def measure(w, dev, args, mode_name, config, unfolded=False, layers=0, uv=False,
         "plan_us": round(float(np.mean(eager["plan"])), 2),
         "kv_bytes": int(w.kv_bytes),
         "mtile": run.dec.params.mtile, "workers": run.dec.params.workers,
+        "split_cost_pages": run.dec.params.split_cost_pages,
         "splits": int(run.dec.offsets[w.R].item()),
         "roofline": roofline(w, run.dec.params.mtile, dec_us, config, mode_name, unfolded),
     }
@@ -620,6 +626,7 @@ def main():
                    "kv_tokens": int(w.lengths.astype(np.int64).sum()), "page": 64,
                    "plan": args.mode, "kv_pools_rotated": args.pools,
                    "mtile": head["mtile"], "workers": head["workers"],
+                   "split_cost_pages": head["split_cost_pages"],
                    "launch": f"hip_graph x{head['chain']} steps"},
         "rows_per_s": head["rows_per_s"],
         "step_us": head["step_us"],

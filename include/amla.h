@@ -46,6 +46,8 @@ extern "C" {
 #define AMLA_MAX_ROWS 1024    /* most folded rows per request (k*H) */
 #define AMLA_MAX_REQS 4096    /* most requests one plan takes */
 #define AMLA_MAX_SPLITS 256   /* most splits per request */
+#define AMLA_MAX_SPLIT_COST 4096  /* largest split_cost_pages */
+#define AMLA_SPLIT_COST_DEFAULT 4
 
 #define AMLA_MAX_SOURCES 64   /* most DCP sources amla_merge_sources takes */
 
@@ -78,6 +80,9 @@ extern "C" {
  *   min_split_tokens  no split is planned shorter than this (rounded up to pages), >= 0
  *   max_splits        most splits per request, 1..AMLA_MAX_SPLITS
  *   mode              AMLA_PLAN_BALANCED or AMLA_PLAN_FIXED
+ *   split_cost_pages  BALANCED: what one split costs its worker beyond its pages (loading
+ *                     its query rows, writing its partials), in pages, 0..AMLA_MAX_SPLIT_COST;
+ *                     AMLA_SPLIT_COST_DEFAULT is this library's measured figure for gfx950
  */
 typedef struct amla_plan_params {
     int32_t rows_per_req;
@@ -86,6 +91,7 @@ typedef struct amla_plan_params {
     int32_t min_split_tokens;
     int32_t max_splits;
     int32_t mode;
+    int32_t split_cost_pages;
 } amla_plan_params;
 
 /*
@@ -140,8 +146,8 @@ int amla_reducer_bands(int32_t rows, int32_t compute_units, int32_t *bands_out);
  * from the batch shape before any launch, so it can be allocated once, ahead of graph
  * capture); the layout is the library's own: a 256-byte header (device status, plan
  * summary), then FP32 partials [num_reqs + 2 * workers][rows_per_req][512] and FP32 log2
- * LSE [num_reqs + 2 * workers][rows_per_req] (every plan has at most
- * num_reqs + 2 * workers splits).  The caller allocates and owns the workspace.
+ * LSE [num_reqs + 2 * workers][rows_per_req] (every plan has fewer than
+ * num_reqs + workers splits).  The caller allocates and owns the workspace.
  * Returns 0 for arguments out of range.
  */
 size_t amla_workspace_bytes(int32_t num_reqs, int32_t rows_per_req, int32_t workers);
@@ -154,20 +160,29 @@ size_t amla_workspace_bytes(int32_t num_reqs, int32_t rows_per_req, int32_t work
  *   d_lengths  int32 [num_reqs]: keys per request, including the draft block
  *   bt_cols    columns of the block table (pages a request may have)
  *   d_counts   int32 [num_reqs]  out: splits per request (0 for an empty request)
- *   d_offsets  int32 [num_reqs+1] out: exclusive prefix sum; slot of split s of r is
- *              offsets[r] + s; offsets[num_reqs] = items in the work list
- *   d_work     int32 [list_len] out: (r, s) pairs, longest split first (ties: lower r,
- *              then lower s), then -1
+ *   d_offsets  int32 [num_reqs+1] out: exclusive prefix sum of the counts; item (and
+ *              workspace slot) offsets[r] + s is split s of r; offsets[num_reqs] = N items
+ *   d_work     int32 [list_len] out: item i as (request, first page) at [2i, 2i+1], items in
+ *              request order, splits of a request in page order; -1 up to 2 * (R + W); then
+ *              at 2 * (R + W) + g the first item of worker group g (g = 0..G, entry G = N),
+ *              G = max(1, W / mt); then -1.  Item i ends where item i+1 starts if that is of
+ *              the same request, else at the request's last page.
  *   list_len   >= 2 * (num_reqs + 2 * workers)
  *   d_workspace / ws_bytes: the workspace (header written here)
- * The split rule: pages_r = ceil(L_r/64), mt = ceil(M/MT).  BALANCED: chunk(B) = the
- * smallest c >= 1 with mt * sum_r ceil(pages_r/c) <= B (the longest request if none), at
- * least ceil(min_split_tokens/64); count_r = min(max_splits, ceil(pages_r/chunk)) with
- * chunk = chunk(W), unless the longest split then exceeds 5/4 of the mean work per worker
- * (4 * max_r ceil(pages_r/count_r) * W > 5 * mt * sum_r pages_r): then chunk = chunk(2W).
- * FIXED: count_r = min(pages_r, clamp(floor(W/(R*mt)), 1, max_splits)).  Split s of r has
- * q + (s < rem) pages starting at page s*q + min(s, rem), q = pages_r / count_r,
- * rem = pages_r % count_r.
+ * The split rule (the pages leave it open; this is the library's reading): pages_r =
+ * ceil(L_r/64), P = sum_r pages_r, mt = ceil(M/MT) row tiles per split, one worker per tile:
+ * worker group g is workers [g*mt, (g+1)*mt).  minp = max(1, ceil(min_split_tokens/64)),
+ * a = split_cost_pages.  BALANCED: every non-empty request is laid out as a head of a pages
+ * and its pages_r pages, the requests end to end (request r from voff_r, V in all), and V
+ * is cut into Gp = min(G, max_splits, max(1, floor(V/minp))) ranges at c_g = floor(g*V/Gp).
+ * A cut strictly inside request r at page x = c_g - voff_r - a of it (negative in the
+ * head) moves to the request's start if x < minp, to its end if pages_r - x < minp, else
+ * cuts r at page x.  The splits of r start at page 0 and at each cut left inside it; group
+ * g takes the items starting in [C_g, C_{g+1}) of the moved cuts (a request's first item
+ * starts at its head; groups g >= Gp take none), so every group costs about V/Gp.
+ * FIXED: count_r = min(pages_r, clamp(floor(W/(R*mt)), 1, max_splits)) splits, split s with
+ * q + (s < rem) pages from page s*q + min(s, rem), q = pages_r / count_r, rem = pages_r %
+ * count_r; group g takes items [floor(g*N/G), floor((g+1)*N/G)).
  */
 int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols,
                      const amla_plan_params *params, int32_t *d_counts, int32_t *d_offsets,
@@ -175,8 +190,9 @@ int amla_plan_splits(const int32_t *d_lengths, int32_t num_reqs, int32_t bt_cols
                      void *stream);
 
 /*
- * Folded split-KV decode: one persistent kernel of `workers` workgroups walks the planned
- * work list; every (request, split, row tile) stages its pages in LDS, computes S = Q K^T
+ * Folded split-KV decode: one persistent kernel of `workers` workgroups; each worker group
+ * walks its items of the planned work list; every (request, split, row tile) stages its
+ * pages in LDS, computes S = Q K^T
  * and O += P V on FP8 MFMA with an online softmax, and writes FP32 partials and the log2
  * LSE of its split into the workspace.  Page "...cutedsl.mla.balanced", module docstring
  * (FP32 split partials; the row max is kept lazily and P is fed to the MMA as E4M3).

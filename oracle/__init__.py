@@ -56,8 +56,8 @@ def _load():
         lib.oracle_plan.restype = ctypes.c_int
         lib.oracle_plan.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                    ctypes.c_int32, ctypes.c_int32, i32p, i32p, i32p,
-                                    ctypes.c_int32]
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p, i32p,
+                                    i32p, ctypes.c_int32]
         lib.oracle_item_range.restype = ctypes.c_int
         lib.oracle_item_range.argtypes = [i32p, ctypes.c_int32, i32p, ctypes.c_int32,
                                           ctypes.c_int32, i32p, i32p, i32p]
@@ -154,11 +154,12 @@ def merge(o, lse):
 # ----------------------------------------------------------------------------- plan
 
 def plan(lengths, bt_cols, M, MT, W, min_split_tokens=256, max_splits=256, mode=BALANCED,
-         list_len=None):
+         list_len=None, split_cost=0):
     """Split plan: (counts int32 [R], offsets int32 [R+1], work int32 [list_len], items).
 
     work: items in request order as (request, first page) pairs, then the first item of each
-    of the G = max(1, W // ceil(M / MT)) worker groups (G + 1 entries) at 2 * (R + W)."""
+    of the G = max(1, W // ceil(M / MT)) worker groups (G + 1 entries) at 2 * (R + W).
+    split_cost: what one split costs a worker beyond its pages, in pages (BALANCED)."""
     lengths = np.ascontiguousarray(lengths, dtype=np.int32)
     R = lengths.shape[0]
     if list_len is None:
@@ -167,7 +168,8 @@ def plan(lengths, bt_cols, M, MT, W, min_split_tokens=256, max_splits=256, mode=
     offsets = np.zeros(R + 1, dtype=np.int32)
     work = np.zeros(max(list_len, 1), dtype=np.int32)
     n = _load().oracle_plan(_ptr(lengths, ctypes.c_int32), R, bt_cols, M, MT, W,
-                            min_split_tokens, max_splits, mode, _ptr(counts, ctypes.c_int32),
+                            min_split_tokens, max_splits, split_cost, mode,
+                            _ptr(counts, ctypes.c_int32),
                             _ptr(offsets, ctypes.c_int32), _ptr(work, ctypes.c_int32), list_len)
     if n == -1:
         raise ValueError("oracle_plan: invalid arguments or lengths")

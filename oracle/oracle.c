@@ -209,17 +209,20 @@ void oracle_merge(const double *o, const double *lse, int32_t n, double *out, do
  * split counts planned from the KV lengths on the device, one wave of persistent workers
  * walking a work list, fixed equal splits per batch shape as the comparator).
  *
- *   pages_r = ceil(L_r / 64); P = sum_r pages_r; mt = ceil(M / MT) row tiles per split; the
- *   mt row tiles of a split go to the mt workers of one group, G = max(1, floor(W / mt))
- *   groups; minp = max(1, ceil(min_split_tokens / 64)).
- *   BALANCED: the requests' pages are laid end to end (request r from off_r, the pages of
- *     the requests before it) and cut into Gp = min(G, max_splits, max(1, floor(P / minp)))
- *     ranges at c_g = floor(g * P / Gp), g = 0..Gp.  A cut inside request r (off_r < c_g <
- *     off_r + pages_r) less than minp pages from the request's start moves to its start,
- *     less than minp pages from its end moves to its end.  Group g takes the pages between
- *     its two moved cuts, so every group has P / Gp pages give or take minp; a request's
- *     splits are its pieces between the moved cuts inside it, each at least minp pages long
- *     or the whole request.
+ *   pages_r = ceil(L_r / 64); mt = ceil(M / MT) row tiles per split; the mt row tiles of a
+ *   split go to the mt workers of one group, G = max(1, floor(W / mt)) groups;
+ *   minp = max(1, ceil(min_split_tokens / 64)); a = split_cost, what one split costs a
+ *   worker beyond its pages (its query rows and its partial output), in pages.
+ *   BALANCED: each non-empty request is laid out as a head of a pages followed by its
+ *     pages_r pages, the requests end to end (request r from voff_r; V in all), and V is
+ *     cut into Gp = min(G, max_splits, max(1, floor(V / minp))) ranges at
+ *     c_g = floor(g * V / Gp), g = 0..Gp.  A cut strictly inside request r at page
+ *     x = c_g - voff_r - a of it (negative in the head) moves to the request's start when
+ *     x < minp and to its end when pages_r - x < minp; otherwise it cuts r at page x.
+ *     A request's splits start at page 0 and at each cut left inside it (every piece is
+ *     then at least minp pages or the whole request); group g takes the items starting in
+ *     [C_g, C_{g+1}) of the moved cuts (an item's start being voff_r for a request's first
+ *     item, voff_r + a + its first page for the others), so every group costs about V / Gp.
  *   FIXED: count_r = min(pages_r, clamp(floor(W / (R * mt)), 1, max_splits)) equal splits,
  *     split s covering pages [s*q + min(s, rem), +q + (s < rem)), q = pages_r / count_r,
  *     rem = pages_r % count_r; group g takes items [floor(g * N / G), floor((g+1) * N / G)).
@@ -234,15 +237,16 @@ void oracle_merge(const double *o, const double *lse, int32_t n, double *out, do
  * bt_cols, bad sizes), -2 if list_len < 2 * (R + 2 * W).
  */
 int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, int32_t MT,
-                int32_t W, int32_t min_split_tokens, int32_t max_splits, int32_t mode,
-                int32_t *counts, int32_t *offsets, int32_t *work, int32_t list_len)
+                int32_t W, int32_t min_split_tokens, int32_t max_splits, int32_t split_cost,
+                int32_t mode, int32_t *counts, int32_t *offsets, int32_t *work,
+                int32_t list_len)
 {
-    int64_t P = 0, n = 0, G, minp, mt;
-    int64_t *pages, *off, *cut = NULL;
+    int64_t V = 0, n = 0, G, minp, mt, a = split_cost;
+    int64_t *pages, *voff, *cut = NULL;
     int32_t *gstart;
 
     if (R < 0 || M < 1 || MT < 1 || W < 1 || max_splits < 1 || min_split_tokens < 0 ||
-        (mode != 0 && mode != 1))
+        split_cost < 0 || (mode != 0 && mode != 1))
         return -1;
     for (int32_t r = 0; r < R; ++r)
         if (lengths[r] < 0 || ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE > bt_cols)
@@ -256,24 +260,24 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
         minp = 1;
 
     pages = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R + 1));
-    off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R + 1));
-    if (!pages || !off) {
+    voff = (int64_t *)malloc(sizeof(int64_t) * (size_t)(R + 1));
+    if (!pages || !voff) {
         free(pages);
-        free(off);
+        free(voff);
         return -1;
     }
     for (int32_t r = 0; r < R; ++r) {
         pages[r] = ((int64_t)lengths[r] + ORACLE_PAGE - 1) / ORACLE_PAGE;
-        off[r] = P;
-        P += pages[r];
+        voff[r] = V;
+        V += pages[r] > 0 ? a + pages[r] : 0;
     }
-    off[R] = P;
+    voff[R] = V;
     for (int32_t k = 0; k < list_len; ++k)
         work[k] = -1;
     gstart = work + 2 * ((int64_t)R + W);
 
     if (mode == 0) {
-        int64_t Gp = P / minp;
+        int64_t Gp = V / minp;
         if (Gp < 1)
             Gp = 1;
         if (Gp > G)
@@ -284,25 +288,27 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
         cut = (int64_t *)malloc(sizeof(int64_t) * (size_t)(Gp + 1));
         if (!cut) {
             free(pages);
-            free(off);
+            free(voff);
             return -1;
         }
         for (int64_t g = 0; g <= Gp; ++g) {
-            int64_t c = g * P / Gp;
+            int64_t c = g * V / Gp;
             cut[g] = c;
             for (int32_t r = 0; r < R; ++r) {
-                if (off[r] < c && c < off[r] + pages[r]) {       /* inside request r */
-                    if (c - off[r] < minp)
-                        cut[g] = off[r];
-                    else if (off[r] + pages[r] - c < minp)
-                        cut[g] = off[r] + pages[r];
+                int64_t end = voff[r] + (pages[r] > 0 ? a + pages[r] : 0);
+                if (voff[r] < c && c < end) {                    /* inside request r */
+                    int64_t x = c - voff[r] - a;
+                    if (x < minp)
+                        cut[g] = voff[r];
+                    else if (pages[r] - x < minp)
+                        cut[g] = end;
                     break;
                 }
             }
         }
         /* each request's splits: its pieces between the distinct moved cuts inside it */
         for (int32_t r = 0; r < R; ++r) {
-            int64_t last = -1;
+            int64_t last = -1, end = voff[r] + a + pages[r];
             offsets[r] = (int32_t)n;
             counts[r] = 0;
             if (pages[r] == 0)
@@ -312,9 +318,9 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
             ++n;
             counts[r] = 1;
             for (int64_t g = 0; g <= Gp; ++g) {
-                if (off[r] < cut[g] && cut[g] < off[r] + pages[r] && cut[g] != last) {
+                if (voff[r] < cut[g] && cut[g] < end && cut[g] != last) {
                     work[2 * n] = r;
-                    work[2 * n + 1] = (int32_t)(cut[g] - off[r]);
+                    work[2 * n + 1] = (int32_t)(cut[g] - voff[r] - a);
                     ++n;
                     ++counts[r];
                     last = cut[g];
@@ -326,7 +332,9 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
             int64_t first = n;
             if (g <= Gp) {
                 for (int64_t i = 0; i < n; ++i) {
-                    if (off[work[2 * i]] + work[2 * i + 1] >= cut[g]) {
+                    int32_t r = work[2 * i];
+                    int64_t start = voff[r] + (work[2 * i + 1] > 0 ? a + work[2 * i + 1] : 0);
+                    if (start >= cut[g]) {
                         first = i;
                         break;
                     }
@@ -357,7 +365,7 @@ int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, i
     offsets[R] = (int32_t)n;
     free(cut);
     free(pages);
-    free(off);
+    free(voff);
     return (int32_t)n;
 }
 

@@ -25,8 +25,9 @@ int oracle_attend(const uint8_t *q8, const uint8_t *kv8, int64_t pool_pages,
                   int32_t R, int32_t M, double q_scale, double k_scale, double sm_scale,
                   const int32_t *tasks, int32_t ntasks, double *out, double *lse);
 int oracle_plan(const int32_t *lengths, int32_t R, int32_t bt_cols, int32_t M, int32_t MT,
-                int32_t W, int32_t min_split_tokens, int32_t max_splits, int32_t mode,
-                int32_t *counts, int32_t *offsets, int32_t *work, int32_t list_len);
+                int32_t W, int32_t min_split_tokens, int32_t max_splits, int32_t split_cost,
+                int32_t mode, int32_t *counts, int32_t *offsets, int32_t *work,
+                int32_t list_len);
 void oracle_merge(const double *o, const double *lse, int32_t n, double *out, double *lse_out);
 
 static void *take(FILE *f, size_t bytes)
@@ -62,14 +63,14 @@ int main(int argc, char **argv)
         fwrite(l, sizeof(double), (size_t)nt, out);
         free(h); free(sc); free(q8); free(kv8); free(bt); free(len); free(tasks); free(o); free(l);
     } else if (!strcmp(argv[1], "plan")) {
-        int32_t *h = take(in, 9 * sizeof(int32_t));
-        const int32_t R = h[0], list_len = h[8];
+        int32_t *h = take(in, 10 * sizeof(int32_t));
+        const int32_t R = h[0], list_len = h[9];
         int32_t *len = take(in, (size_t)R * sizeof(int32_t));
         int32_t *counts = malloc((size_t)R * sizeof(int32_t) + 4);
         int32_t *offsets = malloc((size_t)(R + 1) * sizeof(int32_t));
         int32_t *work = malloc((size_t)list_len * sizeof(int32_t) + 4);
-        int32_t rc = oracle_plan(len, R, h[1], h[2], h[3], h[4], h[5], h[6], h[7], counts,
-                                 offsets, work, list_len);
+        int32_t rc = oracle_plan(len, R, h[1], h[2], h[3], h[4], h[5], h[6], h[7], h[8],
+                                 counts, offsets, work, list_len);
         fwrite(&rc, sizeof rc, 1, out);
         fwrite(counts, sizeof(int32_t), (size_t)R, out);
         fwrite(offsets, sizeof(int32_t), (size_t)R + 1, out);

@@ -23,12 +23,13 @@ def to_dev(w):
 
 
 def run_gpu(w, mode=binding.PLAN_BALANCED, min_split_tokens=256, workers=None, mtile=None,
-            decoder=None, tensors=None):
+            decoder=None, tensors=None, split_cost=binding.SPLIT_COST_DEFAULT):
     """Plan + decode + combine on cuda:0.  Output, LSE and workspace start as NaN, so any
     value the kernels fail to write shows up."""
     q, kv, bt, lengths = tensors if tensors is not None else to_dev(w)
     dec = decoder or binding.FoldedDecoder(w.R, w.M, mode=mode, min_split_tokens=min_split_tokens,
-                                           workers=workers, mtile=mtile)
+                                           workers=workers, mtile=mtile,
+                                           split_cost_pages=split_cost)
     dec.workspace[256:].fill_(0xFF)                      # FP32 NaN pattern
     out = torch.full((w.R, w.M, 512), float("nan"), dtype=torch.bfloat16, device=q.device)
     lse = torch.full((w.R, w.M), float("nan"), dtype=torch.float32, device=q.device)

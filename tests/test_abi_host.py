@@ -45,6 +45,8 @@ def test_header_constants_match_binding():
     assert int(consts["AMLA_UVDIM"]) == b.UVDIM
     assert int(consts["AMLA_MAX_SOURCES"]) == b.MAX_SOURCES
     assert int(consts["AMLA_MAX_REQS"]) == b.MAX_REQS
+    assert int(consts["AMLA_MAX_SPLIT_COST"]) == b.MAX_SPLIT_COST
+    assert int(consts["AMLA_SPLIT_COST_DEFAULT"]) == b.SPLIT_COST_DEFAULT
     assert int(consts["AMLA_ERR_WORKSPACE"]) == b.ERR_WORKSPACE
     assert int(consts["AMLA_DEV_BAD_PAGE"]) == b.DEV_BAD_PAGE
     assert int(consts["AMLA_DEV_BAD_POSITION"]) == b.DEV_BAD_POSITION
@@ -135,6 +137,9 @@ def test_plan_argument_errors():
     assert _call_plan(lib, params=b.make_params(b.MAX_ROWS + 1, 128, 256)) == b.ERR_INVALID
     assert _call_plan(lib, params=b.make_params(32, 32, 256, mode=7)) == b.ERR_INVALID
     assert _call_plan(lib, params=b.make_params(32, 32, 256, max_splits=0)) == b.ERR_INVALID
+    assert _call_plan(lib, params=b.make_params(32, 32, 256, split_cost_pages=-1)) == b.ERR_INVALID
+    assert _call_plan(lib, params=b.make_params(32, 32, 256,
+                                                split_cost_pages=b.MAX_SPLIT_COST + 1)) == b.ERR_INVALID
     assert _call_plan(lib, ws_bytes=100) == b.ERR_WORKSPACE
     assert _call_plan(lib, list_len=2 * (2 + 2 * 256) - 1) == b.ERR_LIST
 

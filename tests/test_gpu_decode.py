@@ -24,27 +24,30 @@ def test_c1_every_row():
     w = wl.generate("c1")
     out, lse, dec = run_gpu(w)
     counts, offsets, work, n = dec.plan_host()
-    assert counts.tolist() == [1, 2]             # 4 pages; 5 pages cut in two
+    assert counts.tolist() == [1, 1]             # 4 + 5 pages, 4-page minimum: no cut inside
     compare(w, out, lse, tag="c1")
     assert dec.device_status() == 0
 
 
-def test_c1_split_partials_match_oracle_chunks():
+@pytest.mark.parametrize("workers", [4, 6])
+def test_c1_split_partials_match_oracle_chunks(workers):
+    # 4 workers, one-page minimum, no split cost: cuts at pages 2, 4 (the request boundary)
+    # and 6, so both requests are cut in two; 6 workers: cuts 1, 3, 4, 6, 7
     w = wl.generate("c1")
-    out, lse, dec = run_gpu(w)
+    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=workers, split_cost=0)
     counts, offsets, work, n = dec.plan_host()
+    assert counts.tolist() == ([2, 2] if workers == 4 else [3, 3])
     part, plse = ws_partials(dec, w)
     vm = vmax(w)
-    for r in range(w.R):
-        for s in range(counts[r]):
-            a, b = oracle.split_range(w.lengths[r], counts[r], s)
-            tasks = [(r, i, a, b) for i in range(w.M)]
-            ro, rl = oracle.attend(w.q8, w.kv8, w.block_table, w.lengths, tasks, w.q_scale,
-                                   w.k_scale, w.sm_scale)
-            slot = offsets[r] + s
-            err = np.max(np.abs(part[slot] - ro))
-            assert err <= OUT_TOL * vm, (r, s, err)
-            assert np.max(np.abs(plse[slot] - rl)) <= 1e-3, (r, s)
+    for i in range(n):
+        r, a, b = oracle.item_range(work, n, w.lengths, i)
+        tasks = [(r, j, a, b) for j in range(w.M)]
+        ro, rl = oracle.attend(w.q8, w.kv8, w.block_table, w.lengths, tasks, w.q_scale,
+                               w.k_scale, w.sm_scale)
+        err = np.max(np.abs(part[i] - ro))      # item i's workspace slot is i
+        assert err <= OUT_TOL * vm, (r, a, b, err)
+        assert np.max(np.abs(plse[i] - rl)) <= 1e-3, (r, a, b)
+    compare(w, out, lse, tag=f"c1-W{workers}")
 
 
 SHAPES = [
@@ -93,24 +96,25 @@ def test_many_splits_small_workers():
 
 
 def test_over_64_splits_per_request():
-    # one-page splits: 201 and 70 splits, so the reducer holds several LSEs per lane
+    # 271 pages over 256 groups (at most 256 splits): 190 and 66 splits of one or two
+    # pages, so the reducer holds several LSEs per lane
     w = wl.small(2, 4, 8, [64 * 200 + 5, 64 * 70], seed=6)
-    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=300)
-    assert dec.plan_host()[0].tolist() == [201, 70]
+    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=300, split_cost=0)
+    assert dec.plan_host()[0].tolist() == [190, 66]
     compare(w, out, lse, tag="201-splits")
 
 
 def test_most_splits_per_request():
     # 300 pages, one-page minimum and 600 workers: the split count hits its cap of 256, so
-    # the reducer holds four LSEs on every lane
-    w = wl.small(2, 4, 8, [64 * 300, 64 * 3], seed=9)
-    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=600)
-    assert dec.plan_host()[0].tolist() == [binding.MAX_SPLITS, 3]
+    # the reducer holds four LSEs on every lane; the second request is empty
+    w = wl.small(2, 4, 8, [64 * 300, 0], seed=9)
+    out, lse, dec = run_gpu(w, min_split_tokens=0, workers=600, split_cost=0)
+    assert dec.plan_host()[0].tolist() == [binding.MAX_SPLITS, 0]
     compare(w, out, lse, tag="256-splits")
 
 
-def test_more_requests_than_the_small_plan_takes():
-    # 300 requests (the block-reduction plan kernel) of mixed short lengths, some empty
+def test_more_requests_than_plan_threads():
+    # 300 requests (some plan threads own two) of mixed short lengths, some empty
     rng = np.random.default_rng(21)
     lengths = rng.integers(0, 900, 300)
     lengths[rng.random(300) < 0.1] = 0

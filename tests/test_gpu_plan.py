@@ -12,12 +12,13 @@ pytestmark = pytest.mark.gpu
 
 
 def plan_both(lengths, M, mode=binding.PLAN_BALANCED, min_split_tokens=256, workers=None,
-              max_splits=256):
+              max_splits=256, split_cost=binding.SPLIT_COST_DEFAULT):
     lengths = np.asarray(lengths, dtype=np.int32)
     R = len(lengths)
     cols = max(1, int(((lengths.astype(np.int64) + 63) // 64).max()) if R else 1)
     dec = binding.FoldedDecoder(max(R, 1), M, mode=mode, min_split_tokens=min_split_tokens,
-                                workers=workers, max_splits=max_splits)
+                                workers=workers, max_splits=max_splits,
+                                split_cost_pages=split_cost)
     dec.work.fill_(12345)
     dec.counts.fill_(777)
     dec.offsets.fill_(777)
@@ -25,7 +26,8 @@ def plan_both(lengths, M, mode=binding.PLAN_BALANCED, min_split_tokens=256, work
     counts, offsets, work, n = dec.plan_host()
     p = dec.params
     rc, ro, rw, rn = oracle.plan(lengths, cols, M, p.mtile, p.workers, min_split_tokens,
-                                 max_splits, mode, list_len=dec.work.numel())
+                                 max_splits, mode, list_len=dec.work.numel(),
+                                 split_cost=p.split_cost_pages)
     assert dec.device_status() == 0
     assert n == rn
     np.testing.assert_array_equal(counts, rc)
@@ -49,7 +51,8 @@ def test_plan_random(seed):
     lengths = rng.integers(0, 40000, R).astype(np.int32)
     lengths[rng.random(R) < 0.15] = 0
     M = int(rng.choice([8, 32, 56, 128, 256, 448]))
-    plan_both(lengths, M, int(rng.integers(0, 2)), int(rng.choice([0, 64, 256, 4096])))
+    plan_both(lengths, M, int(rng.integers(0, 2)), int(rng.choice([0, 64, 256, 4096])),
+              split_cost=int(rng.choice([0, 1, 4, 100])))
 
 
 def test_plan_edges():
@@ -59,6 +62,8 @@ def test_plan_edges():
     plan_both([64], 32, min_split_tokens=0)
     plan_both([131072] + [1024] * 15, 448)
     plan_both([10 ** 6], 32, max_splits=7)
+    plan_both([10 ** 6, 64, 0, 700], 32, split_cost=binding.MAX_SPLIT_COST)
+    plan_both([64] * 300, 56, min_split_tokens=0, split_cost=0)
     rng = np.random.default_rng(5)
     plan_both(rng.integers(0, 3000, binding.MAX_REQS).astype(np.int32), 32)
     plan_both(rng.integers(0, 3000, binding.MAX_REQS).astype(np.int32), 256, binding.PLAN_FIXED)
@@ -70,7 +75,10 @@ def test_plan_bad_length_sets_status_and_empties_plan():
     dec.plan(lengths, 4)
     counts, offsets, work, n = dec.plan_host()
     assert dec.device_status() & binding.DEV_BAD_LENGTH
-    assert n == 0 and np.all(counts == 0) and np.all(work == -1)
+    G = dec.params.workers                 # 32 rows in 32-row tiles: one worker per group
+    gb = 2 * (3 + dec.params.workers)
+    assert n == 0 and np.all(counts == 0) and np.all(work[:gb] == -1)
+    assert np.all(work[gb:gb + G + 1] == 0) and np.all(work[gb + G + 1:] == -1)
     lengths = torch.tensor([100, 64 * 5, 64], dtype=torch.int32, device="cuda")   # > 4 columns
     dec.plan(lengths, 4)
     assert dec.device_status() & binding.DEV_BAD_LENGTH
@@ -78,7 +86,7 @@ def test_plan_bad_length_sets_status_and_empties_plan():
 
 @pytest.mark.parametrize("R", [63, 64, 65, 128, 255, 256, 257])
 def test_plan_request_count_boundaries(R):
-    # up to 256 requests take the single-pass planner, more the block-wide one
+    # up to 256 requests one per plan thread, more several per thread
     rng = np.random.default_rng(R)
     lengths = rng.integers(0, 20000, R).astype(np.int32)
     lengths[rng.random(R) < 0.1] = 0
@@ -90,11 +98,24 @@ def test_plan_request_count_boundaries(R):
 
 
 @pytest.mark.parametrize("R", [100, 300, 1000])
-def test_plan_rebalanced_skewed_batches(R):
-    # log-uniform lengths: the longest split at one unit per worker exceeds 5/4 of the mean,
-    # so the plan takes the finer chunk (more items than workers); both planners, bit-exact
+def test_plan_balances_skewed_batches(R):
+    # log-uniform lengths, bit-exact with the oracle; every group's cost (its pages and the
+    # split cost per item) within two minimum splits and two split costs of the mean (from the
+    # device's own list)
     rng = np.random.default_rng(R)
     lengths = np.floor(np.exp(rng.uniform(np.log(64), np.log(65536), R))).astype(np.int32)
-    dec = plan_both(lengths, 32)
-    n = dec.plan_host()[3]
-    assert n > dec.params.workers
+    dec = plan_both(lengths, 56)
+    counts, offsets, work, n = dec.plan_host()
+    pages = (lengths.astype(np.int64) + 63) // 64
+    W = dec.params.workers
+    gs = work[2 * (R + W):2 * (R + W) + W + 1]
+    a = dec.params.split_cost_pages
+    V = int(pages.sum()) + a * R
+    Gp = min(W, V // 4)
+    for g in range(Gp):
+        got = 0
+        for i in range(gs[g], gs[g + 1]):
+            r = work[2 * i]
+            end = work[2 * i + 3] if i + 1 < n and work[2 * i + 2] == r else pages[r]
+            got += end - work[2 * i + 1] + a
+        assert abs(got - V / Gp) < 2 * 4 + 2 * a, (g, got, V / Gp)

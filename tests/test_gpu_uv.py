@@ -25,12 +25,13 @@ pytestmark = pytest.mark.gpu
 
 
 def run_uv(w, heads, seed=0, workers=None, min_split_tokens=256, with_latent=True, tensors=None,
-           w_uv=None):
+           w_uv=None, split_cost=binding.SPLIT_COST_DEFAULT):
     q, kv, bt, lengths = tensors if tensors is not None else to_dev(w)
     dev = q.device
     wbits = w_uv if w_uv is not None else wl.uv_weights(heads, seed=seed)
     wdev = torch.from_numpy(wbits.view(np.int16)).to(dev)
-    dec = binding.FoldedDecoder(w.R, w.M, workers=workers, min_split_tokens=min_split_tokens)
+    dec = binding.FoldedDecoder(w.R, w.M, workers=workers, min_split_tokens=min_split_tokens,
+                                split_cost_pages=split_cost)
     dec.workspace[256:].fill_(0xFF)
     k = w.M // heads
     attn = torch.full((w.R * k, heads * 128), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -133,8 +134,8 @@ def test_small_shapes_every_row(k, H, lengths):
 
 def test_many_splits_per_request():
     w = wl.small(2, 4, 8, [64 * 200 + 5, 64 * 70], seed=6)
-    res = run_uv(w, 8, workers=300, min_split_tokens=0)
-    assert res["dec"].plan_host()[0].tolist() == [201, 70]
+    res = run_uv(w, 8, workers=300, min_split_tokens=0, split_cost=0)
+    assert res["dec"].plan_host()[0].tolist() == [190, 66]
     check_latent(w, res, tag="201-splits")
     check_projection(w, 8, res, tag="201-splits")
 

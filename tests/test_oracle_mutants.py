@@ -32,12 +32,16 @@ MUTANTS = {
     "exponent bias": ("exponent - 7);", "exponent - 8);"),
     "sign dropped": ("return sign ? -magnitude : magnitude;", "return magnitude;"),
     "merge weight base": ("double w = exp2(lse[s] - *lse_out);", "double w = exp(lse[s] - *lse_out);"),
-    "plan cut not moved to the request start": ("cut[g] = off[r];", "cut[g] = c;"),
-    "plan cut not moved to the request end": ("cut[g] = off[r] + pages[r];", "cut[g] = c;"),
-    "plan ignores min split": ("int64_t Gp = P / minp;", "int64_t Gp = P;"),
+    "plan cut not moved to the request start": ("cut[g] = voff[r];", "cut[g] = c;"),
+    "plan cut not moved to the request end": ("cut[g] = end;", "cut[g] = c;"),
+    "plan ignores min split": ("int64_t Gp = V / minp;", "int64_t Gp = V;"),
     "plan ignores max splits": ("if (Gp > max_splits)\n            Gp = max_splits;", ""),
-    "plan cuts rounded up": ("int64_t c = g * P / Gp;", "int64_t c = (g * P + Gp - 1) / Gp;"),
-    "plan group start off by one": ("work[2 * i + 1] >= cut[g])", "work[2 * i + 1] > cut[g])"),
+    "plan cuts rounded up": ("int64_t c = g * V / Gp;", "int64_t c = (g * V + Gp - 1) / Gp;"),
+    "plan group start off by one": ("if (start >= cut[g])", "if (start > cut[g])"),
+    "plan heads not laid out": ("V += pages[r] > 0 ? a + pages[r] : 0;", "V += pages[r];"),
+    "plan cut page counts the head": ("(int32_t)(cut[g] - voff[r] - a);", "(int32_t)(cut[g] - voff[r]);"),
+    "plan item start skips the head": ("(work[2 * i + 1] > 0 ? a + work[2 * i + 1] : 0)",
+                                       "work[2 * i + 1]"),
     "fixed groups rounded up": ("gstart[g] = (int32_t)(g * n / G);",
                                 "gstart[g] = (int32_t)((g * n + G - 1) / G);"),
     "fixed remainder to the end": ("(int32_t)(s * q + (s < rem ? s : rem));", "(int32_t)(s * q);"),
@@ -56,6 +60,7 @@ PIN_TESTS = [
     plan_pins.test_plan_worked_example_two_requests,
     plan_pins.test_plan_worked_example_cuts_inside_a_request,
     plan_pins.test_plan_worked_example_moved_cuts,
+    plan_pins.test_plan_worked_example_split_cost,
     plan_pins.test_plan_worked_example_row_tiles_and_max_splits,
     plan_pins.test_plan_fixed_mode,
     lambda: plan_pins.test_plan_properties_random(3),

@@ -76,13 +76,14 @@ def pieces(work, n, lengths):
     return out
 
 
-def check_plan(lengths, M, MT, W, min_tokens=256, max_splits=256, mode=oracle.BALANCED):
+def check_plan(lengths, M, MT, W, min_tokens=256, max_splits=256, mode=oracle.BALANCED,
+               cost=0):
     """Every property of a plan that holds in both modes, plus the group rule of each mode;
     returns (counts, offsets, work, n, items, gstart)."""
     lengths = list(lengths)
     R = len(lengths)
     counts, offsets, work, n = oracle.plan(lengths, max(pages_of(lengths) + [1]), M, MT, W,
-                                           min_tokens, max_splits, mode)
+                                           min_tokens, max_splits, mode, split_cost=cost)
     pages = pages_of(lengths)
     P = sum(pages)
     G = groups_of(W, M, MT)
@@ -116,29 +117,34 @@ def check_plan(lengths, M, MT, W, min_tokens=256, max_splits=256, mode=oracle.BA
         return counts, offsets, work, n, items, gstart
     # BALANCED: pieces at least the minimum split unless whole requests
     assert all(e - f >= minp or (f == 0 and e == pages[r]) for r, f, e in items)
-    Gp = max(1, min(G, max_splits, P // minp))
+    # each non-empty request a head of `cost` pages and its pages, end to end
+    v = [p + cost if p else 0 for p in pages]
+    voff = [sum(v[:r]) for r in range(R)]
+    V = sum(v)
+    Gp = max(1, min(G, max_splits, V // minp))
     assert all(g == n for g in gstart[Gp:])
-    # group g takes the pages [B_g, B_{g+1}): B_g is the start of its first item (P if none)
-    starts = [sum(pages[:r]) + f for r, f, _ in items]
-    bounds = [starts[i] if i < n else P for i in gstart[:Gp + 1]]
-    off = [sum(pages[:r]) for r in range(R)] + [P]
+    # group g takes [B_g, B_{g+1}): B_g is the start of its first item (V if none), a
+    # request's first item starting at its head
+    starts = [voff[r] + (cost + f if f else 0) for r, f, _ in items]
+    bounds = [starts[i] if i < n else V for i in gstart[:Gp + 1]]
     for g, B in enumerate(bounds):
-        c = g * P // Gp
-        inside = [r for r in range(R) if off[r] < c < off[r] + pages[r]]
+        c = g * V // Gp
+        inside = [r for r in range(R) if voff[r] < c < voff[r] + v[r]]
         if not inside:
             assert B == c
         else:
             r = inside[0]
-            if c - off[r] < minp:
-                assert B == off[r]
-            elif off[r] + pages[r] - c < minp:
-                assert B == off[r] + pages[r]
+            x = c - voff[r] - cost
+            if x < minp:
+                assert B == voff[r]
+            elif pages[r] - x < minp:
+                assert B == voff[r] + v[r]
             else:
                 assert B == c
-    # a request's splits start exactly at the group boundaries strictly inside it
+    # a request's splits start at page 0 and at the group boundaries strictly inside it
     for r in range(R):
         if pages[r]:
-            cuts = sorted({B - off[r] for B in bounds if off[r] < B < off[r] + pages[r]})
+            cuts = sorted({B - voff[r] - cost for B in bounds if voff[r] < B < voff[r] + v[r]})
             assert [f for _, f, _ in items[offsets[r]:offsets[r + 1]]] == [0] + cuts
     return counts, offsets, work, n, items, gstart
 
@@ -175,6 +181,24 @@ def test_plan_worked_example_moved_cuts():
     assert work[:6].tolist() == [0, 0, 0, 2, 1, 0]
     assert oracle.group_starts(work, 2, 4, 32, 32).tolist() == [0, 1, 2, 2, 3]
     assert oracle.item_range(work, n, [320, 182], 2) == (1, 0, 182)
+
+
+def test_plan_worked_example_split_cost():
+    # pages [4, 5] with a 2-page head each: V = 13 over 4 groups, cuts at 3, 6, 9; cut 3 is
+    # page 1 of request 0, 6 the start of request 1, 9 page 1 of request 1
+    counts, offsets, work, n = oracle.plan([256, 300], 5, M=32, MT=32, W=4, min_split_tokens=0,
+                                           split_cost=2)
+    assert counts.tolist() == [2, 2] and n == 4
+    assert work[:8].tolist() == [0, 0, 0, 1, 1, 0, 1, 1]
+    assert oracle.group_starts(work, 2, 4, 32, 32).tolist() == [0, 1, 2, 3, 4]
+    # the same lengths without the heads: cuts at 2, 4 (the boundary) and 6
+    counts, _, work, n = oracle.plan([256, 300], 5, M=32, MT=32, W=4, min_split_tokens=0)
+    assert work[:8].tolist() == [0, 0, 0, 2, 1, 0, 1, 2]
+    # a head of 3 pages, 2 groups, minimum 2 pages: V = 15, cut 7 is page 7 - 7 - 3 < 2 of
+    # request 1 (whose head starts at 7): moved to its start
+    counts, _, work, n = oracle.plan([256, 300], 5, M=32, MT=32, W=2, min_split_tokens=128,
+                                     split_cost=3)
+    assert counts.tolist() == [1, 1] and oracle.group_starts(work, 2, 2, 32, 32).tolist() == [0, 1, 2]
 
 
 def test_plan_worked_example_row_tiles_and_max_splits():
@@ -223,22 +247,26 @@ def test_plan_properties_random(seed):
     min_tokens = int(rng.choice([0, 64, 256, 1000]))
     max_splits = int(rng.choice([2, 16, 256]))
     for mode in (oracle.BALANCED, oracle.FIXED):
-        check_plan(lengths, M, MT, W, min_tokens, max_splits, mode)
+        for cost in (0, 3):
+            check_plan(lengths, M, MT, W, min_tokens, max_splits, mode, cost)
 
 
-def test_plan_balance_bound():
-    # every group's pages lie within two minimum splits of P / Gp
+@pytest.mark.parametrize("cost", [0, 4])
+def test_plan_balance_bound(cost):
+    # every group's cost (its pages and `cost` per item) lies within two minimum splits and
+    # two heads of V / Gp
     rng = np.random.default_rng(7)
     for _ in range(20):
         R = int(rng.integers(1, 200))
         lengths = np.floor(np.exp(rng.uniform(np.log(64), np.log(65536), R))).astype(np.int64)
         minp = 4
-        counts, offsets, work, n, items, gstart = check_plan(lengths, 56, 64, 256, 64 * minp)
-        P = sum(pages_of(lengths))
-        Gp = min(256, P // minp)
+        counts, offsets, work, n, items, gstart = check_plan(lengths, 56, 64, 256, 64 * minp,
+                                                             cost=cost)
+        V = sum(pages_of(lengths)) + cost * R
+        Gp = min(256, V // minp)
         for g in range(Gp):
-            got = sum(e - f for _, f, e in items[gstart[g]:gstart[g + 1]])
-            assert abs(got - P / Gp) < 2 * minp
+            got = sum(e - f + cost for _, f, e in items[gstart[g]:gstart[g + 1]])
+            assert abs(got - V / Gp) < 2 * minp + 2 * cost
 
 
 def test_plan_exhaustive_small():
@@ -248,7 +276,8 @@ def test_plan_exhaustive_small():
         for lengths in itertools.product(choices, repeat=R):
             for W in (1, 3, 8):
                 for min_tokens in (0, 128, 256):
-                    check_plan(list(lengths), 32, 32, W, min_tokens)
+                    for cost in (0, 1, 4):
+                        check_plan(list(lengths), 32, 32, W, min_tokens, cost=cost)
                 check_plan(list(lengths), 32, 32, W, 0, mode=oracle.FIXED)
 
 

@@ -68,22 +68,23 @@ def test_sanitized_attend_matches(driver):
     assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
 
 
-@pytest.mark.parametrize("lengths,M,MT,W,ms,mode", [
-    ([200, 317], 32, 32, 256, 256, 0),
-    ([0, 0, 5, 64 * 300, 1], 56, 64, 40, 0, 0),
-    ([8192] * 64, 32, 32, 256, 256, 1),
-    ([131072] + [1024] * 15, 448, 128, 256, 256, 0),
-    (list(range(0, 5000, 37)), 256, 128, 96, 64, 1),
+@pytest.mark.parametrize("lengths,M,MT,W,ms,mode,cost", [
+    ([200, 317], 32, 32, 256, 256, 0, 0),
+    ([0, 0, 5, 64 * 300, 1], 56, 64, 40, 0, 0, 3),
+    ([8192] * 64, 32, 32, 256, 256, 1, 4),
+    ([131072] + [1024] * 15, 448, 128, 256, 256, 0, 4),
+    (list(range(0, 5000, 37)), 256, 128, 96, 64, 1, 0),
 ])
-def test_sanitized_plan_matches(driver, lengths, M, MT, W, ms, mode):
+def test_sanitized_plan_matches(driver, lengths, M, MT, W, ms, mode, cost):
     R = len(lengths)
     list_len = 2 * (R + 2 * W)
     cols = max(1, max((l + 63) // 64 for l in lengths))
     lens = np.array(lengths, np.int32)
-    payload = np.array([R, cols, M, MT, W, ms, 256, mode, list_len], np.int32).tobytes() + lens.tobytes()
+    payload = (np.array([R, cols, M, MT, W, ms, 256, cost, mode, list_len], np.int32).tobytes() +
+               lens.tobytes())
     data = np.frombuffer(run(driver, "plan", payload, 4 * (1 + R + R + 1 + list_len)), np.int32)
     counts, offsets, work, n = oracle.plan(lens, cols, M, MT, W, min_split_tokens=ms,
-                                           mode=mode, list_len=list_len)
+                                           mode=mode, list_len=list_len, split_cost=cost)
     assert data[0] == n
     assert np.array_equal(data[1:1 + R], counts)
     assert np.array_equal(data[1 + R:2 + 2 * R], offsets)
