@@ -21,7 +21,14 @@ MAX_ROWS = 1024
 MAX_REQS = 4096
 MAX_SPLITS = 256
 MAX_SPLIT_COST = 4096
-SPLIT_COST_DEFAULT = 4   # pages a split costs its worker beyond its own (query rows, partials)
+# pages a split costs its worker beyond its own (query rows, partials), measured on gfx950
+SPLIT_COST_STREAM = 8      # 32- and 64-row tiles
+SPLIT_COST_TILE128 = 4     # 128-row tiles
+
+
+def split_cost_default(mtile):
+    """The library's measured split cost for a row tile of ``mtile`` rows."""
+    return SPLIT_COST_TILE128 if mtile == 128 else SPLIT_COST_STREAM
 
 OK = 0
 ERR_INVALID = -1
@@ -175,7 +182,9 @@ def workspace_bytes(num_reqs, rows_per_req, workers):
 
 
 def make_params(rows_per_req, mtile, workers, min_split_tokens=256, max_splits=MAX_SPLITS,
-                mode=PLAN_BALANCED, split_cost_pages=SPLIT_COST_DEFAULT) -> PlanParams:
+                mode=PLAN_BALANCED, split_cost_pages=None) -> PlanParams:
+    if split_cost_pages is None:
+        split_cost_pages = split_cost_default(mtile)
     return PlanParams(rows_per_req, mtile, workers, min_split_tokens, max_splits, mode,
                       split_cost_pages)
 
@@ -280,7 +289,7 @@ class FoldedDecoder:
 
     def __init__(self, max_reqs, rows_per_req, device=None, mode=PLAN_BALANCED,
                  min_split_tokens=256, max_splits=MAX_SPLITS, workers=None, mtile=None,
-                 split_cost_pages=SPLIT_COST_DEFAULT):
+                 split_cost_pages=None):
         import torch
 
         load()

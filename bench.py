@@ -195,7 +195,7 @@ class Runner:
         self.pools = [kv0] + [kv0.clone() for _ in range(max(0, pools - 1))]
         self.dec = binding.FoldedDecoder(
             R, M, device=dev, mode=mode, mtile=mtile, workers=workers,
-            split_cost_pages=binding.SPLIT_COST_DEFAULT if split_cost is None else split_cost)
+            split_cost_pages=split_cost)
         self.bmm1, self.bmm2 = binding.bmm_scales(w.sm_scale, w.q_scale, w.k_scale)
         self.out = torch.empty((R, M, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((R, M), dtype=torch.float32, device=dev)

@@ -47,7 +47,8 @@ extern "C" {
 #define AMLA_MAX_REQS 4096    /* most requests one plan takes */
 #define AMLA_MAX_SPLITS 256   /* most splits per request */
 #define AMLA_MAX_SPLIT_COST 4096  /* largest split_cost_pages */
-#define AMLA_SPLIT_COST_DEFAULT 4
+#define AMLA_SPLIT_COST_STREAM 8   /* measured split cost for 32- and 64-row tiles */
+#define AMLA_SPLIT_COST_TILE128 4  /* measured split cost for 128-row tiles */
 
 #define AMLA_MAX_SOURCES 64   /* most DCP sources amla_merge_sources takes */
 
@@ -82,7 +83,8 @@ extern "C" {
  *   mode              AMLA_PLAN_BALANCED or AMLA_PLAN_FIXED
  *   split_cost_pages  BALANCED: what one split costs its worker beyond its pages (loading
  *                     its query rows, writing its partials), in pages, 0..AMLA_MAX_SPLIT_COST;
- *                     AMLA_SPLIT_COST_DEFAULT is this library's measured figure for gfx950
+ *                     this library's measured figures for gfx950: AMLA_SPLIT_COST_STREAM
+ *                     (MT = 32, 64) and AMLA_SPLIT_COST_TILE128 (MT = 128)
  */
 typedef struct amla_plan_params {
     int32_t rows_per_req;

@@ -23,7 +23,7 @@ def to_dev(w):
 
 
 def run_gpu(w, mode=binding.PLAN_BALANCED, min_split_tokens=256, workers=None, mtile=None,
-            decoder=None, tensors=None, split_cost=binding.SPLIT_COST_DEFAULT):
+            decoder=None, tensors=None, split_cost=None):
     """Plan + decode + combine on cuda:0.  Output, LSE and workspace start as NaN, so any
     value the kernels fail to write shows up."""
     q, kv, bt, lengths = tensors if tensors is not None else to_dev(w)

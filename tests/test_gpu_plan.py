@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 def plan_both(lengths, M, mode=binding.PLAN_BALANCED, min_split_tokens=256, workers=None,
-              max_splits=256, split_cost=binding.SPLIT_COST_DEFAULT):
+              max_splits=256, split_cost=None):
     lengths = np.asarray(lengths, dtype=np.int32)
     R = len(lengths)
     cols = max(1, int(((lengths.astype(np.int64) + 63) // 64).max()) if R else 1)

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_uv(w, heads, seed=0, workers=None, min_split_tokens=256, with_latent=True, tensors=None,
-           w_uv=None, split_cost=binding.SPLIT_COST_DEFAULT):
+           w_uv=None, split_cost=None):
     q, kv, bt, lengths = tensors if tensors is not None else to_dev(w)
     dev = q.device
     wbits = w_uv if w_uv is not None else wl.uv_weights(heads, seed=seed)
