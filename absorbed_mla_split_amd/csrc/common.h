@@ -28,16 +28,10 @@ constexpr int kPlanThreads = 256;
 // entries.
 constexpr int kPlanSlack = 2;
 constexpr float kLog2e = 1.4426950408889634f;
-// Lazy max: the running row max is only raised when a page's max exceeds it by more
-// than 2^kTau, so p = 2^(t - m) <= 2^kTau; P is scaled by 2^kPScale before the E4M3
-// cast (kTau + kPScale <= 8 keeps it <= 256 < 448) to keep small weights out of the
-// subnormal range.
-constexpr float kTau = 2.0f;
-constexpr float kPScale = 6.0f;
-// 128-row decode: P = 2^(s - m + kPExp) with m the row's reference plus a whole number,
-// at or above its running max, so P <= 2^8 < 448; the output stays relative to the
-// reference, which only moves when the running max passes it by more than kRefGap (FP32
-// headroom for the unnormalised O).
+// Softmax of the decode kernels: P = 2^(s - m + kPExp) with m the row's reference plus a
+// whole number per key block, at or above that block's running max, so P <= 2^8 < 448 (the
+// E4M3 range); the output stays relative to the reference, which only moves when the
+// running max passes it by more than kRefGap (FP32 headroom for the unnormalised O).
 constexpr float kPExp = 8.0f;
 constexpr int kRefGap = 64;
 
