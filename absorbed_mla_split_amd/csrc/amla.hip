@@ -172,8 +172,17 @@ __device__ int64_t block_exclusive_scan64(int64_t v, int64_t *scratch, int64_t *
     return before + incl - v;
 }
 
+// x / y for 0 <= x, 0 < y: 32-bit division when both fit (a 64-bit one is a long software
+// sequence; the plan's products fit 32 bits for any realistic batch)
+__device__ inline int64_t udiv64(int64_t x, int64_t y)
+{
+    if ((uint64_t)x <= 0xFFFFFFFFull && (uint64_t)y <= 0xFFFFFFFFull)
+        return (int64_t)((uint32_t)x / (uint32_t)y);
+    return x / y;
+}
+
 // ceil(x / y) for x >= 0, y > 0
-__device__ inline int64_t cdiv64(int64_t x, int64_t y) { return x == 0 ? 0 : (x - 1) / y + 1; }
+__device__ inline int64_t cdiv64(int64_t x, int64_t y) { return x == 0 ? 0 : udiv64(x - 1, y) + 1; }
 
 // The split plan, one workgroup; thread t owns the requests [t * per, (t + 1) * per).
 // BALANCED (page "...cutedsl.mla.balanced", module docstring: split counts planned on the
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
     if (tid == 0) voff[R] = V;
 
     // 2. counts and item offsets
-    int64_t Gp = V / minp;
+    int64_t Gp = udiv64(V, minp);
     Gp = Gp < 1 ? 1 : Gp;
     Gp = Gp < G ? Gp : G;
     Gp = Gp < a.max_splits ? Gp : a.max_splits;
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
             w[1] = 0;
             for (int64_t g = g0; g <= g1; ++g) {
                 w[2 * (g - g0 + 1)] = r;
-                w[2 * (g - g0 + 1) + 1] = (int32_t)(g * V / Gp - s);
+                w[2 * (g - g0 + 1) + 1] = (int32_t)(udiv64(g * V, Gp) - s);
             }
             irun += (int32_t)(1 + (g1 >= g0 ? g1 - g0 + 1 : 0));
         } else {
@@ -302,9 +311,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a)
     for (int64_t g = tid; g <= G; g += kPlanThreads) {
         int32_t first = N;
         if (!balanced) {
-            first = (int32_t)(g * N / G);
+            first = (int32_t)udiv64(g * N, G);
         } else if (g < Gp && V > 0) {
-            const int64_t c = g * V / Gp;
+            const int64_t c = udiv64(g * V, Gp);
             int lo = 1, hi = R;                 // the first request with voff > c ...
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
@@ -373,13 +382,14 @@ __device__ __forceinline__ void combine_row(const CombineArgs &a, int64_t g, int
 {
     const int width = 256 * PER_LANE;
     uint16_t *out = a.out + g * kVDim + band * width;
+    // the next batch of split rows (past the last split: zeros, no load; c is uniform)
     auto load_batch = [&](int s0, v4f (&part)[kCombineBatch][PER_LANE]) {
 #pragma unroll
         for (int b = 0; b < kCombineBatch; ++b) {
-            const int s = s0 + b < c ? s0 + b : c - 1;
-            const float *p = a.partial + ((base + s) * a.rows + i) * kVDim + band * width;
+            const float *p = a.partial + ((base + s0 + b) * a.rows + i) * kVDim + band * width;
 #pragma unroll
-            for (int k = 0; k < PER_LANE; ++k) part[b][k] = *(const v4f *)(p + 4 * (lane + 64 * k));
+            for (int k = 0; k < PER_LANE; ++k)
+                part[b][k] = s0 + b < c ? *(const v4f *)(p + 4 * (lane + 64 * k)) : v4f{0, 0, 0, 0};
         }
     };
     float ls[kLsePerLane];
