@@ -8,19 +8,19 @@
 // FP32 partials and a log2 LSE, and a reducer merging the splits into BF16 rows.
 //
 // gfx950 mapping (this library's design, not the pages'):
-//   * plan    (this file) one 256-thread workgroup.  Up to 256 requests: every wave derives
-//             the chunk and the scans by itself (DPP, no barrier), then each thread places one
-//             run of equal-size splits by counting the runs that sort before it.  More
-//             requests: block reductions and scans, a rank or bitonic sort of the runs.
-//   * decode  one persistent workgroup per CU; a work unit is (request, split, row tile of
-//             MT rows); pages (64 tokens x 576 B) go HBM -> LDS by global_load_lds_dwordx4
-//             into a ring of four page slots; S^T = K Q^T and O^T += V^T P^T on
-//             v_mfma_f32_32x32x64_f8f6f4 (the accumulator layout puts one query row per
-//             lane); P in E4M3 against a per-row reference, each key block's P scaled by its
-//             own E8M0 byte in the P V MFMA.  decode_stream.hip: MT = 32, 64 (score and
-//             value waves one entry apart, two waves per SIMD, a stream of entries across
-//             work units); decode128.hip: MT = 128 (four waves per page, key blocks split
-//             between wave pairs, 256 output accumulators per lane in AGPRs).
+//   * plan    (this file) one 256-thread workgroup: the requests' pages (each charged a
+//             head of a few pages for its split's overhead) laid end to end and cut into
+//             equal ranges, one per group of workers; counts, items and group starts in
+//             closed form per request (block scans, no sort).
+//   * decode  one persistent workgroup per CU; each group of ceil(M/MT) workers walks its
+//             items, a work unit being (item, row tile of MT rows); pages (64 tokens x 576 B)
+//             go HBM -> LDS by global_load_lds_dwordx4 into a ring of page slots; S^T = K Q^T
+//             and O^T += V^T P^T on v_mfma_f32_32x32x64_f8f6f4 (the accumulator layout puts
+//             one query row per lane); P in E4M3 against a per-row reference, each key
+//             block's P scaled by its own E8M0 byte in the P V MFMA.  decode_stream.hip:
+//             MT = 32, 64 (score and value waves one entry apart, two waves per SIMD, a
+//             stream of entries across work units); decode128.hip: MT = 128 (four waves,
+//             each owning 32 rows end to end, 256 output accumulators per lane in AGPRs).
 //   * combine (this file) one wave per (row, band); merges the splits of a row with exp2
 //             weights.
 //   * combine_uv  the merge fused with the W_UV up-projection (BF16 MFMA).
