@@ -43,61 +43,8 @@ using namespace amla;
 
 // ------------------------------------------------------------------ block utilities
 
-template <typename T>
-__device__ inline T wave_sum(T v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-template <typename T>
-__device__ inline T wave_max(T v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        T w = __shfl_xor(v, o);
-        v = w > v ? w : v;
-    }
-    return v;
-}
-
-// All-lane reductions of a wave without LDS traffic: DPP within rows of 16 lanes, then
-// v_permlane16_swap / v_permlane32_swap across rows.  64-bit values move as two halves.
-template <int CTRL>
-__device__ __forceinline__ int64_t dpp64(int64_t v)
-{
-    const int lo = __builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_mov_dpp((int)(v >> 32), CTRL, 0xf, 0xf, false);
-    return ((int64_t)hi << 32) | (uint32_t)lo;
-}
-
-template <bool MAX>
-__device__ __forceinline__ int64_t op64(int64_t a, int64_t b)
-{
-    return MAX ? (a > b ? a : b) : a + b;
-}
-
-template <bool MAX>
-__device__ int64_t wave_all64(int64_t v)
-{
-    v = op64<MAX>(v, dpp64<0x128>(v));   // row_ror:8
-    v = op64<MAX>(v, dpp64<0x124>(v));   // row_ror:4
-    v = op64<MAX>(v, dpp64<0x4e>(v));    // quad_perm [2,3,0,1]
-    v = op64<MAX>(v, dpp64<0xb1>(v));    // quad_perm [1,0,3,2]
-    {
-        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        v = op64<MAX>(((int64_t)hi[0] << 32) | lo[0], ((int64_t)hi[1] << 32) | lo[1]);
-    }
-    {
-        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        v = op64<MAX>(((int64_t)hi[0] << 32) | lo[0], ((int64_t)hi[1] << 32) | lo[1]);
-    }
-    return v;
-}
-
+// All-lane max (MAX) or sum of a wave without LDS traffic: DPP within rows of 16 lanes, then
+// v_permlane16_swap / v_permlane32_swap across rows.
 template <bool MAX>
 __device__ float wave_allf(float v)
 {

@@ -413,7 +413,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         // slots, then (rarely) the tiles follow a reference move, and the page's state becomes
         // the previous page's.
         auto page = [&](int t, auto prev) {
-            constexpr bool PREV = decltype(prev)::value;
             if (t > 0) wait_pages_then_barrier(t + 1 < size ? 1 : 0);
             const uint8_t *slot_t = lds + (t % kSlots) * kPageBytes;
             const uint8_t *slot_p = lds + ((t + kSlots - 1) % kSlots) * kPageBytes;
