@@ -913,7 +913,14 @@ int amla_decode_config(int32_t compute_units, int32_t rows_per_req, int32_t *wor
         rows_per_req > AMLA_MAX_ROWS)
         return AMLA_ERR_INVALID;
     *workers_out = compute_units;
-    *mtile_out = rows_per_req <= 32 ? 32 : (rows_per_req <= 64 ? 64 : 128);
+    if (rows_per_req <= 64) {
+        *mtile_out = rows_per_req <= 32 ? 32 : 64;
+    } else {
+        // 128-row tiles unless 64-row tiles leave fewer padding rows in the last tile
+        const int pad64 = ceil_div(rows_per_req, 64) * 64 - rows_per_req;
+        const int pad128 = ceil_div(rows_per_req, 128) * 128 - rows_per_req;
+        *mtile_out = pad128 <= pad64 ? 128 : 64;
+    }
     return AMLA_OK;
 }
 

@@ -102,7 +102,10 @@ def test_decode_config():
     assert b.decode_config(256, 32) == (256, 32)
     assert b.decode_config(256, 56) == (256, 64)
     assert b.decode_config(256, 256) == (256, 128)
-    assert b.decode_config(256, 448) == (256, 128)
+    assert b.decode_config(256, 448) == (256, 64)        # 7 x 64 rows, no padding
+    assert b.decode_config(256, 1024) == (256, 128)
+    assert b.decode_config(256, 129) == (256, 64)        # 3 x 64 pads 63 rows, 2 x 128 127
+    assert b.decode_config(256, 200) == (256, 128)       # 56 padding rows either way
     with pytest.raises(b.AmlaError):
         b.decode_config(256, 0)
     with pytest.raises(b.AmlaError):

@@ -77,7 +77,8 @@ def test_small_shapes_every_row(k, H, lengths, min_split_tokens):
 
 
 @pytest.mark.parametrize("k,H,mtile", [(4, 8, 64), (4, 8, 128), (7, 8, 32), (7, 8, 128),
-                                        (4, 64, 32), (4, 64, 64), (3, 11, 128)])
+                                        (4, 64, 32), (4, 64, 64), (3, 11, 128), (7, 64, 128),
+                                        (5, 13, 128), (3, 43, 128)])
 def test_every_tile_size_for_any_rows(k, H, mtile):
     # the row tile is a free parameter of the ABI: every kernel on shapes it is not picked
     # for by default (several tiles per split, or most of a tile idle)
@@ -213,6 +214,16 @@ def test_full_size_sampled(cfg):
     out, lse, dec = run_gpu(w)
     assert dec.device_status() == 0
     compare(w, out, lse, rows=sample_rows(w, 4 if cfg != "c3" else 2), tag=cfg)
+
+
+@pytest.mark.parametrize("cfg,mtile", [("c4", 64), ("c5", 128)])
+def test_full_size_other_tile_sampled(cfg, mtile):
+    # the tile size the launch shape does not pick for these rows (c4: 64-row tiles; c5:
+    # 128-row tiles, half of the last one idle)
+    w = wl.generate(cfg)
+    out, lse, dec = run_gpu(w, mtile=mtile)
+    assert dec.params.mtile == mtile and dec.device_status() == 0
+    compare(w, out, lse, rows=sample_rows(w, 4), tag=f"{cfg}-MT{mtile}")
 
 
 def test_c5_unfolded_baseline_sampled():
