@@ -22,13 +22,14 @@ MAX_REQS = 4096
 MAX_SPLITS = 256
 MAX_SPLIT_COST = 4096
 # pages a split costs its worker beyond its own (query rows, partials), measured on gfx950
-SPLIT_COST_STREAM = 8      # 32- and 64-row tiles
-SPLIT_COST_TILE128 = 4     # 128-row tiles
+SPLIT_COST_ONE_TILE = 8    # splits of one row tile (M <= MT)
+SPLIT_COST_MULTI_TILE = 4  # splits of several row tiles
 
 
-def split_cost_default(mtile):
-    """The library's measured split cost for a row tile of ``mtile`` rows."""
-    return SPLIT_COST_TILE128 if mtile == 128 else SPLIT_COST_STREAM
+def split_cost_default(mtile, rows_per_req):
+    """The library's measured split cost for splits of ``rows_per_req`` rows in tiles of
+    ``mtile`` rows."""
+    return SPLIT_COST_ONE_TILE if rows_per_req <= mtile else SPLIT_COST_MULTI_TILE
 
 OK = 0
 ERR_INVALID = -1
@@ -184,7 +185,7 @@ def workspace_bytes(num_reqs, rows_per_req, workers):
 def make_params(rows_per_req, mtile, workers, min_split_tokens=256, max_splits=MAX_SPLITS,
                 mode=PLAN_BALANCED, split_cost_pages=None) -> PlanParams:
     if split_cost_pages is None:
-        split_cost_pages = split_cost_default(mtile)
+        split_cost_pages = split_cost_default(mtile, rows_per_req)
     return PlanParams(rows_per_req, mtile, workers, min_split_tokens, max_splits, mode,
                       split_cost_pages)
 

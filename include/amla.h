@@ -47,8 +47,8 @@ extern "C" {
 #define AMLA_MAX_REQS 4096    /* most requests one plan takes */
 #define AMLA_MAX_SPLITS 256   /* most splits per request */
 #define AMLA_MAX_SPLIT_COST 4096  /* largest split_cost_pages */
-#define AMLA_SPLIT_COST_STREAM 8   /* measured split cost for 32- and 64-row tiles */
-#define AMLA_SPLIT_COST_TILE128 4  /* measured split cost for 128-row tiles */
+#define AMLA_SPLIT_COST_ONE_TILE 8    /* measured split cost when a split is one row tile */
+#define AMLA_SPLIT_COST_MULTI_TILE 4  /* measured split cost when a split has several tiles */
 
 #define AMLA_MAX_SOURCES 64   /* most DCP sources amla_merge_sources takes */
 
@@ -83,8 +83,9 @@ extern "C" {
  *   mode              AMLA_PLAN_BALANCED or AMLA_PLAN_FIXED
  *   split_cost_pages  BALANCED: what one split costs its worker beyond its pages (loading
  *                     its query rows, writing its partials), in pages, 0..AMLA_MAX_SPLIT_COST;
- *                     this library's measured figures for gfx950: AMLA_SPLIT_COST_STREAM
- *                     (MT = 32, 64) and AMLA_SPLIT_COST_TILE128 (MT = 128)
+ *                     this library's measured figures for gfx950: AMLA_SPLIT_COST_ONE_TILE
+ *                     when M <= MT (one worker per split), AMLA_SPLIT_COST_MULTI_TILE
+ *                     otherwise
  */
 typedef struct amla_plan_params {
     int32_t rows_per_req;

@@ -46,10 +46,12 @@ def test_header_constants_match_binding():
     assert int(consts["AMLA_MAX_SOURCES"]) == b.MAX_SOURCES
     assert int(consts["AMLA_MAX_REQS"]) == b.MAX_REQS
     assert int(consts["AMLA_MAX_SPLIT_COST"]) == b.MAX_SPLIT_COST
-    assert int(consts["AMLA_SPLIT_COST_STREAM"]) == b.SPLIT_COST_STREAM
-    assert int(consts["AMLA_SPLIT_COST_TILE128"]) == b.SPLIT_COST_TILE128
-    assert b.make_params(448, 128, 256).split_cost_pages == b.SPLIT_COST_TILE128
-    assert b.make_params(56, 64, 256).split_cost_pages == b.SPLIT_COST_STREAM
+    assert int(consts["AMLA_SPLIT_COST_ONE_TILE"]) == b.SPLIT_COST_ONE_TILE
+    assert int(consts["AMLA_SPLIT_COST_MULTI_TILE"]) == b.SPLIT_COST_MULTI_TILE
+    assert b.make_params(448, 128, 256).split_cost_pages == b.SPLIT_COST_MULTI_TILE
+    assert b.make_params(448, 64, 256).split_cost_pages == b.SPLIT_COST_MULTI_TILE
+    assert b.make_params(56, 64, 256).split_cost_pages == b.SPLIT_COST_ONE_TILE
+    assert b.make_params(32, 32, 256).split_cost_pages == b.SPLIT_COST_ONE_TILE
     assert int(consts["AMLA_ERR_WORKSPACE"]) == b.ERR_WORKSPACE
     assert int(consts["AMLA_DEV_BAD_PAGE"]) == b.DEV_BAD_PAGE
     assert int(consts["AMLA_DEV_BAD_POSITION"]) == b.DEV_BAD_POSITION
