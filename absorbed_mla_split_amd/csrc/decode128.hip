@@ -6,6 +6,13 @@
 namespace amla {
 namespace {
 
+// An empty asm that takes x and gives it back: whatever computes x stays before this point.
+template <typename T>
+__device__ __forceinline__ void pin_vgpr(T &x)
+{
+    asm volatile("" : "+v"(x));
+}
+
 // S^T of one key block of a page for one k-step: the key block's K fragment (A) times the
 // row block's Q^T fragment (B), VGPR results.  The kernel's output accumulators are
 // AGPR-form MFMAs; this one is written here so that the score tile stays in VGPRs.  The
@@ -90,6 +97,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                                     // wg.step-th from its own tile
 
     const DmaOffsets dmao = dma_offsets(wave, lane);
+    // the pool bound as a 32-bit scalar (page ids are 32-bit)
+    const int pool32 = a.pool_pages < 0x7FFFFFFF ? (int)a.pool_pages : 0x7FFFFFFF;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t *)lds + wave * (kChunksPerWave * 1024);
 
     // V^T fragment reads (ds_read_b64_tr_b8): within each 16-lane group, source lane i
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         // page t of the split into its ring slot; rows past the request's length (only on
         // its last page) repeat the last valid row, so that P*V reads no foreign codes
         auto issue = [&](int t, int32_t pid) {
-            if (pid < 0 || pid >= a.pool_pages) {
+            if (pid < 0 || pid >= pool32) {
                 page_bad = true;
                 pid = 0;
             }
@@ -285,6 +294,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         // exponentials are done.
         v8i pf, pfa;
         int g0 = 0, g1 = 0, gp0 = 0, gp1 = 0;
+        // A slot's results are first read after the rare reference-move branch, and the
+        // compiler would sink the work that makes them below that branch, out of the MFMA
+        // slots; an empty asm that redefines them keeps the work in its slot.
+        auto here = [](auto &...x) { (pin_vgpr(x), ...); };
         float b0 = 0.f, b1 = 0.f, bp1 = 0.f;
 
         // Score-slot work for the previous page (PREV): its key-block-1 exponentials (two per
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         float pt[4];
         bool bt_next = false;
         int bt_block = 0;
-        auto prev_work = [&](auto ii, bool refill, const uint8_t *src, uint32_t dst, int rvalid,
+        auto prev_work = [&](auto ii, auto dma, const uint8_t *src, uint32_t dst, const uint32_t *co,
                              const uint8_t *slot_p, auto prev) {
             constexpr int i = decltype(ii)::value;
             constexpr bool PREV = decltype(prev)::value;
@@ -307,24 +320,30 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                     pt[2 * (i & 1) + e] = p;
                     ps1 += p;
                 }
+                here(ps1);
                 if constexpr (i & 1) {
                     int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], 0, false);
                     w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[2], pt[3], w4, true);
                     pfa[4 + (i >> 1)] = w4;
+                    here(pfa);
                 }
             }
-            if constexpr (PREV && i == 8) l_run += __builtin_amdgcn_ldexpf(ps1, gp1);
+            if constexpr (PREV && i == 8) {
+                l_run += __builtin_amdgcn_ldexpf(ps1, gp1);
+                here(l_run);
+            }
             if constexpr (PREV && i >= 9 && i <= 16) {
                 const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pfa[i - 9], false);
                 const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pfa[i - 9], true);
                 const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
                 if constexpr (i < 13) qs0 += d4; else qs1 += d4;
-                if constexpr (i == 16)
+                here(qs0, qs1);
+                if constexpr (i == 16) {
                     lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
+                    here(lq_run);
+                }
             }
-            if constexpr (i >= 9) {
-                if (refill) issue_chunk(src, dst + 1024 * (i - 9), chunk_offset(dmao, i - 9, rvalid, wave, lane));
-            }
+            if constexpr (decltype(dma)::value && i >= 9) issue_chunk(src, dst + 1024 * (i - 9), co[i - 9]);
             if constexpr (i == 0) {
                 // the next 64 block-table entries, well before they are read (and before
                 // this page's refill, so that the barrier's vmcnt wait still counts the
@@ -385,6 +404,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                     b0 = none ? 0.f : (kPExp - (float)g0) - m_ref;
                     b1 = none ? 0.f : (kPExp - (float)g1) - m_ref;
                     ps0 = 0.f;
+                    here(l_run, lq_run, b0, b1);
                 } else if constexpr (n >= 4 && n <= 11) {
                     constexpr int i = n - 4;
 #pragma unroll
@@ -393,13 +413,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                         pt[2 * (i & 1) + e] = p;
                         ps0 += p;
                     }
+                    here(ps0);
                     if constexpr (i & 1) {
                         int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], 0, false);
                         w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[2], pt[3], w4, true);
                         pf[i >> 1] = w4;
+                        here(pf);
                     }
                 } else if constexpr (n == 12) {
                     l_run += __builtin_amdgcn_ldexpf(ps0, g0);
+                    here(l_run);
                 }
             }
             if constexpr (n == 13) {
@@ -413,24 +436,37 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         // slots, then (rarely) the tiles follow a reference move, and the page's state becomes
         // the previous page's.
         auto page = [&](int t, auto prev) {
-            if (t > 0) wait_pages_then_barrier(t + 1 < size ? 1 : 0);
+            // page t has landed (the newest nine DMAs, page t+1's or a spare copy, may not)
+            if (t > 0) wait_pages_then_barrier(1);
             const uint8_t *slot_t = lds + (t % kSlots) * kPageBytes;
             const uint8_t *slot_p = lds + ((t + kSlots - 1) % kSlots) * kPageBytes;
-            // the ring refill: page t+2
+            // the ring refill: page t+2, into the slot that page t-2 used; past the unit's end
+            // a spare copy of its last page (the entry pid_next then holds) goes into that
+            // free slot, so that every page issues the same nine DMA instructions with no
+            // branch between the MFMA slots
             const bool refill = t + 2 < size;
             int32_t pid = pid_next;
-            if (refill && (pid < 0 || pid >= a.pool_pages)) {
-                page_bad = true;
+            if (pid < 0 || pid >= pool32) {
+                if (refill) page_bad = true;
                 pid = 0;
             }
             const uint8_t *src = kv_in + (int64_t)pid * kPageBytes;
             const uint32_t dst = lds_base + ((t + 2) % kSlots) * kPageBytes;
-            const int rvalid = L - (first + t + 2) * kPage;
+            const int rvalid = refill ? L - (first + t + 2) * kPage : kPage;
+            // the lane's source offsets of the refill's nine chunks, chosen once per page
+            uint32_t co[kChunksPerWave];
+            if (rvalid >= kPage) {
+#pragma unroll
+                for (int i = 0; i < kChunksPerWave; ++i) co[i] = chunk_offset(dmao, i, kPage, wave, lane);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kChunksPerWave; ++i) co[i] = chunk_offset(dmao, i, rvalid, wave, lane);
+            }
             bt_block = (t >> 6) + 1;
             bt_next = (t & 63) == 8 && 64 * bt_block < size;
             ps1 = qs0 = qs1 = 0.f;
             score_slots(std::true_type{}, slot_t, [&](auto ii) {
-                prev_work(ii, refill, src, dst, rvalid, slot_p, prev);
+                prev_work(ii, std::true_type{}, src, dst, co, slot_p, prev);
             });
             // keys of the page the lane's row sees, counted from the lane's first key
             // (4*half): element e of key block kb holds key 32kb + 8(e/4) + e%4 past it
@@ -458,11 +494,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         page(0, std::false_type{});
         for (int t = 1; t < size; ++t) page(t, std::true_type{});
         {
-            // the last page's key-block-1 exponentials and E4M3 sum, then its P V MFMAs
+            // the last page's key-block-1 exponentials and E4M3 sum, then its P V MFMAs; the
+            // spare copy issued by the last page lands first (the next unit's DMA reuses the
+            // ring)
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
             const uint8_t *slot_l = lds + ((size - 1) % kSlots) * kPageBytes;
             ps1 = qs0 = qs1 = 0.f;
             score_slots(std::false_type{}, slot_l, [&](auto ii) {
-                prev_work(ii, false, slot_l, 0u, 0, slot_l, std::true_type{});
+                prev_work(ii, std::false_type{}, slot_l, 0u, nullptr, slot_l, std::true_type{});
             });
             pv_slots(std::true_type{}, slot_l, pfa, 127 + (half ? gp1 : gp0), [&](auto nn) {
                 cur_work(nn, 0, 0, std::false_type{});
