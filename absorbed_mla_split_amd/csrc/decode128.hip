@@ -26,6 +26,19 @@ __device__ __forceinline__ void score_one(v16f &s, v8i k, v8i q)
         asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
 }
 
+// The row sums of the P that a P V MFMA takes, by the same MFMA with an all-ones A operand
+// (E4M3 1.0 in every byte) and the same B operand and scales: every element of lane l's
+// tile is the sum over the page's keys of row l % 32, as the P V MFMA weighs them.  VGPR
+// results, written here for the same reason as score_one.  The compiler does not see it as
+// an MFMA either, so it may write the operands with VALU instructions right before it: the
+// leading s_nop gives that write the wait states an MFMA operand read needs.
+__device__ __forceinline__ void psum_mfma(v16f &s, v8i ones, v8i p, int sa, int sb)
+{
+    asm volatile("s_nop 4\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+v"(s)
+                 : "v"(ones), "v"(p), "v"(sa), "v"(sb));
+}
+
 // 128-row tiles, four waves, each owning 32 rows of the tile end to end: wave w computes
 // S^T (the page's 64 keys, two key blocks of 32, x its rows [32w, +32)), the softmax of its
 // rows, and O^T (the 512 value dims, sixteen 32-dim tiles in AGPRs, x its rows).  The lane
@@ -34,8 +47,9 @@ __device__ __forceinline__ void score_one(v16f &s, v8i k, v8i q)
 // the waves exchange nothing, and meet only once per page, where the page ring advances.
 //
 // Each wave software-pipelines its pages: while the MFMAs of page t+1's scores run, the
-// VALU computes page t's softmax (mask, row max, reference, exponentials, E4M3 P), and
-// while page t's P V MFMAs run, the VALU adds up page t's E4M3 P.  The LDS ring holds
+// VALU computes page t's softmax (mask, row max, reference, exponentials, E4M3 P); page
+// t's P V MFMAs are followed by one more that sums that P per row (psum_mfma), so that O
+// is normalised by exactly the P it was built from.  The LDS ring holds
 // four pages: V of page t, K of page t+1 and two pages in flight; the DMA of page t+3 goes
 // into the slot that page t-1 used.  Read-only inputs are separate __restrict__
 // arguments; their uniform reads go through the constant address space (scalar loads,
@@ -196,10 +210,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         }
         wait_pages_then_barrier(0);
 
-        // the row's reference and its sums relative to it: FP32 P (for the LSE) and E4M3 P
-        // (O is normalised by the sum of the P it was built from); per lane the keys of
-        // its half, added over the lane pair at the end
-        float m_ref = -INFINITY, l_run = 0.f, lq_run = 0.f;
+        // the row's reference and the FP32 sum of P relative to it, for the LSE (per lane
+        // the keys of its half, added over the lane pair at the end)
+        float m_ref = -INFINITY, l_run = 0.f;
+        // the sums of the E4M3 P by the P V MFMAs' weights, in every element (psum_mfma):
+        // O is normalised by the sum of the P it was built from
+        v16f lq_acc = v16f{0};
+        v8i ones;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;
+        int scale_one = 127;
         v16f acc[16];   // O^T of dim tile n (dims [32n, +32)) x the wave's rows
 #pragma unroll
         for (int n = 0; n < 16; ++n) acc[n] = v16f{0};
@@ -214,9 +234,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         // so VALU work overlaps an MFMA only when it stands between two MFMAs.  A page is
         // therefore 34 slots of one MFMA followed by at most about one MFMA's worth of VALU
         // work: 18 score slots (page t's S^T, key block 0 then key block 1, k-steps 0-8)
-        // carrying page t-1's key-block-1 exponentials, its E4M3 sum and the ring refill, then
+        // carrying page t-1's key-block-1 exponentials and the ring refill, then
         // 16 P V slots (page t-1's O^T update, dim tiles 0-15) carrying page t's mask, row max,
-        // reference and key-block-0 exponentials.
+        // reference and key-block-0 exponentials, and one MFMA for page t-1's row sums.
 
         v16f sc[2];   // S^T of the page in flight: key blocks 0, 1
         // K fragment of score slot i (key block i / 9, k-step i % 9) of the page in `slot`
@@ -281,9 +301,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 work(nn);
                 __builtin_amdgcn_sched_barrier(0);
             });
-            if constexpr (PV)
+            if constexpr (PV) {
+                // the row sums of this P (after the last tile, whose operands it shares)
+                psum_mfma(lq_acc, ones, pfv, scale_one, sbv);
                 asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-                             "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::"v"(vr[15 % 3]), "v"(pfv));
+                             "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::"v"(vr[15 % 3]), "v"(pfv),
+                             "v"(ones), "v"(scale_one), "v"(sbv));
+            }
         };
 
         // Softmax state.  Page t's key block kb has whole-number gap g_kb and bias b_kb (P =
@@ -301,11 +325,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         float b0 = 0.f, b1 = 0.f, bp1 = 0.f;
 
         // Score-slot work for the previous page (PREV): its key-block-1 exponentials (two per
-        // slot, slots 0-7), their FP32 sum into l (slot 8), its E4M3 sum over the whole
-        // fragment (one dword per slot, slots 9-16, into lq at slot 16); the ring refill (REFILL:
+        // slot, slots 0-7), their FP32 sum into l (slot 8); the ring refill (REFILL:
         // one DMA instruction per slot, slots 9-17) and the first V^T fragments of the previous
         // page (slots 16, 17).
-        float ps1 = 0.f, qs0 = 0.f, qs1 = 0.f;
+        float ps1 = 0.f;
         float pt[4];
         bool bt_next = false;
         int bt_block = 0;
@@ -331,17 +354,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
             if constexpr (PREV && i == 8) {
                 l_run += __builtin_amdgcn_ldexpf(ps1, gp1);
                 here(l_run);
-            }
-            if constexpr (PREV && i >= 9 && i <= 16) {
-                const v2f x0 = __builtin_amdgcn_cvt_pk_f32_fp8(pfa[i - 9], false);
-                const v2f x1 = __builtin_amdgcn_cvt_pk_f32_fp8(pfa[i - 9], true);
-                const float d4 = (x0[0] + x0[1]) + (x1[0] + x1[1]);
-                if constexpr (i < 13) qs0 += d4; else qs1 += d4;
-                here(qs0, qs1);
-                if constexpr (i == 16) {
-                    lq_run += __builtin_amdgcn_ldexpf(qs0, gp0) + __builtin_amdgcn_ldexpf(qs1, gp1);
-                    here(lq_run);
-                }
             }
             if constexpr (decltype(dma)::value && i >= 9) issue_chunk(src, dst + 1024 * (i - 9), co[i - 9]);
             if constexpr (i == 0) {
@@ -399,12 +411,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                     g0 = g0 - moved < -127 ? -127 : g0 - moved;
                     g1 = g1 - moved < -127 ? -127 : g1 - moved;
                     l_run *= f;
-                    lq_run *= f;
                     const bool none = m_ref == -INFINITY;
                     b0 = none ? 0.f : (kPExp - (float)g0) - m_ref;
                     b1 = none ? 0.f : (kPExp - (float)g1) - m_ref;
                     ps0 = 0.f;
-                    here(l_run, lq_run, b0, b1);
+                    here(l_run, b0, b1);
                 } else if constexpr (n >= 4 && n <= 11) {
                     constexpr int i = n - 4;
 #pragma unroll
@@ -464,7 +475,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
             }
             bt_block = (t >> 6) + 1;
             bt_next = (t & 63) == 8 && 64 * bt_block < size;
-            ps1 = qs0 = qs1 = 0.f;
+            ps1 = 0.f;
             score_slots(std::true_type{}, slot_t, [&](auto ii) {
                 prev_work(ii, std::true_type{}, src, dst, co, slot_p, prev);
             });
@@ -482,6 +493,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
                 for (int n = 0; n < 16; ++n) scale_acc(acc[n], f);
+                lq_acc *= f;
                 asm volatile("s_nop 7" ::: "memory");
             }
 #pragma unroll
@@ -494,12 +506,12 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         page(0, std::false_type{});
         for (int t = 1; t < size; ++t) page(t, std::true_type{});
         {
-            // the last page's key-block-1 exponentials and E4M3 sum, then its P V MFMAs; the
+            // the last page's key-block-1 exponentials, then its P V MFMAs; the
             // spare copy issued by the last page lands first (the next unit's DMA reuses the
             // ring)
             __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
             const uint8_t *slot_l = lds + ((size - 1) % kSlots) * kPageBytes;
-            ps1 = qs0 = qs1 = 0.f;
+            ps1 = 0.f;
             score_slots(std::false_type{}, slot_l, [&](auto ii) {
                 prev_work(ii, std::false_type{}, slot_l, 0u, nullptr, slot_l, std::true_type{});
             });
@@ -510,12 +522,13 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
 
         if (page_bad && tid == 0) atomicOr(&header[kHdrStatus], AMLA_DEV_BAD_PAGE);
 
-        // epilogue: the lane pair's sums; LSE from the FP32 sum, O normalised by the E4M3
-        // sum (both carry P's 2^kPExp, which cancels in O / lq)
+        // epilogue: LSE from the FP32 sum (the lane pair's), O normalised by the E4M3 sum
+        // (both carry P's 2^kPExp, which cancels in O / lq)
         const size_t slot_idx = (size_t)item;
-        const float l = half_pair_sum(l_run), lq = half_pair_sum(lq_run);
-        // (the last P V MFMAs wrote the tiles read below through asm)
+        const float l = half_pair_sum(l_run);
+        // (the last P V MFMAs and psum_mfma wrote the tiles read below through asm)
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        const float lq = lq_acc[0];
         if (row < M) {
             if (half == 0) lse_out[slot_idx * M + row] = m_ref + __builtin_amdgcn_logf(l) - kPExp;
             const float inv = lq > 0.f ? a.out_scale / lq : 0.f;   // no key: O = 0
