@@ -39,6 +39,19 @@ __device__ __forceinline__ void psum_mfma(v16f &s, v8i ones, v8i p, int sa, int 
                  : "v"(ones), "v"(p), "v"(sa), "v"(sb));
 }
 
+// The page slots (score slots 0-17, then P V slots 18-33) that issue the ring refill's nine
+// DMA instructions, one each.  Score slots 9-17 measured best: slots 0-8 (next to the
+// exponentials) 8 % slower; every other score slot, or the chunks spread over both phases,
+// no faster.
+constexpr int kRefillSlots[kChunksPerWave] = {9, 10, 11, 12, 13, 14, 15, 16, 17};
+// the refill chunk issued in page slot `slot`, or -1
+constexpr int refill_chunk_at(int slot)
+{
+    for (int c = 0; c < kChunksPerWave; ++c)
+        if (kRefillSlots[c] == slot) return c;
+    return -1;
+}
+
 // 128-row tiles, four waves, each owning 32 rows of the tile end to end: wave w computes
 // S^T (the page's 64 keys, two key blocks of 32, x its rows [32w, +32)), the softmax of its
 // rows, and O^T (the 512 value dims, sixteen 32-dim tiles in AGPRs, x its rows).  The lane
@@ -325,8 +338,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         float b0 = 0.f, b1 = 0.f, bp1 = 0.f;
 
         // Score-slot work for the previous page (PREV): its key-block-1 exponentials (two per
-        // slot, slots 0-7), their FP32 sum into l (slot 8); the ring refill (REFILL:
-        // one DMA instruction per slot, slots 9-17) and the first V^T fragments of the previous
+        // slot, slots 0-7), their FP32 sum into l (slot 8); the ring refill (one DMA
+        // instruction per slot, by kRefillSlots) and the first V^T fragments of the previous
         // page (slots 16, 17).
         float ps1 = 0.f;
         float pt[4];
@@ -355,13 +368,14 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 l_run += __builtin_amdgcn_ldexpf(ps1, gp1);
                 here(l_run);
             }
-            if constexpr (decltype(dma)::value && i >= 9) issue_chunk(src, dst + 1024 * (i - 9), co[i - 9]);
             if constexpr (i == 0) {
                 // the next 64 block-table entries, well before they are read (and before
                 // this page's refill, so that the barrier's vmcnt wait still counts the
                 // refill as the newest nine)
                 if (bt_next) issue_bt(bt_block);
             }
+            if constexpr (decltype(dma)::value && refill_chunk_at(i) >= 0)
+                issue_chunk(src, dst + 1024 * refill_chunk_at(i), co[refill_chunk_at(i)]);
             if constexpr (PREV && i >= 16) vr[i - 16] = vtile(slot_p, i - 16);
         };
 
@@ -371,8 +385,11 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         float mx0 = -INFINITY, mx1 = -INFINITY, ps0 = 0.f;
         int32_t bt_v = 0;
         int moved = 0;   // log2 step of the reference on this page
-        auto cur_work = [&](auto nn, int t, int valid, auto softmax) {
+        auto cur_work = [&](auto nn, int t, int valid, auto softmax, auto dma, const uint8_t *src,
+                            uint32_t dst, const uint32_t *co) {
             constexpr int n = decltype(nn)::value;
+            if constexpr (decltype(dma)::value && refill_chunk_at(18 + n) >= 0)
+                issue_chunk(src, dst + 1024 * refill_chunk_at(18 + n), co[refill_chunk_at(18 + n)]);
             if constexpr (decltype(softmax)::value) {
                 if constexpr (n == 0) {
                     // the score MFMAs' results, read by VALU code: wait states the compiler
@@ -483,7 +500,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
             // (4*half): element e of key block kb holds key 32kb + 8(e/4) + e%4 past it
             const int valid = lim - (first + t) * kPage - 4 * half;
             pv_slots(prev, slot_p, pfa, 127 + (half ? gp1 : gp0), [&](auto nn) {
-                cur_work(nn, t, valid, std::true_type{});
+                cur_work(nn, t, valid, std::true_type{}, std::true_type{}, src, dst, co);
             });
             if (__any(moved != 0)) {
                 // the previous page's tiles follow the reference.  An MFMA that has just
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 prev_work(ii, std::false_type{}, slot_l, 0u, nullptr, slot_l, std::true_type{});
             });
             pv_slots(std::true_type{}, slot_l, pfa, 127 + (half ? gp1 : gp0), [&](auto nn) {
-                cur_work(nn, 0, 0, std::false_type{});
+                cur_work(nn, 0, 0, std::false_type{}, std::false_type{}, slot_l, 0u, nullptr);
             });
         }
 
