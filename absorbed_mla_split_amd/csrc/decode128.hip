@@ -232,6 +232,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
         v8i ones;
 #pragma unroll
         for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;
+        pin_vgpr(ones);   // kept in registers, not rebuilt for every page
         int scale_one = 127;
         v16f acc[16];   // O^T of dim tile n (dims [32n, +32)) x the wave's rows
 #pragma unroll
@@ -358,7 +359,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                 }
                 here(ps1);
                 if constexpr (i & 1) {
-                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], 0, false);
+                    // (both halves are written: the old dword only saves a zeroing move)
+                    int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], pfa[4 + (i >> 1)], false);
                     w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[2], pt[3], w4, true);
                     pfa[4 + (i >> 1)] = w4;
                     here(pfa);
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void decode128_kernel(
                     }
                     here(ps0);
                     if constexpr (i & 1) {
-                        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], 0, false);
+                        int w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[0], pt[1], pf[i >> 1], false);
                         w4 = __builtin_amdgcn_cvt_pk_fp8_f32(pt[2], pt[3], w4, true);
                         pf[i >> 1] = w4;
                         here(pf);
