@@ -89,6 +89,20 @@ def test_every_tile_size_for_any_rows(k, H, mtile):
     assert dec.device_status() == 0
 
 
+@pytest.mark.parametrize("mtile,workers", [(128, 2), (128, 5), (64, 4), (32, 3)])
+def test_short_units_back_to_back(mtile, workers):
+    # few workers, many requests of one to five pages (ragged last pages): each worker runs
+    # many short units in a row, so the page ring is refilled across unit ends over and over
+    # (the 128-row kernel's spare copy of a unit's last page, and its wait before the next
+    # unit's first DMA; the stream kernel's ring that runs on across units)
+    lengths = [1, 63, 64, 65, 130, 200, 257, 300, 5, 128, 192, 319]
+    w = wl.small(len(lengths), 4, 64 if mtile != 32 else 8, lengths, seed=mtile + workers)
+    out, lse, dec = run_gpu(w, mtile=mtile, workers=workers)
+    assert dec.params.mtile == mtile and dec.params.workers == workers
+    compare(w, out, lse, tag=f"short units MT{mtile} W{workers}")
+    assert dec.device_status() == 0
+
+
 def test_many_splits_small_workers():
     # few workers and no minimum split: long requests cut into many 1-page splits
     w = wl.small(3, 4, 8, [2000, 64 * 40, 90], seed=3)
