@@ -307,6 +307,9 @@ __global__ __launch_bounds__(2 * kDecodeThreads, 1) void decode_stream_kernel(
     } else {
         // ================================================================ value waves
         const int vwv = wave - 4;
+        // the value waves go first where both waves of a SIMD could issue (measured on c3:
+        // decode 248-249 against 250-251 us; raising the score waves instead: 251-258)
+        __builtin_amdgcn_s_setprio(1);
         const int prb = MT == 64 ? (vwv & 1) : 0;
         const int tile0 = MT == 64 ? NT * (vwv >> 1) : NT * vwv;
         const bool lse_writer = MT == 64 ? (vwv >> 1) == 0 : vwv == 0;
