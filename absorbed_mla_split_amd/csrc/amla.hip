@@ -429,11 +429,12 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a)
 // [R*k, H*128] (the same bytes as [R][M][128] in folded row order).  W_UV is stored
 // latent-contiguous ([H][128][512]; page "drafter.attention", latent_major), so every
 // MFMA operand fragment is 16 adjacent bytes.
-// One workgroup of 8 waves per (head h, 16 rows of that head); row j of head h is draft
-// token t = j % k of request r = j / k, folded row i = t*H + h.  32 threads merge one row;
-// the BF16 latent tile goes through LDS into the B operand of D[v][row] = W^T lat^T, wave w
-// computing output dims [16w, 16w + 16), so each lane ends with four adjacent output dims
-// of one row.
+// One workgroup of 8 waves per (head h, ROWS = 32, 16 or 8 rows of that head); row j of
+// head h is draft token t = j % k of request r = j / k, folded row i = t*H + h.  512 / ROWS
+// threads merge one row; the BF16 latent tile goes through LDS into the B operand of
+// D[v][row] = W^T lat^T, wave w computing output dims [16w, 16w + 16) for every 16-row
+// block of the tile with the same W_UV fragments, so each lane ends with four adjacent
+// output dims of one row per block.
 constexpr int kUvDim = 128;
 constexpr int kUvRows = 16;
 constexpr int kUvStride = kVDim + 8;   // BF16 per LDS latent row: 16 B of padding moves
@@ -457,10 +458,13 @@ struct UvArgs {
 template <int ROWS>
 __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
 {
-    constexpr int TPR = 512 / ROWS;        // threads per row: 32 or 64
-    constexpr int NJ = kVDim / 4 / TPR;    // float4s per thread and split: 4 or 2
-    __shared__ __attribute__((aligned(16))) uint16_t lat[kUvRows * kUvStride];
-    __shared__ float wts[kUvRows][AMLA_MAX_SPLITS];
+    constexpr int TILE = ROWS > kUvRows ? ROWS : kUvRows;   // LDS latent rows: 16 or 32
+    constexpr int RB = TILE / 16;          // 16-row column blocks of the MFMA
+    constexpr int TPR = 512 / ROWS;        // threads per row: 16, 32 or 64
+    constexpr int NJ = kVDim / 4 / TPR;    // float4s per thread and split: 8, 4 or 2
+    constexpr int BATCH = ROWS > kUvRows ? 2 : kUvBatch;   // splits in flight per thread
+    __shared__ __attribute__((aligned(16))) uint16_t lat[TILE * kUvStride];
+    __shared__ float wts[TILE][AMLA_MAX_SPLITS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y;
     const int per_head = a.reqs * a.k;
@@ -499,9 +503,9 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
     const int64_t pstride = (int64_t)a.rows * kVDim;
 
     float ls = tr < c ? lrow_g[(int64_t)tr * a.rows] : -INFINITY;
-    v4f p[kUvBatch][NJ];
+    v4f p[BATCH][NJ];
 #pragma unroll
-    for (int b = 0; b < kUvBatch; ++b) {
+    for (int b = 0; b < BATCH; ++b) {
         const int sb = b < c ? b : (c > 0 ? c - 1 : 0);
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
@@ -531,10 +535,10 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
     v4f acc[NJ];
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) acc[jj] = v4f{0, 0, 0, 0};
-    for (int s0 = 0; s0 < c; s0 += kUvBatch) {
+    for (int s0 = 0; s0 < c; s0 += BATCH) {
         if (s0 > 0) {
 #pragma unroll
-            for (int b = 0; b < kUvBatch; ++b) {
+            for (int b = 0; b < BATCH; ++b) {
                 const int sb = s0 + b < c ? s0 + b : c - 1;
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj)
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
             }
         }
 #pragma unroll
-        for (int b = 0; b < kUvBatch; ++b) {
+        for (int b = 0; b < BATCH; ++b) {
             const float w = s0 + b < c ? wts[rho][s0 + b] * inv : 0.f;
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj) acc[jj] += w * p[b][jj];
@@ -562,8 +566,8 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
         if (a.out && j < per_head)
             *(uint2 *)(a.out + g * kVDim + 4 * tr + 4 * TPR * jj) = make_uint2(lo, hi);
     }
-    if (ROWS < kUvRows) {   // the MFMA's 16 rows: the tile's unused rows are zero
-        for (int x = tid; x < (kUvRows - ROWS) * kVDim / 4; x += 512)
+    if (ROWS < TILE) {   // the MFMA's 16 rows: the tile's unused rows are zero
+        for (int x = tid; x < (TILE - ROWS) * kVDim / 4; x += 512)
             *(uint2 *)(lat + (ROWS + x / (kVDim / 4)) * kUvStride + 4 * (x % (kVDim / 4))) =
                 make_uint2(0u, 0u);
     }
@@ -571,23 +575,31 @@ __global__ __launch_bounds__(512) void combine_uv_kernel(UvArgs a)
         a.out_lse[g] = bad ? NAN : c > 0 ? mx + __builtin_amdgcn_logf(sum) : -INFINITY;
     __syncthreads();
 
-    // D[v][row] over K = 512 in 16 steps; B operand: lane l holds lat[row l%16][c = 32 s +
-    // 8 (l/16) .. +7]
-    v4f d = v4f{0, 0, 0, 0};
-    const uint16_t *lb = lat + (lane & 15) * kUvStride + 8 * (lane >> 4);
+    // D[v][row] over K = 512 in 16 steps for each 16-row block rb (the W_UV fragments serve
+    // every block); B operand: lane l holds lat[row 16 rb + l%16][c = 32 s + 8 (l/16) .. +7]
+    v4f d[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) d[rb] = v4f{0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-        const bf16x8 bfr = *(const bf16x8 *)(lb + 32 * s);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s], bfr, d, 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const uint16_t *lb = lat + (16 * rb + (lane & 15)) * kUvStride + 8 * (lane >> 4);
+            const bf16x8 bfr = *(const bf16x8 *)(lb + 32 * s);
+            d[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s], bfr, d[rb], 0, 0, 0);
+        }
     }
-    // lane l holds D[v = 16 wave + 4 (l/16) + e][row l%16], e < 4
-    const int jr = j0 + (lane & 15);
-    if ((lane & 15) < ROWS && jr < per_head) {
-        const int rr = jr / a.k;
-        const int64_t gr = (int64_t)rr * a.rows + (int64_t)(jr - rr * a.k) * a.heads + h;
-        const uint32_t lo = bf16_rne(d[0]) | ((uint32_t)bf16_rne(d[1]) << 16);
-        const uint32_t hi = bf16_rne(d[2]) | ((uint32_t)bf16_rne(d[3]) << 16);
-        *(uint2 *)(a.attn_out + gr * kUvDim + 16 * wave + 4 * (lane >> 4)) = make_uint2(lo, hi);
+    // lane l holds D[v = 16 wave + 4 (l/16) + e][row 16 rb + l%16], e < 4
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int jl = 16 * rb + (lane & 15), jr = j0 + jl;
+        if (jl < ROWS && jr < per_head) {
+            const int rr = jr / a.k;
+            const int64_t gr = (int64_t)rr * a.rows + (int64_t)(jr - rr * a.k) * a.heads + h;
+            const uint32_t lo = bf16_rne(d[rb][0]) | ((uint32_t)bf16_rne(d[rb][1]) << 16);
+            const uint32_t hi = bf16_rne(d[rb][2]) | ((uint32_t)bf16_rne(d[rb][3]) << 16);
+            *(uint2 *)(a.attn_out + gr * kUvDim + 16 * wave + 4 * (lane >> 4)) = make_uint2(lo, hi);
+        }
     }
 }
 
@@ -1175,9 +1187,15 @@ int amla_combine_uv(const void *d_workspace, size_t ws_bytes, const int32_t *d_c
     a.k = params->rows_per_req / heads;
     a.slots = num_reqs + kPlanSlack * params->workers;
     const int64_t per_head = (int64_t)num_reqs * a.k;
-    // 16-row tiles, or 8-row tiles when 16-row tiles would leave compute units idle
+    // 32-row tiles (each wave's W_UV fragments serve twice the rows) when they give at least
+    // three quarters of the 256 compute units a workgroup (c3's 224 tiles: 17-18 us against
+    // 21-24 us as 448 16-row tiles), else 16-row tiles when those fill them, else 8-row tiles
+    const int64_t tiles32 = (per_head + 2 * kUvRows - 1) / (2 * kUvRows);
     const int64_t tiles16 = (per_head + kUvRows - 1) / kUvRows;
-    if (tiles16 * heads >= 256)
+    if (tiles32 * heads >= 192)
+        hipLaunchKernelGGL(combine_uv_kernel<2 * kUvRows>, dim3((unsigned)tiles32, (unsigned)heads),
+                           dim3(512), 0, (hipStream_t)stream, a);
+    else if (tiles16 * heads >= 256)
         hipLaunchKernelGGL(combine_uv_kernel<kUvRows>, dim3((unsigned)tiles16, (unsigned)heads),
                            dim3(512), 0, (hipStream_t)stream, a);
     else

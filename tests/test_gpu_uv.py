@@ -118,6 +118,10 @@ SHAPES = [
     (16, 64, [70]),                  # M = 1024 (8-row tiles)
     (16, 64, [70, 130, 64, 1]),      # 4 x 16-row tiles per head, 256 workgroups: 16-row tiles
     (5, 4, [900, 64, 2000, 7, 333]),  # 25 rows per head: a full and a partial tile
+    # 8 x 16 rows per head, 4 x 32-row tiles per head x 64 heads: 32-row tiles
+    (16, 64, [70, 130, 64, 1, 300, 2, 65, 900]),
+    # 100 rows per head: three full 32-row tiles and one of 4 rows
+    (4, 64, [1 + 37 * i for i in range(25)]),
 ]
 
 
