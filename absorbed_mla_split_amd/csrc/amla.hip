@@ -669,8 +669,9 @@ __global__ __launch_bounds__(256) void merge_sources_kernel(const uint16_t *__re
 // slot % 64), the query row to [n, H, 576].  Every value passes through BF16 (the model
 // dtype) before the cast.  W_UK_T arrives stored [H][512][128] (the 128 nope weights of a
 // latent dim adjacent), so MFMA operand fragments are 16 adjacent bytes.
-// One launch, two roles: blocks [0, query_blocks) build the query of (16 tokens, head h);
-// the others write the cache rows of 4 tokens (one wave each).
+// One launch, two roles: blocks [0, query_blocks) build the query of (TOK = 16 or 32
+// tokens, head h), the W_UK fragments of each MFMA serving every 16-token block; the others
+// write the cache rows of 4 tokens (one wave each).
 constexpr int kQbTokens = 16;
 
 struct BuildArgs {
@@ -707,8 +708,10 @@ __device__ __forceinline__ void rope_dims(int i, bool neox, int &d0, int &d1)
     d1 = neox ? i + 32 : 2 * i + 1;
 }
 
+template <int TOK>
 __global__ __launch_bounds__(256) void build_query_cache_kernel(BuildArgs a)
 {
+    constexpr int TB = TOK / 16;   // 16-token column blocks of the MFMA
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool neox = a.neox != 0;
     auto bf = [](uint16_t u) { return __uint_as_float((uint32_t)u << 16); };
@@ -723,40 +726,53 @@ __global__ __launch_bounds__(256) void build_query_cache_kernel(BuildArgs a)
 
     if ((int)blockIdx.x < a.query_blocks) {
         const int h = blockIdx.x % a.heads;
-        const int t0 = (blockIdx.x / a.heads) * kQbTokens;
-        // B operand (q_nope^T): lane l holds q_nope[token t0 + l%16][c = 32 ks + 8 (l/16) ..+7]
-        const int tok = t0 + (lane & 15);
-        bf16x8 qb[4];
+        const int t0 = (blockIdx.x / a.heads) * TOK;
+        // B operand (q_nope^T) of token block tb: lane l holds q_nope[token t0 + 16 tb + l%16]
+        // [c = 32 ks + 8 (l/16) ..+7]
+        bf16x8 qb[TB][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (tok < a.n)
-                qb[ks] = *(const bf16x8 *)(a.q + ((int64_t)tok * a.heads + h) * 192 + 32 * ks + 8 * (lane >> 4));
-            else
-                qb[ks] = bf16x8{};
+        for (int tb = 0; tb < TB; ++tb) {
+            const int tok = t0 + 16 * tb + (lane & 15);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if (tok < a.n)
+                    qb[tb][ks] = *(const bf16x8 *)(a.q + ((int64_t)tok * a.heads + h) * 192 + 32 * ks + 8 * (lane >> 4));
+                else
+                    qb[tb][ks] = bf16x8{};
+            }
         }
         // A operand (W_UK): lane l holds W[h][l = 128 wave + 16 mt + l%16][c = 32 ks + 8 (l/16) ..]
         const uint16_t *wh = a.w_uk + ((int64_t)h * kVDim + 128 * wave + (lane & 15)) * 128 + 8 * (lane >> 4);
-        v4f d[8];
+        v4f d[TB][8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            d[mt] = v4f{0, 0, 0, 0};
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) d[tb][mt] = v4f{0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 wa = *(const bf16x8 *)(wh + 16 * 128 * mt + 32 * ks);
-                d[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, qb[ks], d[mt], 0, 0, 0);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    d[tb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, qb[tb][ks], d[tb][mt], 0, 0, 0);
             }
         }
-        // lane l holds ql[token t0 + l%16][latent 128 wave + 16 mt + 4 (l/16) + e]
-        if (tok < a.n) {
-            uint8_t *qo = a.q_out + ((int64_t)tok * a.heads + h) * kKDim + 128 * wave + 4 * (lane >> 4);
+        // lane l holds ql[token t0 + 16 tb + l%16][latent 128 wave + 16 mt + 4 (l/16) + e]
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-                *(uint32_t *)(qo + 16 * mt) =
-                    e4m3x4(bf16_round(d[mt][0]), bf16_round(d[mt][1]), bf16_round(d[mt][2]),
-                           bf16_round(d[mt][3]), a.q_inv);
+        for (int tb = 0; tb < TB; ++tb) {
+            const int tok = t0 + 16 * tb + (lane & 15);
+            if (tok < a.n) {
+                uint8_t *qo = a.q_out + ((int64_t)tok * a.heads + h) * kKDim + 128 * wave + 4 * (lane >> 4);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+                    *(uint32_t *)(qo + 16 * mt) =
+                        e4m3x4(bf16_round(d[tb][mt][0]), bf16_round(d[tb][mt][1]),
+                               bf16_round(d[tb][mt][2]), bf16_round(d[tb][mt][3]), a.q_inv);
+            }
         }
-        // rope(q_pe): thread (token t0 + tid/16, pairs 2 (tid%16) and 2 (tid%16) + 1)
-        const int rt = t0 + (tid >> 4);
+        // rope(q_pe): thread (token t0 + 16 tb + tid/16, pairs 2 (tid%16) and 2 (tid%16) + 1)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+        const int rt = t0 + 16 * tb + (tid >> 4);
         if (rt < a.n) {
             const float *cs = cos_sin_row(rt);
             const uint16_t *pe = a.q + ((int64_t)rt * a.heads + h) * 192 + 128;
@@ -772,6 +788,7 @@ __global__ __launch_bounds__(256) void build_query_cache_kernel(BuildArgs a)
                 qo[d0] = (uint8_t)(w & 0xFF);
                 qo[d1] = (uint8_t)((w >> 8) & 0xFF);
             }
+        }
         }
         return;
     }
@@ -1121,12 +1138,21 @@ int amla_build_query_cache(const uint16_t *d_q, const uint16_t *d_w_uk, const ui
     a.max_pos = max_pos;
     a.q_inv = 1.0f / q_scale;
     a.k_inv = 1.0f / k_scale;
-    const int64_t qblocks = (int64_t)((n_tokens + kQbTokens - 1) / kQbTokens) * heads;
+    // 32-token query blocks (each W_UK fragment serves two MFMAs) when they give at least
+    // three quarters of the 256 compute units a block, else 16-token blocks
+    const int64_t qblocks32 = (int64_t)((n_tokens + 2 * kQbTokens - 1) / (2 * kQbTokens)) * heads;
+    const bool wide = qblocks32 >= 192;
+    const int64_t qblocks =
+        wide ? qblocks32 : (int64_t)((n_tokens + kQbTokens - 1) / kQbTokens) * heads;
     const int64_t cblocks = (n_tokens + 3) / 4;
     if (qblocks + cblocks > 0x7FFFFFFF) return AMLA_ERR_INVALID;
     a.query_blocks = (int32_t)qblocks;
-    hipLaunchKernelGGL(build_query_cache_kernel, dim3((unsigned)(qblocks + cblocks)), dim3(256), 0,
-                       (hipStream_t)stream, a);
+    if (wide)
+        hipLaunchKernelGGL(build_query_cache_kernel<2 * kQbTokens>, dim3((unsigned)(qblocks + cblocks)),
+                           dim3(256), 0, (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(build_query_cache_kernel<kQbTokens>, dim3((unsigned)(qblocks + cblocks)),
+                           dim3(256), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? AMLA_OK : AMLA_ERR_HIP;
 }
 

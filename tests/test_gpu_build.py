@@ -90,7 +90,7 @@ def check_build(inp, n, H, q_out, cache, slots, tag):
 
 
 @pytest.mark.parametrize("n,H,neox", [(37, 8, False), (37, 8, True), (256, 64, False),
-                                      (5, 1, True), (100, 32, False)])
+                                      (5, 1, True), (100, 32, False), (100, 64, True)])
 def test_query_and_cache_rows(n, H, neox):
     inp = wl.query_build_inputs(n, H, seed=n + H, max_pos=4096, neox=neox)
     pool = (n + 63) // 64 + 3
